@@ -1,0 +1,197 @@
+"""Plain float64 attention oracle (test infrastructure only; see the package docstring).
+
+Sources (the pages this follows; cited by page title and section):
+
+* "Fast Attention Kernels and Operator Fusion", section "FlashAttention-Style
+  Kernels": attention with an additive mask M is softmax(Q K^T / sqrt(d) + M) V.
+  The scale is passed in (it is 1/sqrt(d) in every workload used here).  The
+  causal mask is the M whose entries are 0 where key j <= query i and -inf
+  elsewhere (the ``is_causal=True`` call shown in the same section).
+* "Kernel Fusion and Custom Kernels", section "3. FlashAttention: The Milestone
+  of Fusion", v1: the softmax is the numerically stable one (shift each row by
+  its maximum before exponentiating).
+* "Fast Attention Kernels and Operator Fusion", section "Paged Attention
+  Kernels": a sequence's KV cache lives in fixed-size physical blocks; logical
+  block b of a sequence is stored in physical block ``block_table[b]``, and a
+  kernel must translate each logical token position through that table.  The
+  block size in the pages' serving example is 16 tokens.
+
+Readings taken where the pages are silent (each repeated in the design doc):
+
+* LSE is the natural log of the sum of exp over the scaled, masked scores of
+  a row: LSE_i = m_i + ln(l_i), with m_i the row max and l_i the shifted sum.
+* Layout: Q, O are [B, H, N, d]; K, V are [B, Hkv, N, d]; LSE is [B, H, N].
+* Grouped heads: query head h reads KV head floor(h / (H / Hkv)); H % Hkv == 0.
+* Causal alignment: query and key lengths are equal, key j is visible to
+  query i iff j <= i.
+* Decode: one query per sequence at the last position; it sees all L keys.
+  K/V caches are [num_pages, page_size, Hkv, d]; token t of sequence s lives
+  at page ``block_table[s, t // page_size]``, slot ``t % page_size``; slots at
+  t >= L are never read.
+* An empty key set (L = 0) gives O = 0 and LSE = -inf (the empty sum).
+
+The helpers ``_kv_head``, ``_scores``, ``_apply_causal``, ``_softmax`` and
+``_page_slot`` are looked up at call time, so tests can plant a mistake in
+one of them (on the CPU) and check that a pin catches it.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+ROW_BLOCK = 512  # rows of one (b, h) computed at once; only bounds memory
+
+
+def bf16_bits_to_f64(x: np.ndarray) -> np.ndarray:
+    """Exact float64 value of bfloat16 numbers stored as their 16-bit patterns.
+
+    bfloat16 is the upper half of an IEEE binary32, so the value is the
+    binary32 whose upper 16 bits are the pattern and whose lower 16 are zero.
+    """
+    bits = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return bits.view(np.float32).astype(np.float64)
+
+
+def _as_f64(x: np.ndarray) -> np.ndarray:
+    x = np.asarray(x)
+    if x.dtype == np.uint16:  # bfloat16 bit patterns
+        return bf16_bits_to_f64(x)
+    return x.astype(np.float64, copy=False)
+
+
+def _kv_head(h: int, H: int, Hkv: int) -> int:
+    """KV head read by query head h: consecutive groups of H/Hkv query heads."""
+    return h // (H // Hkv)
+
+
+def _scores(q_rows: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """S = scale * Q K^T for a block of query rows [r, d] against keys [n, d]."""
+    return scale * (q_rows @ k.T)
+
+
+def _apply_causal(s: np.ndarray, row_pos: np.ndarray) -> None:
+    """Additive causal mask in place: S[r, j] = -inf where key j > query position."""
+    cols = np.arange(s.shape[1])
+    s[cols[None, :] > row_pos[:, None]] = -np.inf
+
+
+def _softmax(s: np.ndarray):
+    """Row softmax shifted by the row max. Returns (P, m, l) with l = sum exp(S - m)."""
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    l = e.sum(axis=1)
+    return e / l[:, None], m, l
+
+
+def _attend(q_rows, k, v, scale, row_pos=None):
+    """O and LSE for query rows [r, d] over keys/values [n, d] (float64)."""
+    r, d = q_rows.shape
+    if k.shape[0] == 0:  # no visible key: empty sum
+        return np.zeros((r, v.shape[1])), np.full(r, -np.inf)
+    s = _scores(q_rows, k, scale)
+    if row_pos is not None:
+        _apply_causal(s, row_pos)
+    p, m, l = _softmax(s)
+    return p @ v, m + np.log(l)
+
+
+def _check_heads(H: int, Hkv: int) -> None:
+    if H <= 0 or Hkv <= 0 or H % Hkv != 0:
+        raise ValueError(f"query heads {H} must be a positive multiple of KV heads {Hkv}")
+
+
+def softmax_probs(q, k, causal: bool, scale: float, b: int = 0, h: int = 0):
+    """The full probability matrix P [N, N] of one (batch, head); small N only."""
+    q64, k64 = _as_f64(q), _as_f64(k)
+    H, Hkv, N = q64.shape[1], k64.shape[1], q64.shape[2]
+    _check_heads(H, Hkv)
+    s = _scores(q64[b, h], k64[b, _kv_head(h, H, Hkv)], scale)
+    if causal:
+        _apply_causal(s, np.arange(N))
+    return _softmax(s)[0]
+
+
+def attention(q, k, v, causal: bool, scale: float):
+    """Exact attention over [B, H, N, d] queries; returns (O [B,H,N,d], LSE [B,H,N]) in float64.
+
+    Rows are processed ROW_BLOCK at a time; each row still sees its whole key
+    range at once.  For causal rows the keys after the block's last row are
+    left out: every one of them is masked (-inf) for every row of the block,
+    so it would contribute exp(-inf) = 0.
+    """
+    q64, k64, v64 = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, N, d = q64.shape
+    Hkv = k64.shape[1]
+    _check_heads(H, Hkv)
+    o = np.zeros((B, H, N, v64.shape[3]))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            g = _kv_head(h, H, Hkv)
+            for r0 in range(0, N, ROW_BLOCK):
+                r1 = min(N, r0 + ROW_BLOCK)
+                n_keys = r1 if causal else N
+                pos = np.arange(r0, r1) if causal else None
+                o[b, h, r0:r1], lse[b, h, r0:r1] = _attend(
+                    q64[b, h, r0:r1], k64[b, g, :n_keys], v64[b, g, :n_keys], scale, pos)
+    return o, lse
+
+
+def attention_rows(q, k, v, causal: bool, scale: float, rows):
+    """O and LSE of selected query rows only; ``rows`` is a sequence of (b, h, i).
+
+    The same definition as :func:`attention`, one row at a time, for sampled
+    checks at sizes where the full output would take too long.
+    """
+    q_, k_, v_ = np.asarray(q), np.asarray(k), np.asarray(v)
+    H, Hkv = q_.shape[1], k_.shape[1]
+    _check_heads(H, Hkv)
+    out_o, out_l = [], []
+    for b, h, i in rows:
+        g = _kv_head(int(h), H, Hkv)
+        n_keys = int(i) + 1 if causal else k_.shape[2]
+        pos = np.array([int(i)]) if causal else None
+        o, l = _attend(_as_f64(q_[b, h, i])[None, :], _as_f64(k_[b, g, :n_keys]),
+                       _as_f64(v_[b, g, :n_keys]), scale, pos)
+        out_o.append(o[0])
+        out_l.append(l[0])
+    return np.array(out_o), np.array(out_l)
+
+
+def _page_slot(t: np.ndarray, page_size: int):
+    """Logical token positions -> (logical block index, slot within the block)."""
+    return t // page_size, t % page_size
+
+
+def paged_gather(k_cache, v_cache, block_table_row, L: int):
+    """Logical K, V [L, Hkv, d] of one sequence, read through its block table."""
+    page_size = np.asarray(k_cache).shape[1]
+    t = np.arange(int(L))
+    blk, slot = _page_slot(t, page_size)
+    pages = np.asarray(block_table_row)[blk]
+    return _as_f64(np.asarray(k_cache)[pages, slot]), _as_f64(np.asarray(v_cache)[pages, slot])
+
+
+def paged_decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, seqs=None):
+    """Single-query decode over a paged KV cache.
+
+    q [S, H, d]; k_cache, v_cache [num_pages, page_size, Hkv, d];
+    block_table [S, max_pages]; seq_lens [S].  Returns (O [S,H,d], LSE [S,H])
+    in float64 for the sequences in ``seqs`` (default: all), in that order.
+    The query of sequence s sits at position L_s - 1 and sees all L_s keys.
+    """
+    q64 = _as_f64(q)
+    S, H, d = q64.shape
+    Hkv = np.asarray(k_cache).shape[2]
+    _check_heads(H, Hkv)
+    seqs = range(S) if seqs is None else list(seqs)
+    o = np.zeros((len(seqs), H, np.asarray(v_cache).shape[3]))
+    lse = np.zeros((len(seqs), H))
+    for n, s in enumerate(seqs):
+        L = int(seq_lens[s])
+        kk, vv = paged_gather(k_cache, v_cache, np.asarray(block_table)[s], L)
+        for h in range(H):
+            g = _kv_head(h, H, Hkv)
+            o_h, l_h = _attend(q64[s, h][None, :], kk[:, g], vv[:, g], scale, None)
+            o[n, h], lse[n, h] = o_h[0], l_h[0]
+    return o, lse

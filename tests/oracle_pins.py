@@ -1,0 +1,265 @@
+"""Pins for the float64 oracle: facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` function raises AssertionError when the oracle breaks the fact
+it checks.  ``test_oracle_pins.py`` runs them against the oracle as it stands,
+and against copies of it with one planted mistake each (every planted mistake
+must be caught by at least one pin).  Nothing here re-types the oracle's
+formula: the expected values come from closed forms, invariants, a brute-force
+``math.fsum`` loop, ``numpy.repeat`` and the CPU float64
+``torch.nn.functional.scaled_dot_product_attention`` library routine.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rand(shape, seed, mult=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * mult
+
+
+# ---------------------------------------------------------------- prefill pins
+
+def pin_softmax_rows_sum_to_one():
+    """Every probability row sums to 1, entries are in [0, 1], masked entries are exactly 0."""
+    q, k = _rand((1, 2, 37, 8), 1), _rand((1, 2, 37, 8), 2)
+    for causal in (False, True):
+        for h in range(2):
+            p = oracle.softmax_probs(q, k, causal, 0.3, 0, h)
+            assert np.all(np.abs(p.sum(axis=1) - 1.0) < 1e-12)
+            assert np.all(p >= 0) and np.all(p <= 1)
+            if causal:
+                assert np.all(p[np.triu_indices(37, 1)] == 0.0)
+                assert np.all(np.diag(p) > 0)
+
+
+def pin_zero_query_gives_mean_of_visible_values():
+    """Q = 0 makes all visible scores equal: O_i is the mean of the visible V rows, LSE_i = ln(count)."""
+    B, H, N, d = 2, 4, 23, 6
+    v = _rand((B, 2, N, d), 3)
+    k = _rand((B, 2, N, d), 4)
+    q = np.zeros((B, H, N, d))
+    for causal in (False, True):
+        o, lse = oracle.attention(q, k, v, causal, 0.7)
+        for b in range(B):
+            for h in range(H):
+                g = h // 2
+                for i in range(N):
+                    n = i + 1 if causal else N
+                    assert np.allclose(o[b, h, i], v[b, g, :n].mean(axis=0), rtol=0, atol=1e-13)
+                    assert abs(lse[b, h, i] - math.log(n)) < 1e-13
+
+
+def pin_identical_value_rows():
+    """If every V row is the same vector c, every output row is c."""
+    c = _rand((5,), 5)
+    v = np.broadcast_to(c, (1, 1, 19, 5)).copy()
+    q, k = _rand((1, 3, 19, 5), 6, 3.0), _rand((1, 1, 19, 5), 7, 3.0)
+    for causal in (False, True):
+        o, _ = oracle.attention(q, k, v, causal, 0.5)
+        assert np.allclose(o, c, rtol=0, atol=1e-13)
+
+
+def pin_causal_first_row():
+    """With the causal mask, query 0 sees only key 0: O_0 = V_0 and LSE_0 = scale * q_0 . k_0."""
+    q, k, v = _rand((2, 2, 11, 7), 8), _rand((2, 1, 11, 7), 9), _rand((2, 1, 11, 7), 10)
+    scale = 0.37
+    o, lse = oracle.attention(q, k, v, True, scale)
+    for b in range(2):
+        for h in range(2):
+            assert np.array_equal(o[b, h, 0], v[b, 0, 0])
+            assert abs(lse[b, h, 0] - scale * math.fsum(q[b, h, 0] * k[b, 0, 0])) < 1e-13
+
+
+def _brute(q, k, v, causal, scale):
+    """Attention from the definition with pure-Python loops and math.fsum (H == Hkv)."""
+    B, H, N, d = q.shape
+    o = np.zeros((B, H, N, d))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                keys = [j for j in range(N) if (not causal) or j <= i]
+                s = [scale * math.fsum(float(q[b, h, i, c]) * float(k[b, h, j, c]) for c in range(d))
+                     for j in keys]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                tot = math.fsum(w)
+                for c in range(d):
+                    o[b, h, i, c] = math.fsum(w[n] * float(v[b, h, j, c]) for n, j in enumerate(keys)) / tot
+                lse[b, h, i] = mx + math.log(tot)
+    return o, lse
+
+
+def pin_brute_force_tiny():
+    """Agreement with a brute-force fsum implementation on tiny shapes (to 1e-12)."""
+    for N, d, causal, seed in [(1, 1, False, 0), (3, 2, True, 1), (5, 4, False, 2), (8, 4, True, 3),
+                               (7, 3, True, 4)]:
+        q, k, v = _rand((1, 2, N, d), seed), _rand((1, 2, N, d), seed + 10), _rand((1, 2, N, d), seed + 20)
+        o, lse = oracle.attention(q, k, v, causal, 0.61)
+        ob, lb = _brute(q, k, v, causal, 0.61)
+        assert np.allclose(o, ob, rtol=0, atol=1e-12)
+        assert np.allclose(lse, lb, rtol=0, atol=1e-12)
+
+
+def pin_torch_sdpa_float64():
+    """Agreement with torch's CPU float64 scaled_dot_product_attention (GQA via enable_gqa)."""
+    import torch
+    import torch.nn.functional as F
+    for (B, H, Hkv, N, d, causal) in [(2, 4, 2, 33, 16, True), (1, 6, 3, 29, 8, False),
+                                      (1, 8, 2, 64, 32, True), (2, 2, 2, 17, 64, False)]:
+        q, k, v = _rand((B, H, N, d), N), _rand((B, Hkv, N, d), N + 1), _rand((B, Hkv, N, d), N + 2)
+        scale = 1.0 / math.sqrt(d)
+        o, _ = oracle.attention(q, k, v, causal, scale)
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                                             is_causal=causal, scale=scale, enable_gqa=True).numpy()
+        assert np.allclose(o, ref, rtol=0, atol=1e-10)
+
+
+def pin_gqa_equals_mha_with_repeated_kv():
+    """Grouped heads equal plain multi-head attention on K/V repeated per group (numpy.repeat)."""
+    q = _rand((1, 8, 21, 4), 11)
+    k, v = _rand((1, 2, 21, 4), 12), _rand((1, 2, 21, 4), 13)
+    for causal in (False, True):
+        o1, l1 = oracle.attention(q, k, v, causal, 0.9)
+        o2, l2 = oracle.attention(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), causal, 0.9)
+        assert np.allclose(o1, o2, rtol=0, atol=1e-14) and np.allclose(l1, l2, rtol=0, atol=1e-14)
+
+
+def pin_key_permutation_invariance():
+    """Without a mask, permuting keys and values together leaves O and LSE unchanged."""
+    q, k, v = _rand((1, 2, 30, 5), 14), _rand((1, 2, 30, 5), 15), _rand((1, 2, 30, 5), 16)
+    perm = np.random.default_rng(17).permutation(30)
+    o1, l1 = oracle.attention(q, k, v, False, 0.8)
+    o2, l2 = oracle.attention(q, k[:, :, perm], v[:, :, perm], False, 0.8)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-13) and np.allclose(l1, l2, rtol=0, atol=1e-13)
+
+
+def pin_peaked_scores_stay_finite():
+    """Scores in the thousands: the max-shifted softmax stays finite and picks the dominant key.
+
+    Key 3 is q's own direction times 40, every other key is orthogonal to q, so
+    row 0's scores are 1600*|q|^2*scale for key 3 and 0 elsewhere: O_0 = V_3 to
+    within exp(-1000), LSE_0 = that score to within 1e-12 relative.
+    """
+    d = 4
+    qv = np.array([1.0, 2.0, -1.0, 0.5])
+    k = np.zeros((1, 1, 6, d))
+    k[0, 0, 3] = 40.0 * qv
+    k[0, 0, [0, 1, 2, 4, 5]] = np.array([2.0, -1.0, 0.0, 0.0]) * np.arange(1, 6)[:, None]  # orthogonal to qv
+    q = np.zeros((1, 1, 6, d))
+    q[0, 0, :] = 40.0 * qv
+    v = _rand((1, 1, 6, d), 18)
+    o, lse = oracle.attention(q, k, v, False, 0.5)
+    top = 0.5 * 1600.0 * float(qv @ qv)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert np.allclose(o[0, 0, 0], v[0, 0, 3], rtol=0, atol=1e-12)
+    assert abs(lse[0, 0, 0] - top) < 1e-12 * top
+
+
+def pin_rows_equal_full():
+    """attention_rows returns exactly the selected rows of attention."""
+    q, k, v = _rand((2, 4, 40, 8), 19), _rand((2, 2, 40, 8), 20), _rand((2, 2, 40, 8), 21)
+    rows = [(0, 0, 0), (1, 3, 39), (0, 2, 17), (1, 1, 5)]
+    for causal in (False, True):
+        o, lse = oracle.attention(q, k, v, causal, 0.4)
+        ro, rl = oracle.attention_rows(q, k, v, causal, 0.4, rows)
+        for n, (b, h, i) in enumerate(rows):
+            assert np.allclose(ro[n], o[b, h, i], rtol=0, atol=1e-14)
+            assert abs(rl[n] - lse[b, h, i]) < 1e-14
+
+
+# ----------------------------------------------------------------- decode pins
+
+def _golden_example():
+    with open(os.path.join(GOLDEN, "block_table_example.json")) as f:
+        return json.load(f)
+
+
+def _pool_from_table(table, L, Hkv, d, num_pages, page_size, seed):
+    """A pool holding L logical tokens placed by hand from the golden locations rule; NaN elsewhere."""
+    rng = np.random.default_rng(seed)
+    kk, vv = rng.standard_normal((L, Hkv, d)), rng.standard_normal((L, Hkv, d))
+    kc = np.full((num_pages, page_size, Hkv, d), np.nan)
+    vc = np.full((num_pages, page_size, Hkv, d), np.nan)
+    for t in range(L):
+        kc[table[t // page_size], t % page_size] = kk[t]
+        vc[table[t // page_size], t % page_size] = vv[t]
+    return kk, vv, kc, vc
+
+
+def pin_block_table_worked_example():
+    """The pages' table [17, 4, 29, 8]: gathering through it returns the logical tokens in order,
+    and decode over the pages equals attention over the contiguous logical sequence."""
+    ex = _golden_example()
+    table, ps = ex["physical_blocks"], ex["page_size"]
+    Hkv, H, d, L = 2, 4, 8, 57  # the last page is partly filled (57 = 3 * 16 + 9)
+    kk, vv, kc, vc = _pool_from_table(table, L, Hkv, d, 32, ps, 22)
+    for t, page, slot in ex["token_locations"]:
+        if t < L:
+            assert np.array_equal(kc[page, slot], kk[t])
+    gk, gv = oracle.paged_gather(kc, vc, np.array(table), L)
+    assert np.array_equal(gk, kk) and np.array_equal(gv, vv)
+    q = _rand((1, H, d), 23)
+    bt = np.array([table + [-1] * 4], dtype=np.int32)
+    o, lse = oracle.paged_decode(q, kc, vc, bt, np.array([L]), 0.35)
+    # contiguous reference: the same logical tokens as a [1, Hkv, L, d] prefill, non-causal, one query row
+    qp = np.zeros((1, H, L, d))
+    qp[0, :, L - 1] = q[0]
+    o2, l2 = oracle.attention_rows(qp, kk.transpose(1, 0, 2)[None], vv.transpose(1, 0, 2)[None], False, 0.35,
+                                   [(0, h, L - 1) for h in range(H)])
+    assert np.all(np.isfinite(o))
+    assert np.allclose(o[0], o2, rtol=0, atol=1e-14) and np.allclose(lse[0], l2, rtol=0, atol=1e-14)
+
+
+def pin_decode_equals_causal_prefill_last_row():
+    """Decode for a sequence equals the last row of causal prefill over the same L tokens."""
+    H, Hkv, d, L, ps = 4, 2, 8, 45, 16
+    table = [5, 0, 3]
+    kk, vv, kc, vc = _pool_from_table(table, L, Hkv, d, 6, ps, 24)
+    qfull = _rand((1, H, L, d), 25)
+    o, lse = oracle.paged_decode(qfull[:, :, L - 1], kc, vc, np.array([table], dtype=np.int32), [L], 0.5)
+    op, lp = oracle.attention(qfull, kk.transpose(1, 0, 2)[None], vv.transpose(1, 0, 2)[None], True, 0.5)
+    assert np.allclose(o[0], op[0, :, L - 1], rtol=0, atol=1e-13)
+    assert np.allclose(lse[0], lp[0, :, L - 1], rtol=0, atol=1e-13)
+
+
+def pin_decode_single_token():
+    """L = 1: O is the one V row at (block_table[0], slot 0); LSE = scale * q . k."""
+    H, Hkv, d = 2, 1, 6
+    kk, vv, kc, vc = _pool_from_table([3], 1, Hkv, d, 4, 16, 26)
+    q = _rand((1, H, d), 27)
+    o, lse = oracle.paged_decode(q, kc, vc, np.array([[3, -1]], dtype=np.int32), [1], 0.25)
+    for h in range(H):
+        assert np.array_equal(o[0, h], vc[3, 0, 0])
+        assert abs(lse[0, h] - 0.25 * math.fsum(q[0, h] * kc[3, 0, 0])) < 1e-14
+
+
+def pin_decode_empty_sequence():
+    """L = 0: the empty sum, O = 0 and LSE = -inf."""
+    kc = np.full((2, 16, 1, 4), np.nan)
+    o, lse = oracle.paged_decode(_rand((1, 2, 4), 28), kc, kc, np.array([[-1]], dtype=np.int32), [0], 1.0)
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+
+
+def pin_decode_page_permutation_invariance():
+    """Moving the same logical tokens to other physical pages changes nothing."""
+    H, Hkv, d, L = 4, 2, 8, 70
+    q = _rand((1, H, d), 29)
+    t1, t2 = [9, 2, 7, 0, 4], [1, 8, 3, 6, 5]
+    _, _, kc1, vc1 = _pool_from_table(t1, L, Hkv, d, 10, 16, 30)
+    _, _, kc2, vc2 = _pool_from_table(t2, L, Hkv, d, 10, 16, 30)
+    o1, l1 = oracle.paged_decode(q, kc1, vc1, np.array([t1]), [L], 0.3)
+    o2, l2 = oracle.paged_decode(q, kc2, vc2, np.array([t2]), [L], 0.3)
+    assert np.all(np.isfinite(o1)) and np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

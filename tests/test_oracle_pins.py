@@ -1,0 +1,81 @@
+"""CPU tests: the oracle against its pins, and planted mistakes against the pins."""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import exact as A
+import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+def _mut_softmax_no_shift(s):
+    e = np.exp(s)
+    l = e.sum(axis=1)
+    return e / l[:, None], np.zeros(s.shape[0]), l
+
+
+def _mut_softmax_unnormalised(s):
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    return e, m, e.sum(axis=1)
+
+
+def _mut_softmax_lse_without_max(s):
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    l = e.sum(axis=1)
+    return e / l[:, None], np.zeros_like(m), l
+
+
+def _mut_causal_strict(s, row_pos):
+    cols = np.arange(s.shape[1])
+    s[cols[None, :] >= row_pos[:, None]] = -np.inf
+
+
+def _mut_causal_flipped(s, row_pos):
+    cols = np.arange(s.shape[1])
+    s[cols[None, :] < row_pos[:, None]] = -np.inf
+
+
+# Each entry: (helper name in oracle.exact, planted replacement)
+MUTANTS = {
+    "gqa_modulo_mapping": ("_kv_head", lambda h, H, Hkv: h % Hkv),
+    "gqa_off_by_one": ("_kv_head", lambda h, H, Hkv: min(Hkv - 1, (h + 1) // (H // Hkv))),
+    "scale_dropped": ("_scores", lambda q, k, scale: q @ k.T),
+    "scale_squared": ("_scores", lambda q, k, scale: scale * scale * (q @ k.T)),
+    "sign_flipped": ("_scores", lambda q, k, scale: -scale * (q @ k.T)),
+    "key_dims_reversed": ("_scores", lambda q, k, scale: scale * (q @ k[:, ::-1].T)),
+    "causal_masks_diagonal": ("_apply_causal", _mut_causal_strict),
+    "causal_mask_flipped": ("_apply_causal", _mut_causal_flipped),
+    "softmax_no_max_shift": ("_softmax", _mut_softmax_no_shift),
+    "softmax_unnormalised": ("_softmax", _mut_softmax_unnormalised),
+    "lse_without_max": ("_softmax", _mut_softmax_lse_without_max),
+    "page_block_slot_swapped": ("_page_slot", lambda t, ps: (t % ps, t // ps)),
+    "page_off_by_one_token": ("_page_slot", lambda t, ps: ((t + 1) // ps, (t + 1) % ps)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, repl = MUTANTS[name]
+    monkeypatch.setattr(A, attr, repl)
+    caught = []
+    with np.errstate(all="ignore"):
+        for pin in P.ALL_PINS:
+            try:
+                pin()
+            except (AssertionError, IndexError, ValueError, FloatingPointError):
+                caught.append(pin.__name__)
+    assert caught, f"planted mistake {name} escaped every pin"
+
+
+def test_bf16_bits_to_f64_exact():
+    # 1.0, -2.0, 0.15625 (exactly representable), largest finite bf16, smallest normal
+    bits = np.array([0x3F80, 0xC000, 0x3E20, 0x7F7F, 0x0080], dtype=np.uint16)
+    want = np.array([1.0, -2.0, 0.15625, (2 - 2 ** -7) * 2.0 ** 127, 2.0 ** -126])
+    assert np.array_equal(oracle.bf16_bits_to_f64(bits), want)

@@ -1,0 +1,55 @@
+"""CPU tests of the seeded input generators (layout and rounding, no attention math)."""
+
+import numpy as np
+
+from workloads import (WORKLOADS, DecodeWorkload, PrefillWorkload, BF16_NAN, bf16_bits_to_f32,
+                       decode_inputs, f32_to_bf16_bits, prefill_inputs)
+
+
+def test_bf16_rounding_nearest_even():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -8 + 2 ** -20, -3.5, 0.0, np.inf, np.nan],
+                 dtype=np.float32)
+    # 1+2^-8 is a tie between 1 and 1+2^-7: goes to the even pattern (1.0);
+    # 1+3*2^-8 is a tie between 1+2^-7 and 1+2^-6: goes to 1+2^-6 (even mantissa)
+    want = np.array([1.0, 1.0, 1.0 + 2 ** -6, 1.0 + 2 ** -7, -3.5, 0.0, np.inf], dtype=np.float32)
+    got = f32_to_bf16_bits(x)
+    assert np.array_equal(bf16_bits_to_f32(got[:-1]), want)
+    assert got[-1] == BF16_NAN
+
+
+def test_prefill_inputs_shapes_and_outliers():
+    w = PrefillWorkload("t", 1, 4, 2, 300, 64, causal=True, q_mult=4.0, k_outlier_frac=0.01)
+    a = prefill_inputs(w, seed=3)
+    assert a["q"].shape == (1, 4, 300, 64) and a["k"].shape == (1, 2, 300, 64)
+    assert a["q"].dtype == np.uint16
+    assert a["outliers"].shape == (1, 2, 3)
+    for g in range(2):
+        assert len(set(a["outliers"][0, g])) == 3
+    b = prefill_inputs(w, seed=3)
+    assert np.array_equal(a["k"], b["k"])  # seeded
+
+
+def test_named_workloads():
+    assert WORKLOADS["causal_gqa_long_b1h32kv8n16384d128"].q_mult == 4.0
+    assert WORKLOADS["tiny_f32_b1h2n128d64"].scale == 0.125
+    assert WORKLOADS["paged_decode_s64h32kv8d128"].max_pages_per_seq == 512
+
+
+def test_decode_layout_and_poison():
+    w = DecodeWorkload("t", 5, 4, 2, 16, 1, 70, page_size=16, num_pages=40)
+    a = decode_inputs(w, seed=1)
+    lens, bt, kc = a["seq_lens"], a["block_table"], a["k_cache"]
+    assert np.all((lens >= 1) & (lens <= 70))
+    used = []
+    for s in range(5):
+        n = -(-int(lens[s]) // 16)
+        assert np.all(bt[s, :n] >= 0) and np.all(bt[s, n:] == -1)
+        used += list(bt[s, :n])
+        # every slot past the last token of the last page is poisoned
+        last = bt[s, n - 1]
+        tail = int(lens[s]) - 16 * (n - 1)
+        assert np.all(kc[last, tail:] == BF16_NAN)
+        assert not np.any(kc[last, :tail] == BF16_NAN)
+    assert len(used) == len(set(used))  # distinct physical pages
+    unused = sorted(set(range(40)) - set(used))
+    assert np.all(kc[unused] == BF16_NAN)

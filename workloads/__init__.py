@@ -1,0 +1,17 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module only draws and lays out inputs: it holds none of the attention
+arithmetic, and both the HIP library's tests/bench and the oracle consume what
+it returns.  See ``generators`` for the recipes.
+"""
+
+from .generators import (  # noqa: F401
+    WORKLOADS,
+    PrefillWorkload,
+    DecodeWorkload,
+    f32_to_bf16_bits,
+    bf16_bits_to_f32,
+    prefill_inputs,
+    decode_inputs,
+    BF16_NAN,
+)

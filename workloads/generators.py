@@ -1,0 +1,177 @@
+"""Seeded synthetic input recipes (no attention arithmetic lives here).
+
+Recipe shared by every workload:
+  * one ``numpy.random.Generator(PCG64(seed))`` per workload, seed 0 unless
+    given, draws in a fixed order (stated per function below);
+  * values are float32 standard normals; bfloat16 inputs are those float32
+    values rounded to nearest-even and carried as uint16 bit patterns, so the
+    GPU and the oracle read bit-identical numbers;
+  * the scale is float32(1 / sqrt(d)).
+
+The pages measure on no public dataset or benchmark, so these synthetic draws
+are the workloads themselves.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); return uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = BF16_NAN
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """float32 value of bfloat16 bit patterns (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    N: int
+    d: int
+    causal: bool
+    dtype: str = "bf16"          # "bf16" (bf16 in/out, fp32 accumulate) or "f32"
+    q_mult: float = 1.0          # power of two, so it commutes with bf16 rounding
+    k_outlier_frac: float = 0.0  # fraction of K rows per (b, kv head) scaled up
+    k_outlier_mult: float = 8.0
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    def visible_pairs(self) -> int:
+        """Query-key pairs the mask leaves visible, per (b, h)."""
+        return self.N * (self.N + 1) // 2 if self.causal else self.N * self.N
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    num_seqs: int
+    H: int
+    Hkv: int
+    d: int
+    L_lo: int
+    L_hi: int
+    page_size: int = 16
+    num_pages: int = 40000
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def max_pages_per_seq(self) -> int:
+        return -(-self.L_hi // self.page_size)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        PrefillWorkload("tiny_f32_b1h2n128d64", 1, 2, 2, 128, 64, causal=False, dtype="f32"),
+        PrefillWorkload("causal_b4h16n1024d64", 4, 16, 16, 1024, 64, causal=True),
+        PrefillWorkload("causal_gqa_b2h32kv8n4096d128", 2, 32, 8, 4096, 128, causal=True),
+        PrefillWorkload("causal_gqa_long_b1h32kv8n16384d128", 1, 32, 8, 16384, 128, causal=True,
+                        q_mult=4.0, k_outlier_frac=0.01, k_outlier_mult=8.0),
+        DecodeWorkload("paged_decode_s64h32kv8d128", 64, 32, 8, 128, 512, 8192, 16, 40000),
+    ]
+}
+
+
+def prefill_inputs(w: PrefillWorkload, seed: int = 0):
+    """Q [B,H,N,d], K, V [B,Hkv,N,d]; draw order Q, K, V, then outlier rows.
+
+    Q is multiplied by ``q_mult``.  For each (b, kv head) in order,
+    round(k_outlier_frac * N) distinct K rows chosen by the generator are
+    multiplied by ``k_outlier_mult``.  Returns a dict with the arrays (uint16
+    bfloat16 bits or float32) and the outlier row indices.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((w.B, w.H, w.N, w.d), dtype=np.float32)
+    k = rng.standard_normal((w.B, w.Hkv, w.N, w.d), dtype=np.float32)
+    v = rng.standard_normal((w.B, w.Hkv, w.N, w.d), dtype=np.float32)
+    if w.q_mult != 1.0:
+        q *= np.float32(w.q_mult)
+    outliers = np.zeros((w.B, w.Hkv, 0), dtype=np.int64)
+    n_out = int(round(w.k_outlier_frac * w.N))
+    if n_out:
+        outliers = np.zeros((w.B, w.Hkv, n_out), dtype=np.int64)
+        for b in range(w.B):
+            for g in range(w.Hkv):
+                rows = rng.choice(w.N, size=n_out, replace=False)
+                outliers[b, g] = rows
+                k[b, g, rows] *= np.float32(w.k_outlier_mult)
+    if w.dtype == "bf16":
+        q, k, v = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+    elif w.dtype != "f32":
+        raise ValueError(f"unknown dtype {w.dtype}")
+    return {"q": q, "k": k, "v": v, "outliers": outliers, "scale": w.scale}
+
+
+def decode_inputs(w: DecodeWorkload, seed: int = 0, poison: bool = True, seq_lens=None,
+                  block_table=None):
+    """Paged-decode inputs.
+
+    Draw order: sequence lengths (uniform integers in [L_lo, L_hi]), one
+    permutation of the ``num_pages`` physical page ids, Q [S, H, d], then per
+    sequence K [L, Hkv, d] followed by V [L, Hkv, d].  Sequence s takes the
+    next ceil(L_s / page_size) ids of the permutation as its block table, so
+    pages are distinct across all sequences; unused table entries are -1.
+    Token t of sequence s is stored at page block_table[s, t // page_size],
+    slot t % page_size of the [num_pages, page_size, Hkv, d] pools.  With
+    ``poison`` every slot no token occupies (unreferenced pages and the tail
+    of each last page) holds bfloat16 NaN.
+
+    ``seq_lens`` / ``block_table`` may be given to override the drawn ones
+    (then the corresponding draws are still made, to keep the order).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    S, ps = w.num_seqs, w.page_size
+    drawn = rng.integers(w.L_lo, w.L_hi, endpoint=True, size=S)
+    lens = np.asarray(drawn if seq_lens is None else seq_lens, dtype=np.int32)
+    perm = rng.permutation(w.num_pages)
+    max_pages = w.max_pages_per_seq
+    if block_table is None:
+        need = -(-lens.astype(np.int64) // ps)
+        if int(need.sum()) > w.num_pages:
+            raise ValueError("page pool too small for the drawn lengths")
+        bt = np.full((S, max_pages), -1, dtype=np.int32)
+        cursor = 0
+        for s in range(S):
+            n = int(need[s])
+            bt[s, :n] = perm[cursor:cursor + n]
+            cursor += n
+    else:
+        bt = np.asarray(block_table, dtype=np.int32)
+    q = f32_to_bf16_bits(rng.standard_normal((S, w.H, w.d), dtype=np.float32))
+    fill = BF16_NAN if poison else np.uint16(0)
+    k_pool = np.full((w.num_pages, ps, w.Hkv, w.d), fill, dtype=np.uint16)
+    v_pool = np.full((w.num_pages, ps, w.Hkv, w.d), fill, dtype=np.uint16)
+    for s in range(S):
+        L = int(lens[s])
+        kk = f32_to_bf16_bits(rng.standard_normal((L, w.Hkv, w.d), dtype=np.float32))
+        vv = f32_to_bf16_bits(rng.standard_normal((L, w.Hkv, w.d), dtype=np.float32))
+        t = np.arange(L)
+        pages = bt[s, t // ps]
+        k_pool[pages, t % ps] = kk
+        v_pool[pages, t % ps] = vv
+    return {"q": q, "k_cache": k_pool, "v_cache": v_pool, "block_table": bt,
+            "seq_lens": lens, "scale": w.scale, "max_pages_per_seq": max_pages}
