@@ -1,0 +1,122 @@
+/*
+ * paged_attention_attn — exact attention forward and paged-KV decode for one
+ * AMD Instinct MI355X (gfx950), as a C ABI.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library allocates nothing, frees nothing, keeps no per-call state,
+ *    never synchronises the stream and never reads device data on the host.
+ *    Every call only enqueues kernels on `stream` (0 = the null stream) and
+ *    returns; results are ready when that stream reaches them.
+ *  - Tensors are dense, row-major (C order) with the shapes given below.
+ *    q, k, v, o, k_cache, v_cache must be 16-byte aligned; lse, block_table,
+ *    seq_lens and workspace 4-byte aligned (workspace: 16-byte).
+ *  - "bf16" buffers hold IEEE bfloat16 values (2 bytes each).
+ *  - A nonzero return value is an ATTN_ERR_* code describing an argument error
+ *    found on the host before anything was launched, or ATTN_ERR_LAUNCH when
+ *    the HIP runtime rejected a launch.  Unsupported inputs are always an
+ *    error: the library has no slower fallback path.
+ *  - Calls are graph-capturable: no allocation, stable argument addresses.
+ *  - Outputs are deterministic: fixed reduction order, no atomics.
+ */
+#ifndef PAGED_ATTENTION_ATTN_H_
+#define PAGED_ATTENTION_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL_POINTER = 1,          /* a required pointer is NULL */
+  ATTN_ERR_INVALID_SHAPE = 2,         /* negative size, H or Hkv < 1, H % Hkv != 0 */
+  ATTN_ERR_UNSUPPORTED_HEAD_DIM = 3,  /* d not in {64, 128} */
+  ATTN_ERR_UNSUPPORTED_PAGE_SIZE = 4, /* page_size != 16 */
+  ATTN_ERR_WORKSPACE_TOO_SMALL = 5,   /* workspace_bytes below the required size */
+  ATTN_ERR_MISALIGNED = 6,            /* a pointer breaks the alignment rule above */
+  ATTN_ERR_TOO_LARGE = 7,             /* sizes overflow the launch grid or 64-bit offsets */
+  ATTN_ERR_UNSUPPORTED_GROUP = 8,     /* decode: more than 16 query heads per KV head */
+  ATTN_ERR_LAUNCH = 9                 /* hipGetLastError reported a failed launch */
+};
+
+/*
+ * attn_fwd — exact scaled dot-product attention forward, bf16 in/out.
+ *
+ * Computes O = softmax(scale * Q K^T + M) V with M = 0 (causal == 0) or the
+ * causal mask (causal != 0: key j is visible to query i iff j <= i), and the
+ * per-row log-sum-exp LSE_i = ln sum_j exp(scale * q_i . k_j + M_ij).
+ * ("Fast Attention Kernels and Operator Fusion", section "FlashAttention-Style
+ * Kernels", for the formula; the score matrix is never written to memory.)
+ *
+ *   q   [B, H,   N, d] bf16      k, v [B, Hkv, N, d] bf16
+ *   o   [B, H,   N, d] bf16 (written, rounded to nearest even)
+ *   lse [B, H,   N]    fp32 (written; may be NULL to skip)
+ * Query head h reads KV head h / (H / Hkv) (grouped-query attention; H must
+ * be a multiple of Hkv).  d must be 64 or 128.  B == 0 or N == 0 is a valid
+ * empty call (pointers are then not checked and may be NULL).  Arithmetic: bf16 products, fp32 accumulation and softmax; the
+ * probabilities are rounded to bf16 before the product with V.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
+             int causal, float scale, hipStream_t stream);
+
+/*
+ * attn_fwd_f32 — the same operation with fp32 inputs, outputs and arithmetic
+ * throughout (no reduced-precision matrix instructions).  Shapes, masking,
+ * head grouping and LSE as for attn_fwd; d must be 64 or 128.
+ */
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Hkv, int N,
+                 int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * paged_attn_decode_workspace_size — bytes of device workspace that
+ * paged_attn_decode needs for these shapes (0 on invalid shapes).  It grows
+ * linearly in num_seqs, H, d and max_pages_per_seq.
+ */
+size_t paged_attn_decode_workspace_size(int num_seqs, int H, int d, int page_size, int max_pages_per_seq);
+
+/*
+ * paged_attn_decode — single-query attention per sequence over a paged KV
+ * cache ("Fast Attention Kernels and Operator Fusion", section "Paged
+ * Attention Kernels": logical block b of sequence s lives in physical page
+ * block_table[s][b]; the kernel translates every token position through it).
+ *
+ *   q           [num_seqs, H, d] bf16 — the query of each sequence, at its last position
+ *   k_cache     [num_pages, page_size, Hkv, d] bf16
+ *   v_cache     [num_pages, page_size, Hkv, d] bf16
+ *   block_table [num_seqs, max_pages_per_seq] int32 — physical page ids
+ *   seq_lens    [num_seqs] int32 — L_s, tokens cached for sequence s
+ *   o           [num_seqs, H, d] bf16 (written)
+ *   lse         [num_seqs, H] fp32 (written; may be NULL)
+ *   workspace   >= paged_attn_decode_workspace_size(...) bytes, device memory
+ *               the call may overwrite (split partial results); reuse is fine
+ *               once the stream has passed the call.
+ * Token t of sequence s is slot t % page_size of page block_table[s][t / page_size];
+ * the query sees all L_s tokens (no mask).  page_size must be 16, d 64 or 128,
+ * H / Hkv at most 16.  num_seqs == 0 is a valid empty call (pointers may be NULL).
+ * Device-side rules (seq_lens and block_table are never read on the host):
+ * entries at index >= ceil(L_s / page_size) of a table row are never read;
+ * slots at or past L_s are never used (their contents, even NaN, do not
+ * matter); L_s is clamped to [0, max_pages_per_seq * page_size]; a page id
+ * outside [0, num_pages) is not dereferenced and its tokens are treated as
+ * absent.  L_s == 0 gives O = 0 and LSE = -inf.
+ * Internally: a split-KV kernel writes per-split results to the workspace and
+ * a separate reduce kernel merges them on the same stream.
+ */
+int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                      const int32_t* seq_lens, void* o, float* lse, int num_seqs, int H, int Hkv, int d, int page_size,
+                      int max_pages_per_seq, int num_pages, float scale, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* attn_status_string — a static, human-readable description of a status code. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTENTION_ATTN_H_ */

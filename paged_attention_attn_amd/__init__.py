@@ -1,0 +1,17 @@
+"""Exact attention forward and paged-KV decode on AMD Instinct MI355X (gfx950).
+
+The kernels are hand-written HIP in ``csrc/`` behind the C ABI declared in
+``include/paged_attention_attn.h``; this package is the thin Python binding
+(the same names as the C entry points, argument marshalling only).
+"""
+
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    attn_fwd,
+    attn_fwd_f32,
+    attn_status_string,
+    declared_functions,
+    lib,
+    paged_attn_decode,
+    paged_attn_decode_workspace_size,
+)

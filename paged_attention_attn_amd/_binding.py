@@ -1,0 +1,165 @@
+"""ctypes binding over ``libpaged_attention_attn.so``: argument marshalling only.
+
+Every function here has the name of the C entry point it calls and does no
+arithmetic of its own: it checks dtypes/devices/contiguity (an unsupported
+input raises, it is never copied or routed elsewhere), allocates outputs with
+torch when the caller passes none, and hands raw device pointers plus the
+current HIP stream to the library.  If the library has not been built, every
+call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpaged_attention_attn.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "paged_attention_attn.h")
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (loaded on first use; raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               "(run `python -m paged_attention_attn_amd.build`)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+        L.attn_fwd.restype = i
+        L.attn_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+        L.attn_fwd_f32.restype = i
+        L.paged_attn_decode_workspace_size.argtypes = [i, i, i, i, i]
+        L.paged_attn_decode_workspace_size.restype = sz
+        L.paged_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
+        L.paged_attn_decode.restype = i
+        L.attn_status_string.argtypes = [i]
+        L.attn_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions the public header declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def attn_status_string(status: int) -> str:
+    return lib().attn_status_string(int(status)).decode()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise RuntimeError(f"paged_attention_attn error {rc}: {attn_status_string(rc)}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(t, name, dtype, ndim, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (no implicit copies)")
+
+
+def _prefill(entry, dtype, q, k, v, causal, scale, out, lse):
+    _require(q, "q", dtype, 4)
+    _require(k, "k", dtype, 4, q.device)
+    _require(v, "v", dtype, 4, q.device)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
+        raise ValueError(f"k, v must be [B, Hkv, N, d] matching q {tuple(q.shape)}; got {tuple(k.shape)}, "
+                         f"{tuple(v.shape)}")
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out, "out", dtype, 4, q.device)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    if lse is not None:
+        _require(lse, "lse", torch.float32, 3, q.device)
+        if tuple(lse.shape) != (B, H, N):
+            raise ValueError("lse must be [B, H, N]")
+    if scale is None:
+        scale = d ** -0.5
+    _check(entry(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, N, d, int(bool(causal)),
+                 float(scale), _stream(q.device)))
+    return out, lse
+
+
+def attn_fwd(q, k, v, causal: bool, scale: float | None = None, out=None, lse=None):
+    """bf16 attention forward: q [B,H,N,d], k/v [B,Hkv,N,d] -> (out [B,H,N,d] bf16, lse [B,H,N] fp32 or None)."""
+    return _prefill(lib().attn_fwd, torch.bfloat16, q, k, v, causal, scale, out, lse)
+
+
+def attn_fwd_f32(q, k, v, causal: bool, scale: float | None = None, out=None, lse=None):
+    """fp32 attention forward with the same shapes as :func:`attn_fwd`."""
+    return _prefill(lib().attn_fwd_f32, torch.float32, q, k, v, causal, scale, out, lse)
+
+
+def paged_attn_decode_workspace_size(num_seqs: int, H: int, d: int, page_size: int, max_pages_per_seq: int) -> int:
+    return int(lib().paged_attn_decode_workspace_size(num_seqs, H, d, page_size, max_pages_per_seq))
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, scale: float | None = None, num_pages=None,
+                      workspace=None, out=None, lse=None):
+    """Paged decode: q [S,H,d] bf16, caches [P,16,Hkv,d] bf16, block_table [S,max_pages] int32, seq_lens [S] int32.
+
+    Returns (out [S,H,d] bf16, lse [S,H] fp32 or None).  ``workspace`` is a
+    uint8 device tensor of at least paged_attn_decode_workspace_size() bytes
+    (allocated here when not given).
+    """
+    _require(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _require(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _require(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _require(block_table, "block_table", torch.int32, 2, dev)
+    _require(seq_lens, "seq_lens", torch.int32, 1, dev)
+    S, H, d = q.shape
+    P, page_size, Hkv, dk = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or dk != d:
+        raise ValueError("k_cache and v_cache must both be [num_pages, page_size, Hkv, d]")
+    if block_table.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("block_table and seq_lens need one row per sequence")
+    max_pages = block_table.shape[1]
+    if num_pages is None:
+        num_pages = P
+    need = paged_attn_decode_workspace_size(S, H, d, page_size, max_pages)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _require(workspace, "workspace", torch.uint8, 1, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out, "out", torch.bfloat16, 3, dev)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, 2, dev)
+    if scale is None:
+        scale = d ** -0.5
+    _check(lib().paged_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                   _ptr(out), _ptr(lse), S, H, Hkv, d, page_size, max_pages, int(num_pages),
+                                   float(scale), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out, lse

@@ -1,0 +1,127 @@
+// The C ABI: host-side argument checks, then the launchers in launch.hpp.
+// Nothing here touches device memory or synchronises; every check uses only
+// the host-visible sizes and pointer values.
+
+#include <stdint.h>
+
+#include "../../include/paged_attention_attn.h"
+#include "launch.hpp"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Elements of a [a0, a1, a2, a3] tensor, or -1 when it overflows 2^62.
+long long elems(long long a0, long long a1, long long a2, long long a3) {
+  const long long lim = 1LL << 62;
+  long long r = 1;
+  for (long long x : {a0, a1, a2, a3}) {
+    if (x != 0 && r > lim / x) return -1;
+    r *= x;
+  }
+  return r;
+}
+
+// Shape checks first: an empty call (B == 0 or N == 0) is valid whatever the
+// pointers are, because nothing is read or written.
+int check_prefill(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
+                  int Hkv, int N, int d) {
+  if (B < 0 || N < 0 || H < 1 || Hkv < 1 || H % Hkv != 0) return ATTN_ERR_INVALID_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  if (B == 0 || N == 0) return ATTN_OK;
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return ATTN_ERR_MISALIGNED;
+  if (elems(B, H, N, d) < 0) return ATTN_ERR_TOO_LARGE;
+  // query tiles x heads x batch must fit one 1-D grid
+  if ((long long)B * H * ((N + 31) / 32) > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
+  return ATTN_OK;
+}
+
+int launch_status(hipError_t e) {
+  if (e == hipSuccess) return ATTN_OK;
+  if (e == hipErrorInvalidValue) return ATTN_ERR_TOO_LARGE;
+  return ATTN_ERR_LAUNCH;
+}
+
+constexpr size_t kWsAlign = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
+             int causal, float scale, hipStream_t stream) {
+  const int rc = check_prefill(q, k, v, o, lse, B, H, Hkv, N, d);
+  if (rc != ATTN_OK) return rc;
+  if (B == 0 || N == 0) return ATTN_OK;
+  return launch_status(paa::prefill_bf16(q, k, v, o, lse, B, H, Hkv, N, d, causal != 0, scale, stream));
+}
+
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Hkv, int N,
+                 int d, int causal, float scale, hipStream_t stream) {
+  const int rc = check_prefill(q, k, v, o, lse, B, H, Hkv, N, d);
+  if (rc != ATTN_OK) return rc;
+  if (B == 0 || N == 0) return ATTN_OK;
+  return launch_status(paa::prefill_f32(q, k, v, o, lse, B, H, Hkv, N, d, causal != 0, scale, stream));
+}
+
+size_t paged_attn_decode_workspace_size(int num_seqs, int H, int d, int page_size, int max_pages_per_seq) {
+  if (num_seqs < 0 || H < 1 || (d != 64 && d != 128) || page_size != 16 || max_pages_per_seq < 0) return 0;
+  if (num_seqs == 0 || max_pages_per_seq == 0) return kWsAlign;
+  const long long splits = paa::decode_max_splits(num_seqs, page_size, max_pages_per_seq);
+  const long long rows = elems(num_seqs, H, splits, 1);
+  if (rows < 0 || elems(rows, d + 1, 4, 1) < 0) return 0;
+  return round_up((size_t)rows * d * sizeof(float), kWsAlign) + round_up((size_t)rows * sizeof(float), kWsAlign);
+}
+
+int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                      const int32_t* seq_lens, void* o, float* lse, int num_seqs, int H, int Hkv, int d, int page_size,
+                      int max_pages_per_seq, int num_pages, float scale, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  if (num_seqs < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || max_pages_per_seq < 0 || num_pages < 0)
+    return ATTN_ERR_INVALID_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  if (page_size != 16) return ATTN_ERR_UNSUPPORTED_PAGE_SIZE;
+  if (H / Hkv > 16) return ATTN_ERR_UNSUPPORTED_GROUP;
+  if (num_seqs == 0) return ATTN_OK;  // empty call: nothing is read or written
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !workspace) return ATTN_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 4) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(lse, 4) || !aligned(workspace, 16))
+    return ATTN_ERR_MISALIGNED;
+  if (elems(num_pages, page_size, Hkv, d) < 0 || elems(num_seqs, max_pages_per_seq, 1, 1) < 0)
+    return ATTN_ERR_TOO_LARGE;
+  if ((long long)max_pages_per_seq * page_size > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
+  const size_t need = paged_attn_decode_workspace_size(num_seqs, H, d, page_size, max_pages_per_seq);
+  if (need == 0) return ATTN_ERR_TOO_LARGE;
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  const int split_tokens = paa::decode_split_tokens(num_seqs, page_size, max_pages_per_seq);
+  const int max_splits = max_pages_per_seq == 0 ? 1 : paa::decode_max_splits(num_seqs, page_size, max_pages_per_seq);
+  if ((long long)max_splits > 0x7fffffffLL || num_seqs > 65535) return ATTN_ERR_TOO_LARGE;
+  const long long rows = (long long)num_seqs * H * max_splits;
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up((size_t)rows * d * sizeof(float), kWsAlign));
+  return launch_status(paa::paged_decode_bf16(q, k_cache, v_cache, block_table, seq_lens, o, lse, num_seqs, H, Hkv, d,
+                                              page_size, max_pages_per_seq, num_pages, scale, ws_o, ws_lse,
+                                              split_tokens, max_splits, stream));
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "success";
+    case ATTN_ERR_NULL_POINTER: return "a required pointer argument is NULL";
+    case ATTN_ERR_INVALID_SHAPE: return "invalid shape: sizes must be non-negative, H and Hkv >= 1, H % Hkv == 0";
+    case ATTN_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head dimension: d must be 64 or 128";
+    case ATTN_ERR_UNSUPPORTED_PAGE_SIZE: return "unsupported page size: page_size must be 16";
+    case ATTN_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than paged_attn_decode_workspace_size()";
+    case ATTN_ERR_MISALIGNED: return "misaligned pointer: tensors need 16-byte, lse/tables 4-byte alignment";
+    case ATTN_ERR_TOO_LARGE: return "sizes too large for the launch grid or 64-bit offsets";
+    case ATTN_ERR_UNSUPPORTED_GROUP: return "unsupported grouping: at most 16 query heads per KV head in decode";
+    case ATTN_ERR_LAUNCH: return "kernel launch failed (hipGetLastError)";
+    default: return "unknown status code";
+  }
+}
+
+}  // extern "C"

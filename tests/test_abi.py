@@ -1,0 +1,93 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments on the host before anything is launched (no GPU needed,
+and no call here reaches a launch)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import pytest
+
+import paged_attention_attn_amd as paa
+from paged_attention_attn_amd import _binding
+
+ATTN_OK, NULL, SHAPE, HEAD_DIM, PAGE, WS, ALIGN, LARGE, GROUP, LAUNCH = range(10)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(paa.LIB_PATH):
+        from paged_attention_attn_amd import build
+        build.build()
+    return paa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = paa.declared_functions()
+    assert set(names) == {"attn_fwd", "attn_fwd_f32", "paged_attn_decode_workspace_size", "paged_attn_decode",
+                          "attn_status_string"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in range(10):
+        assert paa.attn_status_string(code)
+    assert paa.attn_status_string(12345) == "unknown status code"
+
+
+P = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, P, P, P, None, 1, 2, 2, 8, 64, 1, 0.1), NULL),
+    ((P, P, P, P, None, 1, 4, 3, 8, 64, 1, 0.1), SHAPE),
+    ((P, P, P, P, None, -1, 2, 2, 8, 64, 1, 0.1), SHAPE),
+    ((P, P, P, P, None, 1, 2, 2, 8, 96, 1, 0.1), HEAD_DIM),
+    ((ctypes.c_void_p(0x10008), P, P, P, None, 1, 2, 2, 8, 64, 1, 0.1), ALIGN),
+    ((P, P, P, P, None, 70000, 30000, 1, 100000, 128, 1, 0.1), LARGE),
+    ((P, P, P, P, None, 0, 2, 2, 8, 64, 1, 0.1), ATTN_OK),   # empty batch: nothing to launch
+    ((None, None, None, None, None, 0, 2, 2, 8, 64, 1, 0.1), ATTN_OK),  # empty: pointers unused
+    ((P, P, P, P, None, 1, 2, 2, 0, 64, 1, 0.1), ATTN_OK),   # empty sequence
+])
+def test_prefill_validation(L, args, code):
+    assert L.attn_fwd(*args, None) == code
+    assert L.attn_fwd_f32(*args, None) == code
+
+
+def test_decode_validation(L):
+    ws = paa.paged_attn_decode_workspace_size(4, 8, 128, 16, 10)
+    base = dict(q=P, kc=P, vc=P, bt=P, lens=P, o=P, lse=None, S=4, H=8, Hkv=2, d=128, ps=16, mp=10, np_=100,
+                scale=0.1, ws=P, wsb=ws)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.paged_attn_decode(a["q"], a["kc"], a["vc"], a["bt"], a["lens"], a["o"], a["lse"], a["S"], a["H"],
+                                   a["Hkv"], a["d"], a["ps"], a["mp"], a["np_"], a["scale"], a["ws"], a["wsb"], None)
+
+    assert call(bt=None) == NULL
+    assert call(ws=None) == NULL
+    assert call(Hkv=3) == SHAPE
+    assert call(d=80) == HEAD_DIM
+    assert call(ps=32) == PAGE
+    assert call(wsb=ws - 1) == WS
+    assert call(H=64, Hkv=2, wsb=10 ** 9) == GROUP
+    assert call(q=ctypes.c_void_p(0x10004)) == ALIGN
+    assert call(S=0) == ATTN_OK
+    assert call(S=0, q=None, ws=None) == ATTN_OK  # empty: pointers unused
+
+
+def test_workspace_linear_in_length(L):
+    """Workspace memory grows linearly with the longest sequence, never quadratically."""
+    sizes = [paa.paged_attn_decode_workspace_size(64, 32, 128, 16, mp) for mp in (64, 128, 256, 512, 1024)]
+    for a, b in zip(sizes, sizes[1:]):
+        assert b <= 2.0 * a + 512
+    assert paa.paged_attn_decode_workspace_size(64, 32, 96, 16, 10) == 0
+
+
+def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _binding.lib()

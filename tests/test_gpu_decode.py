@@ -1,0 +1,133 @@
+"""GPU parity of paged_attn_decode (through the C ABI) against the float64 oracle."""
+
+from __future__ import annotations
+
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_attention_attn_amd as paa
+from gpu_util import assert_close_bf16, assert_close_lse, dev_bf16, dev_i32, host_f64
+from workloads import WORKLOADS, DecodeWorkload, decode_inputs
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _announce(msg):
+    print(f"[gpu] {msg}", file=sys.stderr, flush=True)
+
+
+def _run(a, H, num_pages=None):
+    q = dev_bf16(a["q"])
+    kc, vc = dev_bf16(a["k_cache"]), dev_bf16(a["v_cache"])
+    bt, lens = dev_i32(a["block_table"]), dev_i32(a["seq_lens"])
+    lse = torch.empty((q.shape[0], H), dtype=torch.float32, device="cuda:0")
+    o, _ = paa.paged_attn_decode(q, kc, vc, bt, lens, a["scale"], num_pages=num_pages, lse=lse)
+    torch.cuda.synchronize()
+    return host_f64(o), lse.cpu().numpy().astype(np.float64), o
+
+
+def _oracle(a, seqs=None):
+    return oracle.paged_decode(a["q"], a["k_cache"], a["v_cache"], a["block_table"], a["seq_lens"], a["scale"],
+                               seqs=seqs)
+
+
+@pytest.mark.parametrize("d,H,Hkv", [(128, 32, 8), (64, 8, 8), (128, 16, 1), (64, 6, 2)])
+def test_decode_small_ragged_lengths(d, H, Hkv):
+    """Lengths around page and chunk edges, including 1 and 0; NaN in every unused slot."""
+    lens = [1, 15, 16, 17, 31, 32, 33, 100, 257, 0, 700]
+    w = DecodeWorkload("small", len(lens), H, Hkv, d, 1, 1024, 16, 200)
+    _announce(f"decode d{d} H{H} Hkv{Hkv}")
+    a = decode_inputs(w, seed=d + H, seq_lens=lens)
+    o, lse, _ = _run(a, H)
+    ro, rl = _oracle(a)
+    assert np.all(o[9] == 0) and np.all(np.isneginf(lse[9]))  # L = 0
+    assert_close_bf16(o, ro)
+    assert_close_lse(lse, rl)
+
+
+def test_decode_block_table_worked_example():
+    """The pages' block table [17, 4, 29, 8] with a partly filled last page."""
+    with open(os.path.join(GOLDEN, "block_table_example.json")) as f:
+        ex = json.load(f)
+    w = DecodeWorkload("golden", 1, 8, 2, 128, 57, 57, ex["page_size"], 32)
+    bt = np.array([ex["physical_blocks"]], dtype=np.int32)
+    a = decode_inputs(w, seed=11, seq_lens=[57], block_table=bt)
+    o, lse, _ = _run(a, 8)
+    ro, rl = _oracle(a)
+    assert_close_bf16(o, ro)
+    assert_close_lse(lse, rl)
+
+
+def test_decode_page_placement_is_invisible():
+    """The same logical tokens in other physical pages give bitwise-equal outputs."""
+    w = DecodeWorkload("perm", 3, 32, 8, 128, 200, 600, 16, 200)
+    a = decode_inputs(w, seed=3)
+    _, _, o1 = _run(a, 32)
+    # move every used page to a new physical id via a permutation of the pool
+    perm = np.random.default_rng(9).permutation(200)
+    inv = np.argsort(perm)
+    b = dict(a)
+    b["k_cache"], b["v_cache"] = a["k_cache"][inv], a["v_cache"][inv]
+    bt = a["block_table"].copy()
+    bt[bt >= 0] = perm[bt[bt >= 0]]
+    b["block_table"] = bt
+    _, _, o2 = _run(b, 32)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_decode_full_size_sampled():
+    """64 sequences, H=32, Hkv=8, d=128, lengths in [512, 8192], 40000-page pool: 16 sequences vs the oracle."""
+    w = WORKLOADS["paged_decode_s64h32kv8d128"]
+    _announce(w.name)
+    a = decode_inputs(w, seed=0)
+    o, lse, _ = _run(a, w.H)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    lens = a["seq_lens"]
+    seqs = sorted(set([int(np.argmin(lens)), int(np.argmax(lens))] +
+                      list(np.random.default_rng(4).choice(64, 14, replace=False))))
+    ro, rl = _oracle(a, seqs)
+    assert_close_bf16(o[seqs], ro)
+    assert_close_lse(lse[seqs], rl)
+
+
+def test_decode_out_of_range_page_id_is_not_read():
+    """A page id past num_pages is never dereferenced; its tokens count as absent."""
+    w = DecodeWorkload("oob", 1, 4, 1, 64, 48, 48, 16, 8)
+    bt = np.array([[2, 5, 7]], dtype=np.int32)
+    a = decode_inputs(w, seed=5, seq_lens=[48], block_table=bt)
+    a["block_table"] = np.array([[2, 1000000, 7]], dtype=np.int32)
+    o, lse, _ = _run(a, 4)
+    # expected: attention over tokens 0..15 and 32..47 only
+    keep = np.r_[0:16, 32:48]
+    kk = oracle.bf16_bits_to_f64(np.concatenate([a["k_cache"][2], a["k_cache"][7]]))  # [32, 1, 64]
+    vv = oracle.bf16_bits_to_f64(np.concatenate([a["v_cache"][2], a["v_cache"][7]]))
+    assert len(keep) == kk.shape[0]
+    q = oracle.bf16_bits_to_f64(a["q"])[0]  # [H, d]
+    for h in range(4):
+        ro, rl = oracle.attention_rows(q[None, h:h + 1, None, :], kk[None, :, 0][:, None], vv[None, :, 0][:, None],
+                                       False, a["scale"], [(0, 0, 0)])
+        assert_close_bf16(o[0, h][None], ro)
+        assert_close_lse(lse[0, h:h + 1], rl)
+
+
+def test_decode_argument_errors():
+    q = torch.zeros((2, 4, 128), dtype=torch.bfloat16, device="cuda:0")
+    kc = torch.zeros((4, 8, 1, 128), dtype=torch.bfloat16, device="cuda:0")  # page size 8
+    bt = torch.zeros((2, 2), dtype=torch.int32, device="cuda:0")
+    lens = torch.ones((2,), dtype=torch.int32, device="cuda:0")
+    with pytest.raises(RuntimeError, match="page size"):
+        paa.paged_attn_decode(q, kc, kc, bt, lens)
+    kc16 = torch.zeros((4, 16, 1, 128), dtype=torch.bfloat16, device="cuda:0")
+    ws = torch.zeros((8,), dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(RuntimeError, match="workspace"):
+        paa.paged_attn_decode(q, kc16, kc16, bt, lens, workspace=ws)
+    with pytest.raises(TypeError):
+        paa.paged_attn_decode(q, kc16, kc16, bt.long(), lens)

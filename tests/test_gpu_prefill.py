@@ -1,0 +1,153 @@
+"""GPU parity of attn_fwd / attn_fwd_f32 (through the C ABI) against the float64 oracle."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_attention_attn_amd as paa
+from gpu_util import (assert_close_bf16, assert_close_f32, assert_close_lse, dev_bf16, dev_f32, host_f64,
+                      sample_rows)
+from workloads import WORKLOADS, PrefillWorkload, prefill_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"[gpu] {msg}", file=sys.stderr, flush=True)
+
+
+def _run_bf16(a, w):
+    q, k, v = dev_bf16(a["q"]), dev_bf16(a["k"]), dev_bf16(a["v"])
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
+    o, _ = paa.attn_fwd(q, k, v, w.causal, a["scale"], lse=lse)
+    torch.cuda.synchronize()
+    return host_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+# Small shapes: the oracle computes every output.  They span several 64-key
+# tiles and 128-row query tiles, ragged ends, every head-grouping branch and
+# both head dims.
+SMALL = [
+    (2, 4, 2, 300, 64, True), (2, 4, 2, 300, 64, False),
+    (1, 8, 2, 257, 128, True), (1, 8, 2, 257, 128, False),
+    (1, 4, 4, 200, 128, True), (1, 6, 2, 131, 64, True),   # group 3 -> one head per workgroup
+    (1, 8, 1, 190, 128, True),                               # group 8 -> two head subgroups
+    (1, 2, 1, 1, 64, True), (1, 2, 2, 17, 128, False), (1, 2, 2, 64, 64, True), (3, 2, 1, 129, 128, True),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal", SMALL)
+def test_bf16_small_full_parity(B, H, Hkv, N, d, causal):
+    w = PrefillWorkload("small", B, H, Hkv, N, d, causal)
+    _announce(f"attn_fwd bf16 B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal}")
+    a = prefill_inputs(w, seed=N + d)
+    o, lse = _run_bf16(a, w)
+    ro, rl = oracle.attention(a["q"], a["k"], a["v"], causal, a["scale"])
+    assert_close_bf16(o, ro)
+    assert_close_lse(lse, rl)
+
+
+def test_bf16_peaked_scores_small():
+    """Scores with a large range (Q x4, 1% of K rows x8) at a size the oracle covers fully."""
+    w = PrefillWorkload("peaked", 1, 8, 2, 520, 128, True, q_mult=4.0, k_outlier_frac=0.01)
+    _announce("attn_fwd bf16 peaked N520")
+    a = prefill_inputs(w, seed=5)
+    o, lse = _run_bf16(a, w)
+    ro, rl = oracle.attention(a["q"], a["k"], a["v"], True, a["scale"])
+    assert_close_bf16(o, ro)
+    assert_close_lse(lse, rl)
+
+
+def test_bf16_causal_mha_b4h16n1024d64_full():
+    """Causal self-attention B=4, H=16, N=1024, d=64: every output element against the oracle."""
+    w = WORKLOADS["causal_b4h16n1024d64"]
+    _announce(w.name)
+    a = prefill_inputs(w, seed=0)
+    o, lse = _run_bf16(a, w)
+    ro, rl = oracle.attention(a["q"], a["k"], a["v"], True, a["scale"])
+    assert_close_bf16(o, ro)
+    assert_close_lse(lse, rl)
+
+
+@pytest.mark.parametrize("name", ["causal_gqa_b2h32kv8n4096d128", "causal_gqa_long_b1h32kv8n16384d128"])
+def test_bf16_full_size_sampled(name):
+    """Full-size GQA prefill: sampled rows against the oracle, the rest checked finite."""
+    w = WORKLOADS[name]
+    _announce(name)
+    a = prefill_inputs(w, seed=0)
+    o, lse = _run_bf16(a, w)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rows = sample_rows(w.B, w.H, w.N, 160, seed=1)
+    ro, rl = oracle.attention_rows(a["q"], a["k"], a["v"], True, a["scale"], rows)
+    idx = tuple(np.array(rows).T)
+    assert_close_bf16(o[idx], ro)
+    assert_close_lse(lse[idx], rl)
+
+
+def test_bf16_deterministic_and_linear_memory():
+    """Two runs are bitwise equal; the call allocates nothing (peak memory = inputs + outputs)."""
+    w = PrefillWorkload("det", 1, 8, 2, 2048, 128, True)
+    a = prefill_inputs(w, seed=2)
+    q, k, v = dev_bf16(a["q"]), dev_bf16(a["k"]), dev_bf16(a["v"])
+    o1, lse1 = torch.empty_like(q), torch.empty((1, 8, 2048), dtype=torch.float32, device="cuda:0")
+    o2, lse2 = torch.empty_like(q), torch.empty_like(lse1)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    before = torch.cuda.memory_allocated()
+    paa.attn_fwd(q, k, v, True, a["scale"], out=o1, lse=lse1)
+    paa.attn_fwd(q, k, v, True, a["scale"], out=o2, lse=lse2)
+    torch.cuda.synchronize()
+    assert torch.cuda.max_memory_allocated() == before
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(lse1, lse2)
+
+
+def test_f32_tiny_workload_parity():
+    """fp32 path, B=1, H=2, N=128, d=64, non-causal, seed 0: max |err| <= 1e-5."""
+    w = WORKLOADS["tiny_f32_b1h2n128d64"]
+    a = prefill_inputs(w, seed=0)
+    q, k, v = dev_f32(a["q"]), dev_f32(a["k"]), dev_f32(a["v"])
+    lse = torch.empty((1, 2, 128), dtype=torch.float32, device="cuda:0")
+    o, _ = paa.attn_fwd_f32(q, k, v, False, a["scale"], lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(a["q"], a["k"], a["v"], False, a["scale"])
+    assert_close_f32(host_f64(o), ro)
+    assert_close_lse(lse.cpu().numpy().astype(np.float64), rl)
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal", [(1, 2, 2, 128, 64, True), (2, 4, 2, 100, 128, True),
+                                                 (1, 3, 1, 70, 64, False), (1, 2, 1, 1, 128, True)])
+def test_f32_small_parity(B, H, Hkv, N, d, causal):
+    w = PrefillWorkload("f32", B, H, Hkv, N, d, causal, dtype="f32")
+    a = prefill_inputs(w, seed=7)
+    q, k, v = dev_f32(a["q"]), dev_f32(a["k"]), dev_f32(a["v"])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+    o, _ = paa.attn_fwd_f32(q, k, v, causal, a["scale"], lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(a["q"], a["k"], a["v"], causal, a["scale"])
+    assert_close_f32(host_f64(o), ro)
+    assert_close_lse(lse.cpu().numpy().astype(np.float64), rl)
+
+
+def test_empty_and_argument_errors():
+    q = torch.zeros((0, 2, 16, 64), dtype=torch.bfloat16, device="cuda:0")
+    o, _ = paa.attn_fwd(q, q[:, :1], q[:, :1], True)  # B = 0: valid, nothing launched
+    assert o.shape == q.shape
+    x = torch.zeros((1, 2, 16, 96), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(RuntimeError, match="head dimension"):
+        paa.attn_fwd(x, x, x, True)
+    y = torch.zeros((1, 2, 16, 64), dtype=torch.float16, device="cuda:0")
+    with pytest.raises(TypeError):
+        paa.attn_fwd(y, y, y, True)
+    z = torch.zeros((1, 2, 64, 16), dtype=torch.bfloat16, device="cuda:0").transpose(2, 3)
+    with pytest.raises(ValueError, match="contiguous"):
+        paa.attn_fwd(z, z, z, True)
+    k3 = torch.zeros((1, 3, 16, 64), dtype=torch.bfloat16, device="cuda:0")
+    q4 = torch.zeros((1, 4, 16, 64), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(RuntimeError, match="invalid shape"):
+        paa.attn_fwd(q4, k3, k3, True)
