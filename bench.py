@@ -9,16 +9,25 @@ H=32, Hkv=8, d=128, lengths uniform in [512, 8192], 16-token pages in a
 
 Prints ONE JSON line.  ``value`` is the prefill throughput in TFLOP/s on
 algorithmic flops (4*d*B*H*visible pairs); the decode object reports GB/s on
-algorithmic bytes (K/V of valid tokens + Q + O + LSE + table entries read).
-Each kernel call is bracketed by HIP events on the stream it runs on; the
-dominant call of the step (by time) gives the top-level ``roofline``.
-``cpu_baseline`` times the float64 oracle on the host cores on a bounded
-sample (the oracle is imported only for that leg).
+algorithmic bytes (K/V of valid tokens + Q + O + LSE + block-table entries
+and lengths read).  Each call is bracketed by HIP events on the stream it is
+launched on; the call that takes most of the step (the paged decode) gives
+the top-level ``roofline``.  ``cpu_baseline`` times the float64 oracle on the
+host cores on the step's own workload (the oracle is imported only there).
+
+Other modes (used to produce the summaries kept under profiles/):
+  --pmc-pass                 a few launches of every kernel plus a plain copy
+                             of known size, for a rocprofv3 --pmc run
+  --summarize-trace DIR      markdown summary of a rocprofv3 --kernel-trace run
+  --summarize-counters F W   HBM bytes per launch from a FETCH_SIZE run (F)
+                             and a WRITE_SIZE run (W), calibrated by the copy
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -35,54 +44,69 @@ METRIC = "causal prefill attention TFLOP/s + paged decode KV GB/s, % of roofline
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
-KERNEL_SOURCES = ["prefill_bf16.hip", "paged_decode.hip", "device_common.hpp"]
+CSRC = os.path.join(ROOT, "paged_attention_attn_amd", "csrc")
+PHASE_GAP_S = 0.05         # idle time left between phases so a trace can be split by them
+COPY_BYTES = 1 << 30       # calibration copy: 1 GiB read + 1 GiB written
+COPY_KERNEL_TAG = "neg_kernel"  # torch's elementwise negate, used as the plain copy kernel
+PMC_CALLS = 3              # calls of each workload in a counter pass
 
+PREFILL_DEFAULT = "causal_b4h16n1024d64"
+DECODE_DEFAULT = "paged_decode_s64h32kv8d128"
+PREFILL_MORE = ("causal_gqa_b2h32kv8n4096d128", "causal_gqa_long_b1h32kv8n16384d128")
+
+
+# ----------------------------------------------------------------- algorithmic counts
 
 def prefill_flops(w) -> float:
+    """4*d flops (two matmuls) per visible query-key pair."""
     return 4.0 * w.d * w.B * w.H * w.visible_pairs()
 
 
 def prefill_bytes(w) -> float:
-    el = 2
+    """Q, K, V read once, O and LSE written once (K/V once per KV head)."""
+    el = 2 if w.dtype == "bf16" else 4
     return el * (w.B * w.H * w.N * w.d * 2 + w.B * w.Hkv * w.N * w.d * 2) + 4 * w.B * w.H * w.N
 
 
 def decode_bytes(w, lens) -> float:
+    """K and V of the valid tokens, Q, O, LSE, the block-table entries used and the lengths."""
     lens = np.asarray(lens, dtype=np.int64)
     kv = float(lens.sum()) * w.Hkv * w.d * 2 * 2
     qo = 2.0 * len(lens) * w.H * w.d * 2
     return kv + qo + 4.0 * len(lens) * w.H + 4.0 * float((-(-lens // w.page_size)).sum()) + 4.0 * len(lens)
 
 
-def source_digest(names) -> str:
+def source_digest() -> str:
+    """Digest of every kernel source: counter figures are only valid for the sources they were taken on."""
     h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "paged_attention_attn_amd", "csrc", n), "rb") as f:
+    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str):
-    """HBM bytes per launch from the committed counter summary, if taken on the current sources."""
+def read_traffic(workload: str):
+    """HBM bytes per call of ``workload`` from the committed counter summary, if taken on these sources."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    entries = {}
     with open(TRAFFIC_FILE) as f:
         for line in f:
             line = line.strip()
-            if line.startswith("{"):
-                e = json.loads(line)
-                entries[e["kernel"]] = e
-    e = entries.get(kernel)
-    if e is None or e.get("sources") != source_digest(KERNEL_SOURCES):
-        return None
-    return e["hbm_bytes_per_launch"]
+            if not line.startswith("{"):
+                continue
+            e = json.loads(line)
+            if e.get("workload") == workload and e.get("sources") == source_digest():
+                return e["hbm_bytes_per_call"]
+    return None
 
 
 def roofline(kind, achieved, peak, unit, traffic):
     return {"bound": kind, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic}
 
+
+# ----------------------------------------------------------------- device helpers
 
 def to_dev_bf16(torch, bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda:0").view(torch.bfloat16)
@@ -93,7 +117,7 @@ def to_dev_i32(torch, x):
 
 
 def timed(torch, fn, iters, warmup):
-    """Median and mean of event-timed calls of fn on the current stream (ms)."""
+    """Median and mean (ms) of event-timed calls of fn on the current stream."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -107,39 +131,93 @@ def timed(torch, fn, iters, warmup):
     return statistics.median(ts), statistics.fmean(ts)
 
 
-def cpu_baseline(pw, pa, dw, da, budget_s=30.0):
-    """The float64 oracle on host cores: the prefill workload's leading heads and 8 decode sequences."""
+class Phases:
+    """Named phases separated by idle gaps, so a kernel trace of this run can be split per workload."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.names = []
+
+    def start(self, name):
+        self.torch.cuda.synchronize()
+        time.sleep(PHASE_GAP_S)
+        self.names.append(name)
+        print(f"[bench] phase {len(self.names) - 1}: {name}", file=sys.stderr, flush=True)
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------- workload setup
+
+class PrefillCase:
+    def __init__(self, torch, paa, w, seed):
+        from workloads import prefill_inputs
+        self.w = w
+        self.a = prefill_inputs(w, seed=seed)
+        self.q, self.k, self.v = (to_dev_bf16(torch, self.a[n]) for n in ("q", "k", "v"))
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
+        self.paa = paa
+
+    def __call__(self):
+        self.paa.attn_fwd(self.q, self.k, self.v, self.w.causal, self.a["scale"], out=self.o, lse=self.lse)
+
+
+class DecodeCase:
+    def __init__(self, torch, paa, w, seed):
+        from workloads import decode_inputs
+        self.w = w
+        self.a = a = decode_inputs(w, seed=seed)
+        self.q = to_dev_bf16(torch, a["q"])
+        self.kc, self.vc = to_dev_bf16(torch, a["k_cache"]), to_dev_bf16(torch, a["v_cache"])
+        self.bt, self.lens = to_dev_i32(torch, a["block_table"]), to_dev_i32(torch, a["seq_lens"])
+        self.ws = torch.empty(paa.paged_attn_decode_workspace_size(w.num_seqs, w.H, w.d, w.page_size,
+                                                                   w.max_pages_per_seq),
+                              dtype=torch.uint8, device="cuda:0")
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((w.num_seqs, w.H), dtype=torch.float32, device="cuda:0")
+        self.paa = paa
+
+    def __call__(self):
+        self.paa.paged_attn_decode(self.q, self.kc, self.vc, self.bt, self.lens, self.a["scale"],
+                                   workspace=self.ws, out=self.o, lse=self.lse)
+
+
+# ----------------------------------------------------------------- CPU baseline (oracle)
+
+def cpu_baseline(pc, dc, min_seconds=10.0):
+    """The float64 oracle on the host cores over the step's own workload.
+
+    Sample: the whole prefill workload and the whole decode workload, repeated
+    until at least ``min_seconds`` have passed (mean per pass reported).
+    """
     import oracle
     from threadpoolctl import threadpool_info
 
     threads = sum(p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas") or 1
-    # prefill: whole (b, h) slices, as many as fit about half the budget (at least one)
-    heads = pw.B * pw.H
-    t0 = time.perf_counter()
-    oracle.attention(pa["q"][:1, :1], pa["k"][:1, :1], pa["v"][:1, :1], pw.causal, pa["scale"])
-    per_head = time.perf_counter() - t0
-    n = int(max(1, min(heads, (budget_s / 2) / max(per_head, 1e-6))))
-    bsel, hsel = n // pw.H, n % pw.H
-    t0 = time.perf_counter()
-    if bsel:
-        oracle.attention(pa["q"][:bsel], pa["k"][:bsel], pa["v"][:bsel], pw.causal, pa["scale"])
-    if hsel:
-        g = (hsel - 1) // (pw.H // pw.Hkv) + 1
-        oracle.attention(pa["q"][bsel:bsel + 1, :hsel], pa["k"][bsel:bsel + 1, :g], pa["v"][bsel:bsel + 1, :g],
-                         pw.causal, pa["scale"])
-    t_pre = time.perf_counter() - t0
-    flops = 4.0 * pw.d * n * pw.visible_pairs()
-    # decode: 8 sequences of the decode workload
-    seqs = list(range(8))
-    t0 = time.perf_counter()
-    oracle.paged_decode(da["q"], da["k_cache"], da["v_cache"], da["block_table"], da["seq_lens"], da["scale"],
-                        seqs=seqs)
-    t_dec = time.perf_counter() - t0
-    lens = da["seq_lens"][seqs]
-    return {"value": round(flops / t_pre / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{pw.name}: {n} of {heads} (batch, head) slices, {t_pre:.1f} s",
-            "decode": {"value": round(decode_bytes(dw, lens) / t_dec / 1e9, 4), "unit": "GB/s",
-                       "sample": f"{dw.name}: sequences 0-7 ({int(lens.sum())} tokens), {t_dec:.1f} s"},
+    pw, dw, pa, da = pc.w, dc.w, pc.a, dc.a
+    t_pre = t_dec = 0.0
+    passes = 0
+    while passes == 0 or t_pre + t_dec < min_seconds:
+        t0 = time.perf_counter()
+        oracle.attention(pa["q"], pa["k"], pa["v"], pw.causal, pa["scale"])
+        t1 = time.perf_counter()
+        oracle.paged_decode(da["q"], da["k_cache"], da["v_cache"], da["block_table"], da["seq_lens"], da["scale"])
+        t2 = time.perf_counter()
+        t_pre += t1 - t0
+        t_dec += t2 - t1
+        passes += 1
+    t_pre /= passes
+    t_dec /= passes
+    pre_tf = prefill_flops(pw) / t_pre / 1e12
+    dec_gbs = decode_bytes(dw, da["seq_lens"]) / t_dec / 1e9
+    return {"value": round(pre_tf, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole {pw.name} prefill ({t_pre:.2f} s) and whole {dw.name} decode ({t_dec:.2f} s) "
+                      f"per pass, {passes} passes, mean reported",
+            "decode": {"value": round(dec_gbs, 4), "unit": "GB/s"},
+            "ms_per_step": round(1e3 * (t_pre + t_dec), 1),
             "cpu": _cpu_model()}
 
 
@@ -154,63 +232,22 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--prefill-workload", default="causal_b4h16n1024d64")
-    ap.add_argument("--decode-workload", default="paged_decode_s64h32kv8d128")
-    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
-    ap.add_argument("--no-more", action="store_true", help="skip the larger prefill workloads")
-    args = ap.parse_args()
+# ----------------------------------------------------------------- modes
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not supported; "
-              "the kernels run on one MI355X and have no multi-GPU path", file=sys.stderr)
-        return 2
+def run_bench(args, torch, paa) -> dict:
+    from workloads import WORKLOADS
 
-    import torch
+    phases = Phases(torch)
+    pc = PrefillCase(torch, paa, WORKLOADS[args.prefill_workload], args.seed)
+    dc = DecodeCase(torch, paa, WORKLOADS[args.decode_workload], args.seed)
+    pw, dw = pc.w, dc.w
+    _log(f"inputs ready: {pw.name}, {dw.name}")
 
-    import paged_attention_attn_amd as paa
-    from workloads import WORKLOADS, decode_inputs, prefill_inputs
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 2
-    if not os.path.exists(paa.LIB_PATH):
-        from paged_attention_attn_amd import build
-        build.build()
-
-    pw = WORKLOADS[args.prefill_workload]
-    dw = WORKLOADS[args.decode_workload]
-    pa = prefill_inputs(pw, seed=args.seed)
-    da = decode_inputs(dw, seed=args.seed)
-    print(f"[bench] inputs ready: {pw.name}, {dw.name}", file=sys.stderr, flush=True)
-
-    q, k, v = to_dev_bf16(torch, pa["q"]), to_dev_bf16(torch, pa["k"]), to_dev_bf16(torch, pa["v"])
-    o = torch.empty_like(q)
-    lse = torch.empty((pw.B, pw.H, pw.N), dtype=torch.float32, device="cuda:0")
-    dq = to_dev_bf16(torch, da["q"])
-    kc, vc = to_dev_bf16(torch, da["k_cache"]), to_dev_bf16(torch, da["v_cache"])
-    bt, lens = to_dev_i32(torch, da["block_table"]), to_dev_i32(torch, da["seq_lens"])
-    ws = torch.empty(paa.paged_attn_decode_workspace_size(dw.num_seqs, dw.H, dw.d, dw.page_size,
-                                                          dw.max_pages_per_seq), dtype=torch.uint8, device="cuda:0")
-    do = torch.empty_like(dq)
-    dlse = torch.empty((dw.num_seqs, dw.H), dtype=torch.float32, device="cuda:0")
-
-    def prefill():
-        paa.attn_fwd(q, k, v, pw.causal, pa["scale"], out=o, lse=lse)
-
-    def decode():
-        paa.paged_attn_decode(dq, kc, vc, bt, lens, da["scale"], workspace=ws, out=do, lse=dlse)
-
-    # ---- timed steps: W untimed, then exactly K, synchronised on both sides ----
+    # ---- W untimed steps, then exactly K timed steps, synchronised on both sides ----
+    phases.start(f"step: prefill {pw.name} + decode {dw.name}")
     for _ in range(args.warmup):
-        prefill()
-        decode()
+        pc()
+        dc()
     torch.cuda.synchronize()
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
@@ -219,33 +256,33 @@ def main() -> int:
     t_beg.record()
     for i in range(K):
         ev[i][0].record()
-        prefill()
+        pc()
         ev[i][1].record()
-        decode()
+        dc()
         ev[i][2].record()
     t_end.record()
     torch.cuda.synchronize()
     ms_step = t_beg.elapsed_time(t_end) / K
     pre_ms = statistics.fmean(e[0].elapsed_time(e[1]) for e in ev)
     dec_ms = statistics.fmean(e[1].elapsed_time(e[2]) for e in ev)
-    print(f"[bench] {K} steps: {ms_step:.4f} ms/step (prefill {pre_ms:.4f} ms, decode {dec_ms:.4f} ms)",
-          file=sys.stderr, flush=True)
+    _log(f"{K} steps: {ms_step:.4f} ms/step (prefill {pre_ms:.4f} ms, decode {dec_ms:.4f} ms)")
 
     pf = prefill_flops(pw)
-    db = decode_bytes(dw, da["seq_lens"])
+    db = decode_bytes(dw, dc.a["seq_lens"])
     pre_tf = pf / (pre_ms * 1e-3) / 1e12
     dec_gbs = db / (dec_ms * 1e-3) / 1e9
-    pre_roof = roofline("mfma", pre_tf, PEAK_BF16_TFLOPS, "TFLOP/s", read_traffic("prefill_bf16_kernel"))
-    dec_roof = roofline("hbm", dec_gbs, PEAK_HBM_GBS, "GB/s", read_traffic("decode_partial_kernel"))
+    pre_roof = roofline("mfma", pre_tf, PEAK_BF16_TFLOPS, "TFLOP/s", read_traffic(pw.name))
+    dec_roof = roofline("hbm", dec_gbs, PEAK_HBM_GBS, "GB/s", read_traffic(dw.name))
 
-    # decode with the 256 MB last-level cache evicted before every call (512 MB write in between)
+    # ---- decode with the 256 MB last-level cache evicted before every call ----
+    phases.start(f"decode {dw.name}, caches evicted before each call")
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
     cold = []
-    for i in range(10 + 2):
+    for i in range(12):
         scratch.fill_(i & 0xFF)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        decode()
+        dc()
         b.record()
         torch.cuda.synchronize()
         if i >= 2:
@@ -255,30 +292,24 @@ def main() -> int:
 
     more = []
     if not args.no_more:
-        for name in ("causal_gqa_b2h32kv8n4096d128", "causal_gqa_long_b1h32kv8n16384d128"):
-            w = WORKLOADS[name]
-            a_ = prefill_inputs(w, seed=args.seed)
-            q2, k2, v2 = to_dev_bf16(torch, a_["q"]), to_dev_bf16(torch, a_["k"]), to_dev_bf16(torch, a_["v"])
-            o2 = torch.empty_like(q2)
-            l2 = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
-            med, mean = timed(torch, lambda: paa.attn_fwd(q2, k2, v2, True, a_["scale"], out=o2, lse=l2), 20, 3)
-            tf = prefill_flops(w) / (mean * 1e-3) / 1e12
+        for name in PREFILL_MORE:
+            c = PrefillCase(torch, paa, WORKLOADS[name], args.seed)
+            phases.start(f"prefill {name}")
+            med, mean = timed(torch, c, 20, 3)
+            tf = prefill_flops(c.w) / (mean * 1e-3) / 1e12
             more.append({"workload": name, "ms": round(mean, 4), "ms_median": round(med, 4),
                          "value": round(tf, 2), "unit": "TFLOP/s",
-                         "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", None)})
-            del q2, k2, v2, o2, l2
-            print(f"[bench] {name}: {mean:.4f} ms, {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+                         "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", read_traffic(name))})
+            del c
+            _log(f"{name}: {mean:.4f} ms, {tf:.1f} TFLOP/s")
 
     base = None
     if not args.no_cpu_baseline:
-        base = cpu_baseline(pw, pa, dw, da)
-        print(f"[bench] cpu baseline: {base['sample']}; {base['decode']['sample']}", file=sys.stderr, flush=True)
+        base = cpu_baseline(pc, dc)
+        _log(f"cpu baseline: {base['sample']}")
 
-    dominant = dec_roof if dec_ms >= pre_ms else pre_roof
-    dominant = dict(dominant, kernel="paged decode (decode_partial_kernel + decode_reduce_kernel)"
-                    if dec_ms >= pre_ms else "prefill_bf16_kernel")
     props = torch.cuda.get_device_properties(0)
-    line = {
+    return {
         "metric": METRIC,
         "value": round(pre_tf, 3),
         "unit": "TFLOP/s",
@@ -295,9 +326,10 @@ def main() -> int:
                    "prefill": {"B": pw.B, "H": pw.H, "Hkv": pw.Hkv, "N": pw.N, "d": pw.d, "causal": pw.causal},
                    "decode": {"num_seqs": dw.num_seqs, "H": dw.H, "Hkv": dw.Hkv, "d": dw.d,
                               "L": [dw.L_lo, dw.L_hi], "page_size": dw.page_size, "num_pages": dw.num_pages,
-                              "tokens": int(da["seq_lens"].sum())},
+                              "tokens": int(dc.a["seq_lens"].sum())},
                    "seed": args.seed},
-        "roofline": dominant,
+        "roofline": dict(dec_roof, kernel="paged_attn_decode: decode_partial_kernel + decode_reduce_kernel",
+                         workload=dw.name, bytes_per_call=round(db)),
         "prefill": {"workload": pw.name, "ms": round(pre_ms, 5), "value": round(pre_tf, 3), "unit": "TFLOP/s",
                     "algorithmic_gflop": round(pf / 1e9, 4), "algorithmic_mb": round(prefill_bytes(pw) / 1e6, 3),
                     "roofline": pre_roof},
@@ -306,9 +338,178 @@ def main() -> int:
                    "cold_ms": round(cold_ms, 5), "cold_value": round(db / (cold_ms * 1e-3) / 1e9, 2)},
         "prefill_more": more,
         "cpu_baseline": base,
+        "phases": phases.names,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
-    print(json.dumps(line))
+
+
+def run_pmc_pass(args, torch, paa) -> dict:
+    """A short run for hardware counters: a calibration copy, then a few calls of each workload."""
+    from workloads import WORKLOADS
+
+    phases = Phases(torch)
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0").normal_()
+    dst = torch.empty_like(src)
+    phases.start(f"copy {COPY_BYTES} bytes")
+    for _ in range(PMC_CALLS):
+        torch.neg(src, out=dst)
+    del src, dst
+    cases = [DecodeCase(torch, paa, WORKLOADS[args.decode_workload], args.seed),
+             PrefillCase(torch, paa, WORKLOADS[args.prefill_workload], args.seed)]
+    cases += [PrefillCase(torch, paa, WORKLOADS[n], args.seed) for n in PREFILL_MORE]
+    for c in cases:
+        phases.start(c.w.name)
+        for _ in range(PMC_CALLS):
+            c()
+    torch.cuda.synchronize()
+    return {"phases": phases.names, "sources": source_digest()}
+
+
+# ----------------------------------------------------------------- rocprofv3 summaries
+
+def _split_phases(dispatches, n_phases):
+    """Split dispatches (sorted by start) into phases at the n_phases-1 largest idle gaps."""
+    if n_phases <= 1 or len(dispatches) < 2:
+        return [dispatches]
+    gaps = sorted(range(1, len(dispatches)),
+                  key=lambda i: dispatches[i]["start"] - dispatches[i - 1]["end"], reverse=True)[:n_phases - 1]
+    cuts = [0] + sorted(gaps) + [len(dispatches)]
+    return [dispatches[a:b] for a, b in zip(cuts, cuts[1:])]
+
+
+def _short(name: str) -> str:
+    name = name.replace("paa::(anonymous namespace)::", "")
+    return name.split("(")[0] if name.startswith("void ") is False else name[5:].split("(")[0]
+
+
+def _load_dispatches(d):
+    out = []
+    for p in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(p)):
+            out.append({"name": r["Kernel_Name"], "start": int(r["Start_Timestamp"]), "end": int(r["End_Timestamp"]),
+                        "grid": (r["Grid_Size_X"], r["Grid_Size_Y"], r["Grid_Size_Z"]), "wg": r["Workgroup_Size_X"],
+                        "vgpr": r["VGPR_Count"], "agpr": r.get("Accum_VGPR_Count", ""), "lds": r["LDS_Block_Size"]})
+    out.sort(key=lambda x: x["start"])
+    return out
+
+
+def summarize_trace(trace_dir, bench_json, command) -> str:
+    with open(bench_json) as f:
+        line = [l for l in f if l.startswith("{")][-1]
+    bench = json.loads(line)
+    names = bench["phases"]
+    ds = _load_dispatches(trace_dir)
+    ours = [d for d in ds if "paa::" in d["name"] or "FillFunctor" in d["name"]]
+    groups = _split_phases(ours, len(names))
+    out = ["# rocprofv3 kernel trace: attention kernels on the bench workloads", "",
+           f"Command (run from the repository root): `{command}`", "",
+           f"Kernel sources digest: `{source_digest()}`", "",
+           "Durations are rocprofv3 kernel-trace start/end per dispatch (ns), grouped by the bench phase the "
+           "dispatch fell in (phases are separated by idle gaps) and by kernel.", "",
+           "| phase | kernel | grid | wg | calls | avg us | min us | max us |", "|---|---|---|---|---|---|---|---|"]
+    for name, g in zip(names, groups):
+        by = {}
+        for d in g:
+            by.setdefault((_short(d["name"]), d["grid"], d["wg"]), []).append(d["end"] - d["start"])
+        for (k, grid, wg), t in by.items():
+            out.append(f"| {name} | `{k}` | {'x'.join(grid)} | {wg} | {len(t)} | {statistics.fmean(t) / 1e3:.2f} | "
+                       f"{min(t) / 1e3:.2f} | {max(t) / 1e3:.2f} |")
+    out += ["", "Bench line of the same run (event-timed, not under the profiler's overhead):", "",
+            "```", json.dumps({k: bench.get(k) for k in ("ms_per_step", "prefill", "decode", "prefill_more")},
+                              indent=1), "```"]
+    return "\n".join(out) + "\n"
+
+
+def _load_counters(d, counter):
+    rows = []
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(p)):
+            if r["Counter_Name"] != counter:
+                continue
+            if "paa::" not in r["Kernel_Name"] and COPY_KERNEL_TAG not in r["Kernel_Name"]:
+                continue
+            rows.append({"name": r["Kernel_Name"], "value": float(r["Counter_Value"]),
+                         "start": int(r["Start_Timestamp"]), "end": int(r["End_Timestamp"])})
+    rows.sort(key=lambda x: x["start"])
+    return rows
+
+
+def summarize_counters(fetch_dir, write_dir, pass_json, command) -> str:
+    """JSON lines: per workload, HBM bytes per call (FETCH_SIZE + WRITE_SIZE, calibrated by the copy)."""
+    with open(pass_json) as f:
+        meta = json.loads([l for l in f if l.startswith("{")][-1])
+    names = meta["phases"]
+    per = {}
+    factors = {}
+    lines = ["# HBM traffic per call from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per dispatch).",
+             f"# Commands (repository root): {command}",
+             f"# Each counter is scaled by the factor that maps its reading for a plain copy kernel "
+             f"(elementwise negate of {COPY_BYTES} bytes of bf16) to the {COPY_BYTES} bytes it must read "
+             f"and the {COPY_BYTES} bytes it must write."]
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        groups = _split_phases(_load_counters(d, counter), len(names))
+        if len(groups) != len(names) or any(COPY_KERNEL_TAG not in r["name"] for r in groups[0]):
+            raise SystemExit(f"{counter}: dispatches do not split into the pass's phases {names}")
+        kib = statistics.median(r["value"] for r in groups[0])
+        factors[counter] = COPY_BYTES / (kib * 1024.0)
+        lines.append(f"# {counter}: the copy reads {kib:.0f} KiB per dispatch -> factor {factors[counter]:.4f}")
+        for name, g in zip(names[1:], groups[1:]):
+            per.setdefault(name, {})[counter] = sum(r["value"] for r in g) / PMC_CALLS * 1024.0 * factors[counter]
+            per[name].setdefault("kernels", sorted({_short(r["name"]) for r in g}))
+    for name in names[1:]:
+        e = {"workload": name, "kernels": per[name]["kernels"],
+             "fetch_bytes_per_call": round(per[name]["FETCH_SIZE"]),
+             "write_bytes_per_call": round(per[name]["WRITE_SIZE"]),
+             "hbm_bytes_per_call": round(per[name]["FETCH_SIZE"] + per[name]["WRITE_SIZE"]),
+             "sources": meta["sources"]}
+        lines.append(json.dumps(e))
+    return "\n".join(lines) + "\n"
+
+
+# ----------------------------------------------------------------- main
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--prefill-workload", default=PREFILL_DEFAULT)
+    ap.add_argument("--decode-workload", default=DECODE_DEFAULT)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--no-more", action="store_true", help="skip the larger prefill workloads")
+    ap.add_argument("--pmc-pass", action="store_true", help="short run for a rocprofv3 --pmc pass")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"))
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PASS_JSON"))
+    ap.add_argument("--command", default="", help="command line recorded in a summary")
+    args = ap.parse_args()
+
+    if args.summarize_trace:
+        sys.stdout.write(summarize_trace(*args.summarize_trace, args.command))
+        return 0
+    if args.summarize_counters:
+        sys.stdout.write(summarize_counters(*args.summarize_counters, args.command))
+        return 0
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not supported; "
+              "the kernels run on one MI355X and have no multi-GPU path", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import paged_attention_attn_amd as paa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if not os.path.exists(paa.LIB_PATH):
+        from paged_attention_attn_amd import build
+        build.build()
+
+    line = run_pmc_pass(args, torch, paa) if args.pmc_pass else run_bench(args, torch, paa)
+    print(json.dumps(line), flush=True)
     return 0
 
 
