@@ -74,8 +74,10 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
 
 /*
  * paged_attn_decode_workspace_size — bytes of device workspace that
- * paged_attn_decode needs for these shapes (0 on invalid shapes).  It grows
- * linearly in num_seqs, H, d and max_pages_per_seq.
+ * paged_attn_decode needs for these shapes (0 on invalid shapes).  It is
+ * about (P + num_seqs) * H * (d + 1) * 4 bytes, where P <= 32768 / H is the
+ * number of equal page ranges the decode cuts the cache into: linear in
+ * num_seqs, H and d, and never larger for longer sequences.
  */
 size_t paged_attn_decode_workspace_size(int num_seqs, int H, int d, int page_size, int max_pages_per_seq);
 
@@ -104,8 +106,11 @@ size_t paged_attn_decode_workspace_size(int num_seqs, int H, int d, int page_siz
  * matter); L_s is clamped to [0, max_pages_per_seq * page_size]; a page id
  * outside [0, num_pages) is not dereferenced and its tokens are treated as
  * absent.  L_s == 0 gives O = 0 and LSE = -inf.
- * Internally: a split-KV kernel writes per-split results to the workspace and
- * a separate reduce kernel merges them on the same stream.
+ * Internally: a split-KV kernel cuts the pages of all sequences, laid end to
+ * end, into equal ranges (one workgroup each, independent of the length mix)
+ * and writes one partial result per (range, sequence) pair to the workspace;
+ * a separate reduce kernel merges them on the same stream.  Its cost per
+ * workgroup includes one pass over seq_lens (num_seqs reads).
  */
 int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
                       const int32_t* seq_lens, void* o, float* lse, int num_seqs, int H, int Hkv, int d, int page_size,

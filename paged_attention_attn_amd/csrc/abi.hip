@@ -68,13 +68,40 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
   return launch_status(paa::prefill_f32(q, k, v, o, lse, B, H, Hkv, N, d, causal != 0, scale, stream));
 }
 
+namespace {
+
+// Workspace layout: partial outputs [slots, H, d] fp32, partial LSE [slots, H]
+// fp32, then the [num_seqs, 2] int32 slot range of each sequence and one int32
+// holding the total page count; each region
+// starts on a kWsAlign boundary.  slots = partitions + num_seqs.
+struct DecodeWs {
+  long long slots;
+  size_t o_bytes, lse_bytes, range_bytes;
+  size_t total() const { return o_bytes + lse_bytes + range_bytes; }
+};
+
+bool decode_ws(int num_seqs, int H, int d, int max_pages_per_seq, DecodeWs* w) {
+  long long parts = paa::decode_max_parts(H);
+  const long long pages = (long long)num_seqs * max_pages_per_seq;
+  if (parts > pages) parts = pages;
+  if (parts < 1) parts = 1;
+  w->slots = parts + num_seqs;
+  const long long rows = elems(w->slots, H, 1, 1);
+  if (rows < 0 || elems(rows, d + 1, 4, 1) < 0) return false;
+  w->o_bytes = round_up((size_t)rows * d * sizeof(float), kWsAlign);
+  w->lse_bytes = round_up((size_t)rows * sizeof(float), kWsAlign);
+  w->range_bytes = round_up(((size_t)num_seqs * 2 + 1) * sizeof(int32_t), kWsAlign);
+  return true;
+}
+
+}  // namespace
+
 size_t paged_attn_decode_workspace_size(int num_seqs, int H, int d, int page_size, int max_pages_per_seq) {
   if (num_seqs < 0 || H < 1 || (d != 64 && d != 128) || page_size != 16 || max_pages_per_seq < 0) return 0;
-  if (num_seqs == 0 || max_pages_per_seq == 0) return kWsAlign;
-  const long long splits = paa::decode_max_splits(num_seqs, page_size, max_pages_per_seq);
-  const long long rows = elems(num_seqs, H, splits, 1);
-  if (rows < 0 || elems(rows, d + 1, 4, 1) < 0) return 0;
-  return round_up((size_t)rows * d * sizeof(float), kWsAlign) + round_up((size_t)rows * sizeof(float), kWsAlign);
+  if (num_seqs == 0) return kWsAlign;
+  DecodeWs w;
+  if (!decode_ws(num_seqs, H, d, max_pages_per_seq, &w)) return 0;
+  return w.total();
 }
 
 int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
@@ -87,25 +114,30 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, c
   if (page_size != 16) return ATTN_ERR_UNSUPPORTED_PAGE_SIZE;
   if (H / Hkv > 16) return ATTN_ERR_UNSUPPORTED_GROUP;
   if (num_seqs == 0) return ATTN_OK;  // empty call: nothing is read or written
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !workspace) return ATTN_ERR_NULL_POINTER;
+  // block_table may be NULL only when it has no columns (then it is never read)
+  if (!q || !k_cache || !v_cache || (!block_table && max_pages_per_seq > 0) || !seq_lens || !o || !workspace)
+    return ATTN_ERR_NULL_POINTER;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 4) ||
       !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(lse, 4) || !aligned(workspace, 16))
     return ATTN_ERR_MISALIGNED;
-  if (elems(num_pages, page_size, Hkv, d) < 0 || elems(num_seqs, max_pages_per_seq, 1, 1) < 0)
+  if (elems(num_pages, page_size, Hkv, d) < 0) return ATTN_ERR_TOO_LARGE;
+  // page positions and (sequence, head) rows are 32-bit inside the kernels
+  if ((long long)num_seqs * max_pages_per_seq > 0x7fffffffLL / page_size ||
+      (long long)num_seqs * H > 0x7fffffffLL)
     return ATTN_ERR_TOO_LARGE;
-  if ((long long)max_pages_per_seq * page_size > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
   const size_t need = paged_attn_decode_workspace_size(num_seqs, H, d, page_size, max_pages_per_seq);
   if (need == 0) return ATTN_ERR_TOO_LARGE;
   if (workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
-  const int split_tokens = paa::decode_split_tokens(num_seqs, page_size, max_pages_per_seq);
-  const int max_splits = max_pages_per_seq == 0 ? 1 : paa::decode_max_splits(num_seqs, page_size, max_pages_per_seq);
-  if ((long long)max_splits > 0x7fffffffLL || num_seqs > 65535) return ATTN_ERR_TOO_LARGE;
-  const long long rows = (long long)num_seqs * H * max_splits;
-  float* ws_o = static_cast<float*>(workspace);
-  float* ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up((size_t)rows * d * sizeof(float), kWsAlign));
+  const int parts = paa::decode_parts(num_seqs, H, Hkv, max_pages_per_seq);
+  DecodeWs w;
+  if (!decode_ws(num_seqs, H, d, max_pages_per_seq, &w)) return ATTN_ERR_TOO_LARGE;
+  char* base = static_cast<char*>(workspace);
+  float* ws_o = reinterpret_cast<float*>(base);
+  float* ws_lse = reinterpret_cast<float*>(base + w.o_bytes);
+  int* ws_range = reinterpret_cast<int*>(base + w.o_bytes + w.lse_bytes);
   return launch_status(paa::paged_decode_bf16(q, k_cache, v_cache, block_table, seq_lens, o, lse, num_seqs, H, Hkv, d,
-                                              page_size, max_pages_per_seq, num_pages, scale, ws_o, ws_lse,
-                                              split_tokens, max_splits, stream));
+                                              max_pages_per_seq, num_pages, scale, ws_o, ws_lse, ws_range, parts,
+                                              (int)w.slots, stream));
 }
 
 const char* attn_status_string(int status) {

@@ -13,14 +13,16 @@ hipError_t prefill_bf16(const void* q, const void* k, const void* v, void* o, fl
 hipError_t prefill_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Hkv,
                        int N, int d, bool causal, float scale, hipStream_t stream);
 
-// Tokens per split of the decode partial kernel and the resulting split count
-// per sequence: functions of host-known shapes only (never of seq_lens).
-int decode_split_tokens(int num_seqs, int page_size, int max_pages_per_seq);
-int decode_max_splits(int num_seqs, int page_size, int max_pages_per_seq);
+// Decode partitions: the concatenated page list is cut into `parts` equal
+// ranges, one workgroup each.  Both are functions of host-known shapes only
+// (never of seq_lens).  decode_max_parts(H) bounds decode_parts(...) for every
+// Hkv that divides H with at most 16 query heads per KV head.
+int decode_max_parts(int H);
+int decode_parts(int num_seqs, int H, int Hkv, int max_pages_per_seq);
 
 hipError_t paged_decode_bf16(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
                              const int* seq_lens, void* o, float* lse, int num_seqs, int H, int Hkv, int d,
-                             int page_size, int max_pages_per_seq, int num_pages, float scale, float* ws_o,
-                             float* ws_lse, int split_tokens, int max_splits, hipStream_t stream);
+                             int max_pages_per_seq, int num_pages, float scale, float* ws_o, float* ws_lse,
+                             int* ws_range, int parts, int slots, hipStream_t stream);
 
 }  // namespace paa

@@ -12,15 +12,25 @@
 // decode differs from prefill).
 //
 // Two kernels, stream-ordered, no host synchronisation:
-//  1. decode_partial: one workgroup per (sequence, split of C tokens, block of
-//     KV heads); one wave per KV head handles all query heads of its group.
-//     Per chunk of 2 pages (32 tokens) it reads K straight into the MFMA A
-//     layout, stages V through wave-private LDS for transposed reads, and
-//     keeps a running max / sum / rescaled output (the online softmax of
-//     "Kernel Fusion and Custom Kernels", section 3).  It writes the split's
-//     normalised output and its log-sum-exp to a workspace.
-//  2. decode_reduce: merges the splits of each (sequence, head) with the same
-//     rescaling identity: weights exp(LSE_c - max LSE).
+//  1. decode_partial: the pages of all sequences, laid end to end, are cut
+//     into `parts` equal ranges (one per workgroup, whatever the length mix,
+//     so every workgroup streams the same number of bytes).  A workgroup has
+//     one wave per KV head; each wave walks its range two pages (32 tokens)
+//     at a time, keeps a running max / sum / rescaled output for the query
+//     heads of its group (the online softmax of "Kernel Fusion and Custom
+//     Kernels", section 3) and, where its range leaves a sequence, writes that
+//     sequence's partial output (normalised) and log-sum-exp to the workspace.
+//     The next two pages are loaded while the current two are computed; K is
+//     loaded straight into the MFMA A layout and V is staged through
+//     wave-private LDS for transposed reads.
+//  2. decode_reduce: merges the partials of each (sequence, head) with the
+//     same rescaling identity, weights exp(LSE_c - max LSE).
+//
+// A partial of sequence s written by workgroup (range) r goes to workspace
+// slot s + r: the ranges of one sequence are consecutive and the next
+// sequence starts in the range where this one ends, so slots never collide
+// and there are at most parts + num_seqs of them.  The workgroups holding a
+// sequence's first and last page also record those two slots for the reduce.
 //
 // Bounds: pages past ceil(L / page_size) are never read; slots at or past L
 // (the unused tail of the last page) are masked by index and their V rows are
@@ -36,12 +46,14 @@ namespace paa {
 namespace {
 
 constexpr int kPage = 16;         // tokens per page (the ABI accepts only 16)
-constexpr int kChunkTokens = 32;  // 2 pages per MFMA k-step over tokens
+constexpr int kStepTokens = 32;   // 2 pages per MFMA k-step over tokens
+constexpr int kMaxWaves = 8;      // KV heads (waves) per workgroup
+constexpr int kTargetWaves = 2048;  // waves per launch: 8 per CU on 256 CUs
 
 template <int D>
 struct DecodeLds {
   static constexpr int kStrideV = D + 16;  // bf16 elements; rows 8 dwords apart in bank space
-  static constexpr int kPerWave = kChunkTokens * kStrideV;
+  static constexpr int kPerWave = kStepTokens * kStrideV;
 };
 
 struct DecodeArgs {
@@ -50,9 +62,12 @@ struct DecodeArgs {
   const uint16_t* vc;
   const int* bt;
   const int* lens;
-  float* ws_o;
-  float* ws_lse;
-  int H, Hkv, group, max_pages, num_pages, split_tokens, max_splits, waves;
+  float* ws_o;     // [slots, H, D] partial outputs (normalised)
+  float* ws_lse;   // [slots, H] partial log-sum-exp
+  int* ws_range;   // [S, 2] first and last slot of each sequence, then the total page count
+  uint16_t* o;
+  float* lse;
+  int S, H, Hkv, group, max_pages, num_pages, parts, slots, waves;
   float scale, scale_log2;
 };
 
@@ -63,8 +78,82 @@ __device__ __forceinline__ int seq_len_clamped(const DecodeArgs& a, int s) {
   return L > cap ? cap : L;
 }
 
+__device__ __forceinline__ int pages_of(int L) { return (L + kPage - 1) / kPage; }
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Inclusive prefix sum across the workgroup (nthreads <= 512); `red` holds kMaxWaves ints.
+__device__ __forceinline__ int block_inclusive_scan(int v, int* red) {
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int u = __shfl_up(v, m);
+    if (lane >= m) v += u;
+  }
+  if (lane == 63) red[wave] = v;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += red[w];
+  __syncthreads();
+  return v + before;
+}
+
+// First global page of range r when `total` pages are cut into `parts` ranges.
+__device__ __forceinline__ int range_begin(int r, long long total, int parts) {
+  return (int)(((long long)r * total + parts - 1) / parts);
+}
+
+// A step: up to two pages of one sequence.  Every field is wave-uniform.
+struct Step {
+  int s;      // sequence
+  int p;      // local index of the first page
+  int np;     // pages in the step: 1 or 2 (0 = the range is exhausted)
+  int L;      // tokens of sequence s
+  int n;      // pages of sequence s
+  bool first; // first step of this range's segment of sequence s
+  bool last;  // last step of that segment
+  int pid[2]; // physical pages of the step (filled when its loads are issued; -1 = none)
+};
+
+// Walks the global page range [x, end) of one workgroup, sequence by sequence.
+struct Walker {
+  int s, c, n, L;  // current sequence, its first global page, its page count and length
+  int x, end;      // next global page, end of the range
+
+  __device__ Step next(const DecodeArgs& a) {
+    Step st;
+    st.np = 0;
+    if (x >= end) return st;
+    bool fresh = false;
+    while (x >= c + n) {  // leave finished (or empty) sequences; x < end <= total keeps s < S
+      c += n;
+      if (++s >= a.S) {  // unreachable while the page counts agree with the scan; stop rather than read past
+        x = end;
+        return st;
+      }
+      L = seq_len_clamped(a, s);
+      n = pages_of(L);
+      fresh = true;
+    }
+    st.s = s;
+    st.p = x - c;
+    const int seg_hi = min(end, c + n) - c;
+    st.np = min(2, seg_hi - st.p);
+    st.L = L;
+    st.n = n;
+    st.first = fresh;
+    st.last = st.p + st.np == seg_hi;
+    x += st.np;
+    return st;
+  }
+};
+
 template <int D>
-__global__ __launch_bounds__(512) void decode_partial_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeArgs a) {
   constexpr int kKSteps = D / 32;          // 16x16x32 k-steps over d for the scores
   constexpr int kDBlocks = D / 16;         // 16-wide d blocks of the output
   constexpr int kChunksPerRow = D / 8;     // 16-byte chunks per V row
@@ -72,63 +161,131 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(DecodeArgs a) {
   using Lds = DecodeLds<D>;
 
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_raw[];
+  __shared__ int red[kMaxWaves];
+  __shared__ int found[2];
   const int wave = threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
+  const int nthreads = 64 * a.waves;
   const int c16 = lane / 16;  // 16-lane group
   const int r16 = lane % 16;  // token row (K loads) / head column (scores)
   PAA_LDS uint16_t* vl = (PAA_LDS uint16_t*)lds_raw + wave * Lds::kPerWave;
 
-  const int split = blockIdx.x;
-  const int s = blockIdx.y;
-  const int g = blockIdx.z * a.waves + wave;
-  const int L = seq_len_clamped(a, s);
-  const int t_begin = split * a.split_tokens;
-  if (t_begin >= L) return;  // uniform across the workgroup
-  const int t_end = min(L, t_begin + a.split_tokens);
+  // ---- this workgroup's range of the concatenated page list ----
+  int part_pages = 0;
+  for (int s = threadIdx.x; s < a.S; s += nthreads) part_pages += pages_of(seq_len_clamped(a, s));
+  part_pages = wave_sum(part_pages);
+  if (lane == 0) red[wave] = part_pages;
+  if (threadIdx.x == 0) found[0] = -1;
+  __syncthreads();
+  long long total = 0;
+  for (int w = 0; w < a.waves; ++w) total += red[w];
+  __syncthreads();
+  const int r = blockIdx.x;
+  if (r == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.ws_range[2 * a.S] = (int)total;  // for the reduce
+  const int start = range_begin(r, total, a.parts);
+  const int end = range_begin(r + 1, total, a.parts);
+  if (start >= end) return;  // an empty range (more ranges than pages); uniform across the workgroup
 
-  const size_t tok_stride = (size_t)a.Hkv * D;  // elements between consecutive slots
-  const int* bt_row = a.bt + (size_t)s * a.max_pages;
+  // the sequence holding global page `start`, and that sequence's first global page
+  int carry = 0;
+  for (int base = 0; base < a.S; base += nthreads) {
+    const int s = base + threadIdx.x;
+    const int v = s < a.S ? pages_of(seq_len_clamped(a, s)) : 0;
+    const int incl = block_inclusive_scan(v, red);
+    if (v > 0 && carry + incl - v <= start && start < carry + incl) {
+      found[0] = s;
+      found[1] = carry + incl - v;
+    }
+    if (threadIdx.x == nthreads - 1) red[0] = incl;
+    __syncthreads();
+    carry += red[0];
+    const bool done = found[0] >= 0;
+    __syncthreads();
+    if (done) break;
+  }
+  const int s0 = found[0];
+  const int c0 = found[1];
 
-  // Q^T fragment (B operand): head g*group + r16 (zero beyond the group), d = 32t + 8*c16 + 0..7
-  const int head = g * a.group + r16;
+  const int g = blockIdx.y * a.waves + wave;  // KV head of this wave
+  const int head = g * a.group + r16;         // query head of this lane's score column
   const bool head_ok = r16 < a.group;
-  u32x4_t qf[kKSteps];
-#pragma unroll
-  for (int t = 0; t < kKSteps; ++t)
-    qf[t] = head_ok ? *(const u32x4_t*)(a.q + ((size_t)s * a.H + head) * D + 32 * t + 8 * c16) : u32x4_t{0, 0, 0, 0};
+  const size_t tok_stride = (size_t)a.Hkv * D;  // elements between consecutive slots of a page
 
-  float m_run = -INFINITY;
-  float l_run = 0.f;  // this lane's share of the sum for head r16
-  f32x4_t acc[kDBlocks];
-#pragma unroll
-  for (int nb = 0; nb < kDBlocks; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  Walker wk;
+  wk.s = s0;
+  wk.c = c0;
+  wk.L = seq_len_clamped(a, s0);
+  wk.n = pages_of(wk.L);
+  wk.x = start;
+  wk.end = end;
 
-  for (int t0 = t_begin; t0 < t_end; t0 += kChunkTokens) {
-    u32x4_t kf[2][kKSteps];
-    u32x4_t vr[2][kVChunks];
-    bool page_ok[2];
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const int tp = t0 + kPage * pp;  // first token of this page
-      int pid = -1;
-      if (tp < t_end) pid = bt_row[tp / kPage];
-      page_ok[pp] = pid >= 0 && pid < a.num_pages;
-      const uint16_t* kpage = a.kc + (size_t)(page_ok[pp] ? pid : 0) * kPage * tok_stride + (size_t)g * D;
-      const uint16_t* vpage = a.vc + (size_t)(page_ok[pp] ? pid : 0) * kPage * tok_stride + (size_t)g * D;
+  // block-table window: lane j holds bt[bt_s][bt_base + j]
+  int bt_vec = -1, bt_s = -1, bt_base = 0;
+  auto page_id = [&](const Step& st, int k) -> int {  // physical page of local page st.p + k
+    const int lp = st.p + k;
+    if (st.s != bt_s || lp < bt_base || lp >= bt_base + 64) {
+      bt_s = st.s;
+      bt_base = lp;
+      const int j = lp + lane;
+      bt_vec = j < st.n ? a.bt[(size_t)st.s * a.max_pages + j] : -1;
+    }
+    return __builtin_amdgcn_readlane(bt_vec, lp - bt_base);
+  };
+
+  u32x4_t kf[2][kKSteps], vr[2][kVChunks], qf[kKSteps];
+  u32x4_t kn[2][kKSteps], vn[2][kVChunks], qn[kKSteps];
+
+  // loads of one step into (k, v, q): K in the MFMA A layout, V rows as 16-byte chunks
+  auto issue = [&](Step& st, u32x4_t (&k)[2][kKSteps], u32x4_t (&v)[2][kVChunks], u32x4_t (&qq)[kKSteps]) {
+    if (st.first) {
 #pragma unroll
       for (int t = 0; t < kKSteps; ++t)
-        kf[pp][t] = page_ok[pp] ? *(const u32x4_t*)(kpage + r16 * tok_stride + 32 * t + 8 * c16)
-                                : u32x4_t{0, 0, 0, 0};
+        qq[t] = head_ok ? *(const u32x4_t*)(a.q + ((size_t)st.s * a.H + head) * D + 32 * t + 8 * c16)
+                        : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const int tp = (st.p + pp) * kPage;  // first token of this page
+      const int pid = pp < st.np ? page_id(st, pp) : -1;
+      st.pid[pp] = pid;
+      const bool ok = pid >= 0 && pid < a.num_pages;
+      const uint16_t* kpage = a.kc + (size_t)(ok ? pid : 0) * kPage * tok_stride + (size_t)g * D;
+      const uint16_t* vpage = a.vc + (size_t)(ok ? pid : 0) * kPage * tok_stride + (size_t)g * D;
+#pragma unroll
+      for (int t = 0; t < kKSteps; ++t)
+        k[pp][t] = ok ? *(const u32x4_t*)(kpage + r16 * tok_stride + 32 * t + 8 * c16) : u32x4_t{0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < kVChunks; ++i) {
         const int c = lane + 64 * i;
         const int row = c / kChunksPerRow;
         const int col = (c % kChunksPerRow) * 8;
-        const bool ok = page_ok[pp] && (tp + row < t_end);
-        vr[pp][i] = ok ? *(const u32x4_t*)(vpage + row * tok_stride + col) : u32x4_t{0, 0, 0, 0};
+        v[pp][i] = (ok && tp + row < st.L) ? *(const u32x4_t*)(vpage + row * tok_stride + col)
+                                           : u32x4_t{0, 0, 0, 0};
       }
     }
-    // stage V rows [page][slot][d] into this wave's LDS slice
+  };
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;  // this lane's share of the sum for head r16
+  f32x4_t acc[kDBlocks];
+
+  Step cur = wk.next(a);
+  cur.first = true;
+  issue(cur, kf, vr, qf);
+  int seg_lo = 0;  // local page where the current segment began
+
+  while (cur.np > 0) {
+    Step nxt = wk.next(a);
+    if (cur.first) {
+      seg_lo = cur.p;
+      m_run = -INFINITY;
+      l_run = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < kDBlocks; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    // next step's loads are in flight while this one is computed
+    if (nxt.np > 0) issue(nxt, kn, vn, qn);
+    // stage V rows [page][slot][d] of the current step into this wave's LDS slice
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
@@ -147,16 +304,18 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(DecodeArgs a) {
 #pragma unroll
       for (int t = 0; t < kKSteps; ++t) sc[pp] = mfma16x16x32(kf[pp][t], qf[t], sc[pp]);
     }
-    // mask slots at or past the end and every slot of a page that was not read
+    // mask slots at or past the end, pages outside the step and pages that were not read
     float tmax = -INFINITY;
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp)
+    for (int pp = 0; pp < 2; ++pp) {
+      const bool ok = cur.pid[pp] >= 0 && cur.pid[pp] < a.num_pages;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = t0 + kPage * pp + 4 * c16 + i;
-        if (!page_ok[pp] || tok >= t_end) sc[pp][i] = -INFINITY;
+        const int tok = (cur.p + pp) * kPage + 4 * c16 + i;
+        if (!ok || tok >= cur.L) sc[pp][i] = -INFINITY;
         tmax = fmaxf(tmax, sc[pp][i]);
       }
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float m_new = fmaxf(m_run, tmax);
@@ -196,103 +355,159 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(DecodeArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
 
-  // split result for head r16: normalised output and log-sum-exp
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (head_ok) {
-    // a split whose pages were all rejected has no visible key: zero output, LSE = -inf
-    const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const size_t base = ((size_t)s * a.H + head) * a.max_splits + split;
-    float* wo = a.ws_o + base * D;
+    if (cur.last) {
+      // this range's partial of sequence cur.s for head r16: normalised output and log-sum-exp
+      float l_tot = l_run + __shfl_xor(l_run, 16);
+      l_tot += __shfl_xor(l_tot, 32);
+      const int slot = cur.s + blockIdx.x;
+      if (head_ok) {
+        // a segment whose pages were all rejected has no visible key: zero output, LSE = -inf
+        const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const size_t base = (size_t)slot * a.H + head;
+        float* wo = a.ws_o + base * D;
 #pragma unroll
-    for (int nb = 0; nb < kDBlocks; ++nb) {
-      f32x4_t w = acc[nb] * inv_l;
-      *(f32x4_t*)(wo + 16 * nb + 4 * c16) = w;
+        for (int nb = 0; nb < kDBlocks; ++nb) {
+          f32x4_t w = acc[nb] * inv_l;
+          *(f32x4_t*)(wo + 16 * nb + 4 * c16) = w;
+        }
+        if (c16 == 0) a.ws_lse[base] = l_tot > 0.f ? a.scale * m_run + __logf(l_tot) : -INFINITY;
+      }
+      if (g == 0 && lane == 0) {
+        if (seg_lo == 0) a.ws_range[2 * cur.s] = slot;  // this range holds page 0
+        if (cur.p + cur.np == cur.n) a.ws_range[2 * cur.s + 1] = slot;  // ... and/or the last page
+      }
     }
-    if (c16 == 0) a.ws_lse[base] = l_tot > 0.f ? a.scale * m_run + __logf(l_tot) : -INFINITY;
+    // the step that begins a segment resets the state, whatever the previous one was
+    cur = nxt;
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+#pragma unroll
+      for (int t = 0; t < kKSteps; ++t) kf[pp][t] = kn[pp][t];
+#pragma unroll
+      for (int i = 0; i < kVChunks; ++i) vr[pp][i] = vn[pp][i];
+    }
+    if (cur.first) {
+#pragma unroll
+      for (int t = 0; t < kKSteps; ++t) qf[t] = qn[t];
+    }
   }
 }
 
-// One wave per (sequence, head): merge the splits of that row.
+// One wave per (sequence, head): merge the partials of that row.  The
+// sequence's partials sit in slots first..last; slot j came from range j - s,
+// and a range with no pages (possible when there are more ranges than pages)
+// wrote nothing, so it is skipped.
 template <int D>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a, uint16_t* o, float* lse, int rows) {
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
   constexpr int kPerLane = D / 64;
   const int row = blockIdx.x * 4 + threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
-  if (row >= rows) return;
+  if (row >= a.S * a.H) return;
   const int s = row / a.H;
+  const int h = row % a.H;
   const int L = seq_len_clamped(a, s);
-  const int n = (L + a.split_tokens - 1) / a.split_tokens;
-  const size_t base = (size_t)row * a.max_splits;
-  float mx = -INFINITY;
-  for (int c = 0; c < n; ++c) mx = fmaxf(mx, a.ws_lse[base + c]);
-  float wsum = 0.f;
   float out[kPerLane];
 #pragma unroll
   for (int i = 0; i < kPerLane; ++i) out[i] = 0.f;
-  for (int c = 0; c < n && mx != -INFINITY; ++c) {
-    const float lc = a.ws_lse[base + c];
-    if (lc == -INFINITY) continue;  // split without a visible key
-    const float w = __expf(lc - mx);
-    wsum += w;
-    const float* src = a.ws_o + (base + c) * D;
+  float wsum = 0.f, mx = -INFINITY;
+  if (L > 0) {
+    const long long total = a.ws_range[2 * a.S];
+    // clamped so that a stale or damaged range can never address outside the workspace
+    const int first = min(max(a.ws_range[2 * s], 0), a.slots - 1);
+    const int last = min(max(a.ws_range[2 * s + 1], first), a.slots - 1);
+    const int n = last - first + 1;
+    auto lse_of = [&](int j) -> float {  // LSE of slot first + j, -inf for an empty range
+      const int r = first + j - s;
+      if (r < 0 || r >= a.parts || range_begin(r, total, a.parts) >= range_begin(r + 1, total, a.parts))
+        return -INFINITY;
+      return a.ws_lse[(size_t)(first + j) * a.H + h];
+    };
+    // max over the partials' LSE, 64 at a time
+    for (int c0 = 0; c0 < n; c0 += 64) mx = fmaxf(mx, c0 + lane < n ? lse_of(c0 + lane) : -INFINITY);
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) out[i] = fmaf(w, src[lane + 64 * i], out[i]);
+    for (int m = 1; m < 64; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+    for (int c0 = 0; c0 < n && mx != -INFINITY; c0 += 64) {
+      const int cnt = min(64, n - c0);
+      const float lc = lane < cnt ? lse_of(c0 + lane) : -INFINITY;
+      const float w = lc == -INFINITY ? 0.f : __expf(lc - mx);  // a partial without a visible key weighs 0
+      float ws = w;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) ws += __shfl_xor(ws, m);
+      wsum += ws;
+      // four partials per round, loads issued together; a slot whose weight is 0 (empty range, or no
+      // visible key) may hold anything, so its values are replaced by 0 rather than multiplied by 0
+      for (int j0 = 0; j0 < cnt; j0 += 4) {
+        float v[4][kPerLane], wj[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = min(j0 + u, cnt - 1);
+          wj[u] = j0 + u < cnt ? __shfl(w, j) : 0.f;
+          const float* src = a.ws_o + ((size_t)(first + c0 + j) * a.H + h) * D;
+#pragma unroll
+          for (int i = 0; i < kPerLane; ++i) v[u][i] = src[lane + 64 * i];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < kPerLane; ++i) out[i] = fmaf(wj[u], wj[u] == 0.f ? 0.f : v[u][i], out[i]);
+      }
+    }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  uint16_t* orow = o + (size_t)row * D;
+  uint16_t* orow = a.o + (size_t)row * D;
 #pragma unroll
   for (int i = 0; i < kPerLane; ++i) {
     const uint32_t w = pack_bf16x2(out[i] * inv, 0.f);
     orow[lane + 64 * i] = (uint16_t)(w & 0xffffu);
   }
-  if (lse != nullptr && lane == 0) lse[row] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
+  if (a.lse != nullptr && lane == 0) a.lse[row] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
+}
+
+int waves_for(int Hkv) {
+  for (int w = kMaxWaves; w >= 1; --w)
+    if (Hkv % w == 0) return w;
+  return 1;
 }
 
 template <int D>
-hipError_t launch_decode(DecodeArgs a, uint16_t* o, float* lse, int num_seqs, hipStream_t stream) {
-  int waves = 1;
-  for (int w = 8; w >= 1; --w)
-    if (a.Hkv % w == 0) { waves = w; break; }
-  a.waves = waves;
-  const int lds_bytes = waves * DecodeLds<D>::kPerWave * 2;
-  // allow the largest slice (8 waves) once; thread-safe static initialisation
+hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {
+  a.waves = waves_for(a.Hkv);
+  const int lds_bytes = a.waves * DecodeLds<D>::kPerWave * 2;
+  // allow the largest slice once; thread-safe static initialisation
   static const hipError_t attr = hipFuncSetAttribute((const void*)decode_partial_kernel<D>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     8 * DecodeLds<D>::kPerWave * 2);
+                                                     kMaxWaves * DecodeLds<D>::kPerWave * 2);
   if (attr != hipSuccess) return attr;
-  dim3 grid1((unsigned)a.max_splits, (unsigned)num_seqs, (unsigned)(a.Hkv / waves));
-  hipLaunchKernelGGL(decode_partial_kernel<D>, grid1, dim3(64 * waves), lds_bytes, stream, a);
+  dim3 grid1((unsigned)a.parts, (unsigned)(a.Hkv / a.waves));
+  hipLaunchKernelGGL(decode_partial_kernel<D>, grid1, dim3(64 * a.waves), lds_bytes, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int rows = num_seqs * a.H;
-  hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a, o, lse, rows);
+  const long long rows = (long long)a.S * a.H;
+  hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int decode_split_tokens(int num_seqs, int page_size, int max_pages_per_seq) {
-  const long long max_len = (long long)page_size * max_pages_per_seq;
-  int c = 256;
-  // shorter splits when there would be too few workgroups to fill 256 CUs
-  while (c > kChunkTokens && (long long)num_seqs * ((max_len + c - 1) / c) < 1024) c /= 2;
-  return c;
+int decode_max_parts(int H) {
+  // Hkv >= H / 16 (at most 16 query heads per KV head), so kTargetWaves / Hkv <= 16 * kTargetWaves / H
+  const int by_heads = (16 * kTargetWaves) / (H > 0 ? H : 1);
+  return by_heads < 1 ? 1 : (by_heads > kTargetWaves ? kTargetWaves : by_heads);
 }
 
-int decode_max_splits(int num_seqs, int page_size, int max_pages_per_seq) {
-  const long long max_len = (long long)page_size * max_pages_per_seq;
-  const int c = decode_split_tokens(num_seqs, page_size, max_pages_per_seq);
-  return (int)((max_len + c - 1) / c);
+int decode_parts(int num_seqs, int H, int Hkv, int max_pages_per_seq) {
+  long long p = kTargetWaves / Hkv;
+  const long long pages = (long long)num_seqs * max_pages_per_seq;
+  if (p > pages) p = pages;
+  if (p > decode_max_parts(H)) p = decode_max_parts(H);
+  return p < 1 ? 1 : (int)p;
 }
 
 hipError_t paged_decode_bf16(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
                              const int* seq_lens, void* o, float* lse, int num_seqs, int H, int Hkv, int d,
-                             int page_size, int max_pages_per_seq, int num_pages, float scale, float* ws_o,
-                             float* ws_lse, int split_tokens, int max_splits, hipStream_t stream) {
-  (void)page_size;
+                             int max_pages_per_seq, int num_pages, float scale, float* ws_o, float* ws_lse,
+                             int* ws_range, int parts, int slots, hipStream_t stream) {
   DecodeArgs a{};
   a.q = (const uint16_t*)q;
   a.kc = (const uint16_t*)k_cache;
@@ -301,17 +516,21 @@ hipError_t paged_decode_bf16(const void* q, const void* k_cache, const void* v_c
   a.lens = seq_lens;
   a.ws_o = ws_o;
   a.ws_lse = ws_lse;
+  a.ws_range = ws_range;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.S = num_seqs;
   a.H = H;
   a.Hkv = Hkv;
   a.group = H / Hkv;
   a.max_pages = max_pages_per_seq;
   a.num_pages = num_pages;
-  a.split_tokens = split_tokens;
-  a.max_splits = max_splits;
+  a.parts = parts;
+  a.slots = slots;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
-  if (d == 64) return launch_decode<64>(a, (uint16_t*)o, lse, num_seqs, stream);
-  return launch_decode<128>(a, (uint16_t*)o, lse, num_seqs, stream);
+  if (d == 64) return launch_decode<64>(a, stream);
+  return launch_decode<128>(a, stream);
 }
 
 }  // namespace paa

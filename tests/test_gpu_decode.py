@@ -131,3 +131,58 @@ def test_decode_argument_errors():
         paa.paged_attn_decode(q, kc16, kc16, bt, lens, workspace=ws)
     with pytest.raises(TypeError):
         paa.paged_attn_decode(q, kc16, kc16, bt.long(), lens)
+
+
+def test_decode_one_long_sequence_many_ranges():
+    """One 8000-token sequence: its pages are cut across many workgroup ranges (more than 64 partials)."""
+    w = DecodeWorkload("long1", 1, 32, 8, 128, 8000, 8000, 16, 600)
+    _announce("decode one long sequence")
+    a = decode_inputs(w, seed=12)
+    o, lse, _ = _run(a, 32)
+    ro, rl = _oracle(a)
+    assert_close_bf16(o, ro)
+    assert_close_lse(lse, rl)
+
+
+def test_decode_many_short_sequences():
+    """600 sequences (more than one scan chunk per workgroup) of 0..40 tokens."""
+    S = 600
+    lens = np.random.default_rng(13).integers(0, 41, size=S)
+    w = DecodeWorkload("many", S, 8, 8, 64, 0, 40, 16, 2000)
+    _announce("decode 600 short sequences")
+    a = decode_inputs(w, seed=13, seq_lens=lens)
+    o, lse, _ = _run(a, 8)
+    ro, rl = _oracle(a)
+    empty = lens == 0
+    assert np.all(o[empty] == 0) and np.all(np.isneginf(lse[empty]))
+    assert_close_bf16(o, ro)
+    assert_close_lse(lse, rl)
+
+
+def test_decode_zero_page_table():
+    """max_pages_per_seq == 0: every length clamps to 0, so O = 0 and LSE = -inf."""
+    q = torch.randn((3, 4, 128), device="cuda:0").to(torch.bfloat16)
+    kc = torch.zeros((2, 16, 1, 128), dtype=torch.bfloat16, device="cuda:0")
+    bt = torch.zeros((3, 0), dtype=torch.int32, device="cuda:0")
+    lens = torch.full((3,), 5, dtype=torch.int32, device="cuda:0")
+    lse = torch.empty((3, 4), dtype=torch.float32, device="cuda:0")
+    o, _ = paa.paged_attn_decode(q, kc, kc, bt, lens, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(o.float() == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_decode_repeated_calls_reuse_workspace():
+    """A second call with other lengths on the same workspace gives the oracle's result (no stale partials)."""
+    w = DecodeWorkload("reuse", 5, 16, 4, 128, 1, 900, 16, 400)
+    ws_bytes = paa.paged_attn_decode_workspace_size(5, 16, 128, 16, w.max_pages_per_seq)
+    ws = torch.full((ws_bytes,), 0xFF, dtype=torch.uint8, device="cuda:0")  # NaN-patterned garbage
+    for seed, lens in ((21, [900, 3, 450, 0, 17]), (22, [16, 700, 1, 899, 300])):
+        a = decode_inputs(w, seed=seed, seq_lens=lens)
+        lse = torch.empty((5, 16), dtype=torch.float32, device="cuda:0")
+        o, _ = paa.paged_attn_decode(dev_bf16(a["q"]), dev_bf16(a["k_cache"]), dev_bf16(a["v_cache"]),
+                                     dev_i32(a["block_table"]), dev_i32(a["seq_lens"]), a["scale"], workspace=ws,
+                                     lse=lse)
+        torch.cuda.synchronize()
+        ro, rl = _oracle(a)
+        assert_close_bf16(host_f64(o), ro)
+        assert_close_lse(lse.cpu().numpy().astype(np.float64), rl)
