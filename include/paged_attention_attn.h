@@ -41,7 +41,8 @@ enum {
   ATTN_ERR_MISALIGNED = 6,            /* a pointer breaks the alignment rule above */
   ATTN_ERR_TOO_LARGE = 7,             /* sizes overflow the launch grid or 64-bit offsets */
   ATTN_ERR_UNSUPPORTED_GROUP = 8,     /* decode: more than 16 query heads per KV head */
-  ATTN_ERR_LAUNCH = 9                 /* hipGetLastError reported a failed launch */
+  ATTN_ERR_LAUNCH = 9,                /* hipGetLastError reported a failed launch */
+  ATTN_ERR_INVALID_SCALE = 10         /* scale is not a finite positive number */
 };
 
 /*
@@ -57,7 +58,8 @@ enum {
  *   o   [B, H,   N, d] bf16 (written, rounded to nearest even)
  *   lse [B, H,   N]    fp32 (written; may be NULL to skip)
  * Query head h reads KV head h / (H / Hkv) (grouped-query attention; H must
- * be a multiple of Hkv).  d must be 64 or 128.  B == 0 or N == 0 is a valid
+ * be a multiple of Hkv).  d must be 64 or 128; scale must be finite and
+ * positive (1/sqrt(d) in the pages' formula).  B == 0 or N == 0 is a valid
  * empty call (pointers are then not checked and may be NULL).  Arithmetic: bf16 products, fp32 accumulation and softmax; the
  * probabilities are rounded to bf16 before the product with V.
  */
@@ -99,7 +101,7 @@ size_t paged_attn_decode_workspace_size(int num_seqs, int H, int d, int page_siz
  *               once the stream has passed the call.
  * Token t of sequence s is slot t % page_size of page block_table[s][t / page_size];
  * the query sees all L_s tokens (no mask).  page_size must be 16, d 64 or 128,
- * H / Hkv at most 16.  num_seqs == 0 is a valid empty call (pointers may be NULL).
+ * H / Hkv at most 16, scale finite and positive.  num_seqs == 0 is a valid empty call (pointers may be NULL).
  * Device-side rules (seq_lens and block_table are never read on the host):
  * entries at index >= ceil(L_s / page_size) of a table row are never read;
  * slots at or past L_s are never used (their contents, even NaN, do not

@@ -24,10 +24,15 @@ long long elems(long long a0, long long a1, long long a2, long long a3) {
 
 // Shape checks first: an empty call (B == 0 or N == 0) is valid whatever the
 // pointers are, because nothing is read or written.
+// The kernels track the running maximum of raw (unscaled) scores, which is the
+// maximum of the scaled ones only for a positive scale.
+bool scale_ok(float scale) { return scale > 0.f && scale <= 3.4e38f; }
+
 int check_prefill(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
-                  int Hkv, int N, int d) {
+                  int Hkv, int N, int d, float scale) {
   if (B < 0 || N < 0 || H < 1 || Hkv < 1 || H % Hkv != 0) return ATTN_ERR_INVALID_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_SCALE;
   if (B == 0 || N == 0) return ATTN_OK;
   if (!q || !k || !v || !o) return ATTN_ERR_NULL_POINTER;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
@@ -54,7 +59,7 @@ extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
              int causal, float scale, hipStream_t stream) {
-  const int rc = check_prefill(q, k, v, o, lse, B, H, Hkv, N, d);
+  const int rc = check_prefill(q, k, v, o, lse, B, H, Hkv, N, d, scale);
   if (rc != ATTN_OK) return rc;
   if (B == 0 || N == 0) return ATTN_OK;
   return launch_status(paa::prefill_bf16(q, k, v, o, lse, B, H, Hkv, N, d, causal != 0, scale, stream));
@@ -62,7 +67,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Hkv, int N,
                  int d, int causal, float scale, hipStream_t stream) {
-  const int rc = check_prefill(q, k, v, o, lse, B, H, Hkv, N, d);
+  const int rc = check_prefill(q, k, v, o, lse, B, H, Hkv, N, d, scale);
   if (rc != ATTN_OK) return rc;
   if (B == 0 || N == 0) return ATTN_OK;
   return launch_status(paa::prefill_f32(q, k, v, o, lse, B, H, Hkv, N, d, causal != 0, scale, stream));
@@ -113,6 +118,7 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, c
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
   if (page_size != 16) return ATTN_ERR_UNSUPPORTED_PAGE_SIZE;
   if (H / Hkv > 16) return ATTN_ERR_UNSUPPORTED_GROUP;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_SCALE;
   if (num_seqs == 0) return ATTN_OK;  // empty call: nothing is read or written
   // block_table may be NULL only when it has no columns (then it is never read)
   if (!q || !k_cache || !v_cache || (!block_table && max_pages_per_seq > 0) || !seq_lens || !o || !workspace)
@@ -152,6 +158,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_TOO_LARGE: return "sizes too large for the launch grid or 64-bit offsets";
     case ATTN_ERR_UNSUPPORTED_GROUP: return "unsupported grouping: at most 16 query heads per KV head in decode";
     case ATTN_ERR_LAUNCH: return "kernel launch failed (hipGetLastError)";
+    case ATTN_ERR_INVALID_SCALE: return "invalid scale: it must be a finite positive number";
     default: return "unknown status code";
   }
 }

@@ -14,8 +14,13 @@
 //  * a workgroup is 4 waves; each wave owns 32 query rows of one query head.
 //    The 4 waves cover HPW heads of one GQA group x (4 / HPW) row blocks, so
 //    all of them read the same K/V head and share its LDS tiles.
-//  * K/V tiles of 64 keys are staged global -> VGPR -> LDS, double buffered:
-//    the loads of tile j+1 are in flight while tile j is computed.
+//  * K/V tiles of 64 keys go from global memory straight into LDS
+//    (global_load_lds_dwordx4, no VGPR staging), two stages deep: the loads of
+//    tile j+1 are in flight while tile j is computed, one barrier per tile.
+//    Each 16-byte chunk c of tile row r is stored at chunk position
+//    c ^ swz(r), which keeps both the row-wise K reads and the transposed V
+//    reads below free of LDS bank conflicts; the swizzle is applied by
+//    choosing which chunk each lane fetches, so the loads stay coalesced.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q kept in
 //    VGPRs for the whole kernel), so each lane ends up holding 16 scores of
 //    ONE query row (row l%32; the two half-waves split the keys).  Row max is
@@ -26,10 +31,19 @@
 //    keys is permuted to match where the score MFMA left each probability.
 //    The accumulator of lane l again belongs to query row l%32, so the
 //    rescale by exp(m_old - m_new) is lane-local.
+//  * the running maximum is only moved when some row of the wave grew by more
+//    than kRescaleLog2 (in log2 units); otherwise the old maximum stays the
+//    reference point and probabilities may exceed 1 by up to 2^kRescaleLog2.
+//    Numerator and denominator share the reference point, so the result is
+//    the same softmax; the output and LSE use the reference actually kept.
 //  * causal: tiles entirely above the diagonal of the workgroup are never
 //    loaded; a wave whose rows all precede a tile skips its math; only tiles
 //    crossing the diagonal (or the ragged end of the sequence) are masked.
-//    Work units are issued heaviest first.
+//    Work units are issued heaviest first, and consecutive units (which the
+//    dispatcher spreads over the 8 XCDs) differ in their (batch, KV head), so
+//    each XCD's L2 keeps serving the same K/V heads.
+
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -41,18 +55,30 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 32;
-constexpr int kBc = 64;  // keys per tile
+constexpr int kBc = 64;               // keys per tile
+constexpr float kRescaleLog2 = 8.0f;  // lazy rescale threshold (probabilities stay <= 256)
 
 template <int D>
-struct PrefillLds {
-  // K rows padded by 16 bytes: 16 consecutive rows read at one column hit distinct banks.
-  static constexpr int kStrideK = D + 8;    // in bf16 elements
-  // V rows padded by 64 bytes: the 4-row blocks of the transposed reads hit distinct banks.
-  static constexpr int kStrideV = D + 32;
-  static constexpr int kTileK = kBc * kStrideK;
-  static constexpr int kTileV = kBc * kStrideV;
-  static constexpr int kBytes = 2 * (kTileK + kTileV) * 2;  // double buffered, 2 bytes each
+struct TileLayout {
+  static constexpr int kCpr = D / 8;                       // 16-byte chunks per row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileBytes = kBc * kRowBytes;       // one K or V tile
+  static constexpr int kRowsPerBlock = 64 / kCpr;          // rows of one wave-wide 16 B/lane load
+  static constexpr int kBlocks = kBc / kRowsPerBlock;      // such loads per tile
+  static constexpr int kBlocksPerWave = kBlocks / kWaves;
+  static_assert(kBlocks % kWaves == 0, "tile rows must split evenly over the waves");
 };
+
+// Chunk position swizzle of tile row r (a function of r % 16 only).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    return 4 * (r & 3) + ((r >> 2) & 3);
+  } else {
+    const int x = (r >> 1) & 7;  // bit-reversed
+    return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1);
+  }
+}
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -65,26 +91,31 @@ struct PrefillArgs {
   int units_per_qt;  // B * Hkv * (group / HPW)
   float scale;       // softmax scale applied to Q.K
   float scale_log2;  // scale * log2(e)
+  float rescale_raw; // kRescaleLog2 / scale_log2: the lazy rescale threshold in raw score units
 };
 
 template <int D, bool CAUSAL, int HPW>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a) {
-  constexpr int kRowBlocks = kWaves / HPW;            // row blocks of 32 per head in a workgroup
+  constexpr int kRowBlocks = kWaves / HPW;             // row blocks of 32 per head in a workgroup
   constexpr int kTileRows = kRowBlocks * kRowsPerWave; // query rows per head in a workgroup
-  constexpr int kChunksPerRow = D / 8;                // 16-byte chunks in one K/V row
-  constexpr int kChunksPerThread = kBc * kChunksPerRow / kThreads;
-  constexpr int kKSteps = D / 16;                     // MFMA k-steps over the head dim
-  constexpr int kDBlocks = D / 32;                    // 32-wide blocks of the head dim in O
-  using L = PrefillLds<D>;
+  constexpr int kKSteps = D / 16;                      // MFMA k-steps over the head dim
+  constexpr int kDBlocks = D / 32;                     // 32-wide blocks of the head dim in O
+  using T = TileLayout<D>;
 
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds_raw[];
-  PAA_LDS uint16_t* lds = (PAA_LDS uint16_t*)lds_raw;
+  // Two K stages and two V stages, as separate objects so the compiler can tell that the loads
+  // landing in one stage never alias the reads of the other.
+  __shared__ __attribute__((aligned(1024))) char k_st0[T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_st1[T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_st0[T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_st1[T::kTileBytes];
 
   const int tid = threadIdx.x;
   const int wave = tid / 64;
   const int lane = tid % 64;
   const int half = lane / 32;  // which half-wave
   const int l32 = lane % 32;
+  const int gi = lane % 16;
+  const int colhalf = (lane / 16) % 2;
 
   // ---- work unit: heaviest query tiles first ----
   const int unit = blockIdx.x;
@@ -107,6 +138,28 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   const uint16_t* kh = a.k + ((size_t)b * a.Hkv + g) * N * D;
   const uint16_t* vh = a.v + ((size_t)b * a.Hkv + g) * N * D;
 
+  // ---- key tiles: the workgroup loads [0, n_tiles); this wave computes [0, n_act) ----
+  const int kv_end = CAUSAL ? min(a.N, q0_tile + kTileRows) : a.N;
+  const int n_tiles = (kv_end + kBc - 1) / kBc;
+  const int n_act = CAUSAL ? min(n_tiles, (q0 + kRowsPerWave - 1) / kBc + 1) : n_tiles;
+
+  // ---- direct global -> LDS load of one tile of K or V; this wave fetches kBlocksPerWave 1 KB blocks ----
+  auto dma = [&](const uint16_t* src, int j, PAA_LDS char* dst) {
+#pragma unroll
+    for (int i = 0; i < T::kBlocksPerWave; ++i) {
+      const int blk = wave * T::kBlocksPerWave + i;
+      const int r = blk * T::kRowsPerBlock + lane / T::kCpr;  // tile row written by this lane
+      const int c = (lane % T::kCpr) ^ swz<D>(r);             // data chunk stored at this lane's position
+      const int key = min(j * kBc + r, a.N - 1);  // rows past the end repeat a valid row; they are masked
+      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)key * D + c * 8), (PAA_LDS void*)(dst + blk * 1024),
+                                       16, 0, 0);
+    }
+  };
+
+  dma(kh, 0, (PAA_LDS char*)k_st0);
+  dma(vh, 0, (PAA_LDS char*)v_st0);
+  if (n_tiles > 1) dma(kh, 1, (PAA_LDS char*)k_st1);
+
   // ---- Q fragment (B operand of S^T = K Q^T): row my_row, d = 16t + 8*half + 0..7 ----
   u32x4_t qf[kKSteps];
 #pragma unroll
@@ -117,145 +170,150 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
       qf[t] = u32x4_t{0, 0, 0, 0};
   }
 
-  // ---- key range of this workgroup ----
-  const int kv_end = CAUSAL ? min(a.N, q0_tile + kTileRows) : a.N;
-  const int n_tiles = (kv_end + kBc - 1) / kBc;
-
-  // ---- staging: thread owns chunks tid + 256*i of the [64 x D] tile ----
-  u32x4_t kreg[kChunksPerThread], vreg[kChunksPerThread];
-  auto load_tile = [&](int j) {
+  // ---- per-lane LDS byte offsets inside a tile ----
+  // K (A operand of the score MFMA): row l32 (+32 for the second key block), chunk 2t + half
+  int koff[kKSteps];
 #pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-      const int c = tid + kThreads * i;
-      const int r = c / kChunksPerRow;
-      const int col = (c % kChunksPerRow) * 8;
-      const int key = j * kBc + r;
-      if (key < a.N) {
-        kreg[i] = *(const u32x4_t*)(kh + (size_t)key * D + col);
-        vreg[i] = *(const u32x4_t*)(vh + (size_t)key * D + col);
-      } else {
-        kreg[i] = u32x4_t{0, 0, 0, 0};
-        vreg[i] = u32x4_t{0, 0, 0, 0};
-      }
+  for (int t = 0; t < kKSteps; ++t) koff[t] = l32 * T::kRowBytes + (((2 * t + half) ^ swz<D>(l32)) * 16);
+  // V (transposed reads): row 4*half + gi/4 (+8 for the second read, +16 per k-step), 8 bytes at column
+  // 32*db + 16*colhalf + 4*(gi%4)
+  int voff[kDBlocks][2];
+#pragma unroll
+  for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = 4 * half + gi / 4 + 8 * e;
+      const int col = 32 * db + 16 * colhalf + 4 * (gi % 4);
+      voff[db][e] = r * T::kRowBytes + (((col / 8) ^ swz<D>(r)) * 16) + (col % 8) * 2;
     }
-  };
-  auto store_tile = [&](int buf) {
-    PAA_LDS uint16_t* kt = lds + buf * (L::kTileK + L::kTileV);
-    PAA_LDS uint16_t* vt = kt + L::kTileK;
+
+  // S^T block mb of one tile: keys k0 + 32mb + 8(i/4) + 4*half + i%4, query my_row
+  auto scores = [&](const PAA_LDS char* kt, f32x16_t (&s)[2]) {
 #pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-      const int c = tid + kThreads * i;
-      const int r = c / kChunksPerRow;
-      const int col = (c % kChunksPerRow) * 8;
-      *(PAA_LDS u32x4_t*)(kt + r * L::kStrideK + col) = kreg[i];
-      *(PAA_LDS u32x4_t*)(vt + r * L::kStrideV + col) = vreg[i];
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int t = 0; t < kKSteps; ++t) {
+        const u32x4_t kf = *(const PAA_LDS u32x4_t*)(kt + koff[t] + mb * 32 * T::kRowBytes);
+        s[mb] = t == 0 ? mfma32x32x16(kf, qf[t], f32x16_t{}) : mfma32x32x16(kf, qf[t], s[mb]);
+      }
     }
   };
 
   // ---- running state of row my_row ----
-  float m_run = -INFINITY;  // running max of raw scores (before scale)
+  float m_run = -INFINITY;  // reference maximum of raw scores (before scale)
   float l_run = 0.f;        // this lane's share of the running sum
   f32x16_t acc[kDBlocks];
 #pragma unroll
   for (int db = 0; db < kDBlocks; ++db)
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  load_tile(0);
-  store_tile(0);
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1);
-    __syncthreads();
-
+  // Softmax of tile j, first half: mask, row max, and a rescale of the state when the reference
+  // maximum moves.  Returns -reference * scale_log2, the exponent shift of this tile.
+  auto softmax_prep = [&](int j, f32x16_t (&s)[2]) -> float {
     const int k0 = j * kBc;
-    const bool wave_active = !CAUSAL || (k0 <= q0 + kRowsPerWave - 1);
-    if (wave_active) {
-      const PAA_LDS uint16_t* kt = lds + buf * (L::kTileK + L::kTileV);
-      const PAA_LDS uint16_t* vt = kt + L::kTileK;
-
-      // S^T block mb: keys k0 + 32mb + 8(i/4) + 4*half + i%4, query my_row
-      f32x16_t s[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        for (int i = 0; i < 16; ++i) s[mb][i] = 0.f;
-#pragma unroll
-        for (int t = 0; t < kKSteps; ++t) {
-          const u32x4_t kf = *(const PAA_LDS u32x4_t*)(kt + (32 * mb + l32) * L::kStrideK + 16 * t + 8 * half);
-          s[mb] = mfma32x32x16(kf, qf[t], s[mb]);
-        }
-      }
-
-      // mask: causal keys after the row, and keys past the end of the sequence
-      const bool need_mask = (CAUSAL && (k0 + kBc - 1 > q0)) || (k0 + kBc > a.N);
-      if (need_mask) {
-        const int lim = CAUSAL ? min(my_row, a.N - 1) : a.N - 1;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + 32 * mb + 8 * (i / 4) + 4 * half + (i % 4);
-            if (key > lim) s[mb][i] = -INFINITY;
-          }
-      }
-
-      // online softmax update for row my_row
-      float tmax = -INFINITY;
+    // mask: causal keys after the row, and keys past the end of the sequence
+    const bool need_mask = (CAUSAL && (k0 + kBc - 1 > q0)) || (k0 + kBc > a.N);
+    if (need_mask) {
+      const int lim = CAUSAL ? min(my_row, a.N - 1) : a.N - 1;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[mb][i]);
-      tmax = fmaxf(tmax, swap_halves(tmax, half));
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2((m_run - m_use) * a.scale_log2);
-      const float neg_ms = -m_use * a.scale_log2;
-      m_run = m_new;
-
-      u32x4_t pf[4];  // B operands of the 4 PV k-steps (16 keys each)
-      float psum = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        float p[16];
-#pragma unroll
         for (int i = 0; i < 16; ++i) {
-          p[i] = fast_exp2(fmaf(s[mb][i], a.scale_log2, neg_ms));
-          psum += p[i];
+          const int key = k0 + 32 * mb + 8 * (i / 4) + 4 * half + (i % 4);
+          if (key > lim) s[mb][i] = -INFINITY;
         }
+    }
+    float tmax = -INFINITY;
 #pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-          pf[2 * mb + sh] = u32x4_t{pack_bf16x2(p[8 * sh + 0], p[8 * sh + 1]), pack_bf16x2(p[8 * sh + 2], p[8 * sh + 3]),
-                                    pack_bf16x2(p[8 * sh + 4], p[8 * sh + 5]), pack_bf16x2(p[8 * sh + 6], p[8 * sh + 7])};
-        }
-      }
-      l_run = l_run * alpha + psum;
-
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int db = 0; db < kDBlocks; ++db) {
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[mb][i]);
+    tmax = fmaxf(tmax, swap_halves(tmax, half));
+    // move the reference maximum only when some row of the wave outgrew it by the threshold
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + a.rescale_raw) != 0) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_run - m_new) * a.scale_log2);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-      }
+    }
+    return m_run == -INFINITY ? 0.f : -m_run * a.scale_log2;
+  };
 
-      // O^T += V^T P^T.  PV k-step ks covers keys 16ks..16ks+15 of the tile; logical k = 8*half + jj
-      // maps to key 16ks + 8(jj/4) + 4*half + jj%4.  A operand via two transposed reads.
-      const int grp = lane / 16;       // 16-lane group
-      const int gi = lane % 16;        // lane within the group
-      const int colhalf = grp % 2;     // which 16 columns of the 32-wide d block
+  // Softmax of tile j, second half (no branches, so it can interleave with MFMAs): probabilities
+  // relative to the reference, their row sum, and the bf16 B operands of the PV product.
+  auto softmax_exp = [&](const f32x16_t (&s)[2], float neg_ms, u32x4_t (&pf)[4]) {
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int db = 0; db < kDBlocks; ++db) {
+    for (int mb = 0; mb < 2; ++mb) {
+      float p[16];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int krow = 16 * ks + 4 * half + gi / 4;
-          const int dcol = 32 * db + 16 * colhalf + 4 * (gi % 4);
-          const u32x2_t lo = lds_read_tr16(vt + krow * L::kStrideV + dcol);
-          const u32x2_t hi = lds_read_tr16(vt + (krow + 8) * L::kStrideV + dcol);
-          const u32x4_t vf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-          acc[db] = mfma32x32x16(vf, pf[ks], acc[db]);
-        }
+      for (int i = 0; i < 16; ++i) {
+        p[i] = fast_exp2(fmaf(s[mb][i], a.scale_log2, neg_ms));
+        ps[i % 4] += p[i];
+      }
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh)
+        pf[2 * mb + sh] = u32x4_t{pack_bf16x2(p[8 * sh + 0], p[8 * sh + 1]), pack_bf16x2(p[8 * sh + 2], p[8 * sh + 3]),
+                                  pack_bf16x2(p[8 * sh + 4], p[8 * sh + 5]), pack_bf16x2(p[8 * sh + 6], p[8 * sh + 7])};
+    }
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+
+  // O^T += V^T P^T.  PV k-step ks covers keys 16ks..16ks+15 of the tile; logical k = 8*half + jj maps
+  // to key 16ks + 8(jj/4) + 4*half + jj%4.  A operand via two transposed reads.
+  auto pv = [&](const PAA_LDS char* vt, const u32x4_t (&pf)[4]) {
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x2_t lo = lds_read_tr16((const PAA_LDS uint16_t*)(vt + voff[db][0] + 16 * ks * T::kRowBytes));
+        const u32x2_t hi = lds_read_tr16((const PAA_LDS uint16_t*)(vt + voff[db][1] + 16 * ks * T::kRowBytes));
+        acc[db] = mfma32x32x16(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pf[ks], acc[db]);
       }
     }
+  };
 
-    if (j + 1 < n_tiles) store_tile(buf ^ 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16_t s_cur[2];
+  scores((const PAA_LDS char*)k_st0, s_cur);  // tile 0 is visible to every row
+  __syncthreads();                            // everyone is done with K stage 0 before it is refilled
+
+  // One tile: loads of K_{j+2} and V_{j+1} are issued first; then the scores of tile j+1 (MFMA) are
+  // computed next to the softmax of tile j (VALU), then O += P_j V_j.  ST = j % 2 is a template
+  // constant so every LDS address is a register offset plus an immediate.
+  auto tile = [&](auto st_tag, int j) {
+    constexpr int ST = decltype(st_tag)::value;
+    PAA_LDS char* k_this = ST == 0 ? (PAA_LDS char*)k_st0 : (PAA_LDS char*)k_st1;  // held K_j: free now
+    PAA_LDS char* k_next = ST == 0 ? (PAA_LDS char*)k_st1 : (PAA_LDS char*)k_st0;  // holds K_{j+1}
+    PAA_LDS char* v_this = ST == 0 ? (PAA_LDS char*)v_st0 : (PAA_LDS char*)v_st1;  // holds V_j
+    PAA_LDS char* v_next = ST == 0 ? (PAA_LDS char*)v_st1 : (PAA_LDS char*)v_st0;  // held V_{j-1}: free now
+    if (j + 2 < n_tiles) dma(kh, j + 2, k_this);
+    if (j + 1 < n_tiles) dma(vh, j + 1, v_next);
+    if (j < n_act) {
+      const float neg_ms = softmax_prep(j, s_cur);
+      // one branch-free block: scores of tile j+1 (computed even past the last active tile, where they
+      // are simply dropped), exponentials of tile j, then O += P_j V_j
+      f32x16_t s_nxt[2];
+      scores(k_next, s_nxt);
+      u32x4_t pf[4];
+      softmax_exp(s_cur, neg_ms, pf);
+      pv(v_this, pf);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) s_cur[mb] = s_nxt[mb];
+    }
+    // the next tiles have landed (own loads, then everyone's) and every wave is done with these stages
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  for (int j = 0; j < n_tiles; j += 2) {
+    tile(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, j + 1);
   }
 
   // ---- epilogue: O = acc / l, LSE = scale * m + ln(l) ----
@@ -286,13 +344,7 @@ hipError_t launch_prefill(const PrefillArgs& base, hipStream_t stream) {
   a.units_per_qt = a.B * a.Hkv * ((a.H / a.Hkv) / HPW);
   const long long units = (long long)a.n_qtiles * a.units_per_qt;
   if (units > 0x7fffffffLL) return hipErrorInvalidValue;
-  constexpr int lds_bytes = PrefillLds<D>::kBytes;
-  // raise the dynamic LDS limit once per instantiation (thread-safe static initialisation)
-  static const hipError_t attr = hipFuncSetAttribute((const void*)prefill_bf16_kernel<D, CAUSAL, HPW>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, HPW>), dim3((unsigned)units), dim3(kThreads), lds_bytes,
-                     stream, a);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, HPW>), dim3((unsigned)units), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -320,6 +372,7 @@ hipError_t prefill_bf16(const void* q, const void* k, const void* v, void* o, fl
   a.N = N;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
+  a.rescale_raw = kRescaleLog2 / a.scale_log2;
   if (d == 64) return causal ? dispatch_hpw<64, true>(a, stream) : dispatch_hpw<64, false>(a, stream);
   return causal ? dispatch_hpw<128, true>(a, stream) : dispatch_hpw<128, false>(a, stream);
 }

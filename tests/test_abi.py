@@ -12,7 +12,7 @@ import pytest
 import paged_attention_attn_amd as paa
 from paged_attention_attn_amd import _binding
 
-ATTN_OK, NULL, SHAPE, HEAD_DIM, PAGE, WS, ALIGN, LARGE, GROUP, LAUNCH = range(10)
+ATTN_OK, NULL, SHAPE, HEAD_DIM, PAGE, WS, ALIGN, LARGE, GROUP, LAUNCH, SCALE = range(11)
 
 
 @pytest.fixture(scope="module")
@@ -32,8 +32,8 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for code in range(10):
-        assert paa.attn_status_string(code)
+    for code in range(11):
+        assert paa.attn_status_string(code) != "unknown status code"
     assert paa.attn_status_string(12345) == "unknown status code"
 
 
@@ -50,6 +50,10 @@ P = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails valid
     ((P, P, P, P, None, 0, 2, 2, 8, 64, 1, 0.1), ATTN_OK),   # empty batch: nothing to launch
     ((None, None, None, None, None, 0, 2, 2, 8, 64, 1, 0.1), ATTN_OK),  # empty: pointers unused
     ((P, P, P, P, None, 1, 2, 2, 0, 64, 1, 0.1), ATTN_OK),   # empty sequence
+    ((P, P, P, P, None, 1, 2, 2, 8, 64, 1, 0.0), SCALE),
+    ((P, P, P, P, None, 1, 2, 2, 8, 64, 1, -0.125), SCALE),
+    ((P, P, P, P, None, 1, 2, 2, 8, 64, 1, float("nan")), SCALE),
+    ((P, P, P, P, None, 1, 2, 2, 8, 64, 1, float("inf")), SCALE),
 ])
 def test_prefill_validation(L, args, code):
     assert L.attn_fwd(*args, None) == code
@@ -74,6 +78,8 @@ def test_decode_validation(L):
     assert call(wsb=ws - 1) == WS
     assert call(H=64, Hkv=2, wsb=10 ** 9) == GROUP
     assert call(q=ctypes.c_void_p(0x10004)) == ALIGN
+    assert call(scale=0.0) == SCALE
+    assert call(scale=float("nan")) == SCALE
     assert call(S=0) == ATTN_OK
     assert call(S=0, q=None, ws=None) == ATTN_OK  # empty: pointers unused
 
