@@ -52,9 +52,6 @@ namespace paa {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerWave = 32;
 constexpr int kBc = 64;               // keys per tile
 constexpr float kRescaleLog2 = 8.0f;  // lazy rescale threshold (probabilities stay <= 256)
 
@@ -65,9 +62,35 @@ struct TileLayout {
   static constexpr int kTileBytes = kBc * kRowBytes;       // one K or V tile
   static constexpr int kRowsPerBlock = 64 / kCpr;          // rows of one wave-wide 16 B/lane load
   static constexpr int kBlocks = kBc / kRowsPerBlock;      // such loads per tile
-  static constexpr int kBlocksPerWave = kBlocks / kWaves;
-  static_assert(kBlocks % kWaves == 0, "tile rows must split evenly over the waves");
 };
+
+// vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4, lgkmcnt 11:8).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for the tile loop.  The only LDS writes in the loop are direct global->LDS
+// loads, whose completion is tracked by vmcnt and awaited explicitly (wait_vmcnt) just before; a
+// workgroup-scope fence would make the compiler wait for every one of them (vmcnt(0)), which
+// would drain the load ring.  The wavefront-scope fences keep the compiler from moving memory
+// accesses across the barrier; lgkmcnt(0) retires this wave's own LDS reads first.
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0) only
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int I, int S, typename F>
+__device__ __forceinline__ void for_stages(F& f, int j, int n) {
+  if (j + I < n) {
+    f(std::integral_constant<int, I>{}, j + I);
+    if constexpr (I + 1 < S) for_stages<I + 1, S>(f, j, n);
+  }
+}
 
 // Chunk position swizzle of tile row r (a function of r % 16 only).
 template <int D>
@@ -94,20 +117,54 @@ struct PrefillArgs {
   float rescale_raw; // kRescaleLog2 / scale_log2: the lazy rescale threshold in raw score units
 };
 
-template <int D, bool CAUSAL, int HPW>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a) {
-  constexpr int kRowBlocks = kWaves / HPW;             // row blocks of 32 per head in a workgroup
-  constexpr int kTileRows = kRowBlocks * kRowsPerWave; // query rows per head in a workgroup
+// WAVES waves per workgroup, RB blocks of 32 query rows per wave, STAGES-deep K and V rings in LDS.
+template <int D, int WAVES, int RB, int STAGES>
+struct PrefillCfg {
+  static constexpr int kBlocksPerWave = TileLayout<D>::kBlocks / WAVES;  // 1 KB loads per wave per tile
+  static_assert(TileLayout<D>::kBlocks % WAVES == 0, "tile rows must split evenly over the waves");
+  static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
+  static_assert(RB == 1 || RB == 2, "one or two 32-row blocks per wave");
+  static constexpr int kRowsPerWave = 32 * RB;
+  // loads a wave may still have in flight, beyond the ones the next tile needs, at the end of a tile
+  static constexpr int kInFlightAfter = (STAGES - 2) * 2 * kBlocksPerWave;
+};
+
+template <int D, bool CAUSAL, int HPW, int WAVES, int RB, int STAGES>
+__global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_kernel(
+    PrefillArgs a) {
+  using T = TileLayout<D>;
+  using C = PrefillCfg<D, WAVES, RB, STAGES>;
+  constexpr int kWaveRows = C::kRowsPerWave;
+  constexpr int kRowBlocks = WAVES / HPW;              // waves per head in a workgroup
+  constexpr int kTileRows = kRowBlocks * kWaveRows;    // query rows per head in a workgroup
   constexpr int kKSteps = D / 16;                      // MFMA k-steps over the head dim
   constexpr int kDBlocks = D / 32;                     // 32-wide blocks of the head dim in O
-  using T = TileLayout<D>;
 
-  // Two K stages and two V stages, as separate objects so the compiler can tell that the loads
-  // landing in one stage never alias the reads of the other.
+  // K and V rings, one LDS object per stage, so the compiler can tell that loads landing in one
+  // stage never alias the reads of another (stages beyond STAGES are never referenced).
   __shared__ __attribute__((aligned(1024))) char k_st0[T::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char k_st1[T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_st2[T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_st3[T::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char v_st0[T::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char v_st1[T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_st2[T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_st3[T::kTileBytes];
+  auto kst = [&](auto i_tag) -> PAA_LDS char* {
+    constexpr int i = decltype(i_tag)::value % STAGES;
+    if constexpr (i == 0) return (PAA_LDS char*)k_st0;
+    else if constexpr (i == 1) return (PAA_LDS char*)k_st1;
+    else if constexpr (i == 2) return (PAA_LDS char*)k_st2;
+    else return (PAA_LDS char*)k_st3;
+  };
+  auto vst = [&](auto i_tag) -> PAA_LDS char* {
+    constexpr int i = decltype(i_tag)::value % STAGES;
+    if constexpr (i == 0) return (PAA_LDS char*)v_st0;
+    else if constexpr (i == 1) return (PAA_LDS char*)v_st1;
+    else if constexpr (i == 2) return (PAA_LDS char*)v_st2;
+    else return (PAA_LDS char*)v_st3;
+  };
+  using I0 = std::integral_constant<int, 0>;
 
   const int tid = threadIdx.x;
   const int wave = tid / 64;
@@ -130,8 +187,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
 
   const int head = g * group + hsub * HPW + wave / kRowBlocks;
   const int q0_tile = qt * kTileRows;
-  const int q0 = q0_tile + (wave % kRowBlocks) * kRowsPerWave;  // first row of this wave
-  const int my_row = q0 + l32;
+  const int q0 = q0_tile + (wave % kRowBlocks) * kWaveRows;  // first row of this wave; block rb starts at q0 + 32rb
 
   const size_t N = a.N;
   const uint16_t* qh = a.q + ((size_t)b * a.H + head) * N * D;
@@ -141,13 +197,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
   // ---- key tiles: the workgroup loads [0, n_tiles); this wave computes [0, n_act) ----
   const int kv_end = CAUSAL ? min(a.N, q0_tile + kTileRows) : a.N;
   const int n_tiles = (kv_end + kBc - 1) / kBc;
-  const int n_act = CAUSAL ? min(n_tiles, (q0 + kRowsPerWave - 1) / kBc + 1) : n_tiles;
+  const int n_act = CAUSAL ? min(n_tiles, (q0 + kWaveRows - 1) / kBc + 1) : n_tiles;
 
   // ---- direct global -> LDS load of one tile of K or V; this wave fetches kBlocksPerWave 1 KB blocks ----
   auto dma = [&](const uint16_t* src, int j, PAA_LDS char* dst) {
 #pragma unroll
-    for (int i = 0; i < T::kBlocksPerWave; ++i) {
-      const int blk = wave * T::kBlocksPerWave + i;
+    for (int i = 0; i < C::kBlocksPerWave; ++i) {
+      const int blk = wave * C::kBlocksPerWave + i;
       const int r = blk * T::kRowsPerBlock + lane / T::kCpr;  // tile row written by this lane
       const int c = (lane % T::kCpr) ^ swz<D>(r);             // data chunk stored at this lane's position
       const int key = min(j * kBc + r, a.N - 1);  // rows past the end repeat a valid row; they are masked
@@ -156,18 +212,25 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     }
   };
 
-  dma(kh, 0, (PAA_LDS char*)k_st0);
-  dma(vh, 0, (PAA_LDS char*)v_st0);
-  if (n_tiles > 1) dma(kh, 1, (PAA_LDS char*)k_st1);
+  // prologue loads: K_0 .. K_{STAGES-1} and V_0 .. V_{STAGES-2}
+  auto prologue = [&](auto i_tag, int j) {
+    dma(kh, j, kst(i_tag));
+    if (decltype(i_tag)::value + 1 < STAGES) dma(vh, j, vst(i_tag));
+  };
+  for_stages<0, STAGES>(prologue, 0, n_tiles);
 
-  // ---- Q fragment (B operand of S^T = K Q^T): row my_row, d = 16t + 8*half + 0..7 ----
-  u32x4_t qf[kKSteps];
+  // ---- Q fragments (B operand of S^T = K Q^T): row q0 + 32rb + l32, d = 16t + 8*half + 0..7 ----
+  u32x4_t qf[RB][kKSteps];
 #pragma unroll
-  for (int t = 0; t < kKSteps; ++t) {
-    if (my_row < a.N)
-      qf[t] = *(const u32x4_t*)(qh + (size_t)my_row * D + 16 * t + 8 * half);
-    else
-      qf[t] = u32x4_t{0, 0, 0, 0};
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = q0 + 32 * rb + l32;
+#pragma unroll
+    for (int t = 0; t < kKSteps; ++t) {
+      if (row < a.N)
+        qf[rb][t] = *(const u32x4_t*)(qh + (size_t)row * D + 16 * t + 8 * half);
+      else
+        qf[rb][t] = u32x4_t{0, 0, 0, 0};
+    }
   }
 
   // ---- per-lane LDS byte offsets inside a tile ----
@@ -187,34 +250,42 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
       voff[db][e] = r * T::kRowBytes + (((col / 8) ^ swz<D>(r)) * 16) + (col % 8) * 2;
     }
 
-  // S^T block mb of one tile: keys k0 + 32mb + 8(i/4) + 4*half + i%4, query my_row
-  auto scores = [&](const PAA_LDS char* kt, f32x16_t (&s)[2]) {
+  // S^T of one tile for every row block: block (rb, mb) holds keys k0 + 32mb + 8(i/4) + 4*half + i%4
+  // of query row q0 + 32rb + l32.  Each K fragment read from LDS feeds RB MFMAs.
+  auto scores = [&](const PAA_LDS char* kt, f32x16_t (&s)[RB][2]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int t = 0; t < kKSteps; ++t) {
         const u32x4_t kf = *(const PAA_LDS u32x4_t*)(kt + koff[t] + mb * 32 * T::kRowBytes);
-        s[mb] = t == 0 ? mfma32x32x16(kf, qf[t], f32x16_t{}) : mfma32x32x16(kf, qf[t], s[mb]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          s[rb][mb] = t == 0 ? mfma32x32x16(kf, qf[rb][t], f32x16_t{}) : mfma32x32x16(kf, qf[rb][t], s[rb][mb]);
       }
     }
   };
 
-  // ---- running state of row my_row ----
-  float m_run = -INFINITY;  // reference maximum of raw scores (before scale)
-  float l_run = 0.f;        // this lane's share of the running sum
-  f32x16_t acc[kDBlocks];
+  // ---- running state of the lane's row in each block ----
+  float m_run[RB], l_run[RB];  // reference maximum of raw scores (before scale); this lane's share of the sum
+  f32x16_t acc[RB][kDBlocks];
 #pragma unroll
-  for (int db = 0; db < kDBlocks; ++db)
-    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+      for (int i = 0; i < 16; ++i) acc[rb][db][i] = 0.f;
+  }
 
-  // Softmax of tile j, first half: mask, row max, and a rescale of the state when the reference
-  // maximum moves.  Returns -reference * scale_log2, the exponent shift of this tile.
-  auto softmax_prep = [&](int j, f32x16_t (&s)[2]) -> float {
+  // Softmax of tile j, first half, for row block rb: mask, row max, and a rescale of the state when
+  // the reference maximum moves.  Returns -reference * scale_log2, the exponent shift of this tile.
+  auto softmax_prep = [&](int j, int rb, f32x16_t (&s)[2]) -> float {
     const int k0 = j * kBc;
+    const int rq0 = q0 + 32 * rb;
     // mask: causal keys after the row, and keys past the end of the sequence
-    const bool need_mask = (CAUSAL && (k0 + kBc - 1 > q0)) || (k0 + kBc > a.N);
+    const bool need_mask = (CAUSAL && (k0 + kBc - 1 > rq0)) || (k0 + kBc > a.N);
     if (need_mask) {
-      const int lim = CAUSAL ? min(my_row, a.N - 1) : a.N - 1;
+      const int lim = CAUSAL ? min(rq0 + l32, a.N - 1) : a.N - 1;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -230,22 +301,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
       for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[mb][i]);
     tmax = fmaxf(tmax, swap_halves(tmax, half));
     // move the reference maximum only when some row of the wave outgrew it by the threshold
-    if (__builtin_amdgcn_ballot_w64(tmax > m_run + a.rescale_raw) != 0) {
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_run - m_new) * a.scale_log2);
-      m_run = m_new;
-      l_run *= alpha;
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run[rb] + a.rescale_raw) != 0) {
+      const float m_new = fmaxf(m_run[rb], tmax);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_run[rb] - m_new) * a.scale_log2);
+      m_run[rb] = m_new;
+      l_run[rb] *= alpha;
 #pragma unroll
       for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        for (int i = 0; i < 16; ++i) acc[rb][db][i] *= alpha;
     }
-    return m_run == -INFINITY ? 0.f : -m_run * a.scale_log2;
+    return m_run[rb] == -INFINITY ? 0.f : -m_run[rb] * a.scale_log2;
   };
 
   // Softmax of tile j, second half (no branches, so it can interleave with MFMAs): probabilities
   // relative to the reference, their row sum, and the bf16 B operands of the PV product.
-  auto softmax_exp = [&](const f32x16_t (&s)[2], float neg_ms, u32x4_t (&pf)[4]) {
+  auto softmax_exp = [&](int rb, const f32x16_t (&s)[2], float neg_ms, u32x4_t (&pf)[4]) {
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -260,100 +331,129 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
         pf[2 * mb + sh] = u32x4_t{pack_bf16x2(p[8 * sh + 0], p[8 * sh + 1]), pack_bf16x2(p[8 * sh + 2], p[8 * sh + 3]),
                                   pack_bf16x2(p[8 * sh + 4], p[8 * sh + 5]), pack_bf16x2(p[8 * sh + 6], p[8 * sh + 7])};
     }
-    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    l_run[rb] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
   };
 
-  // O^T += V^T P^T.  PV k-step ks covers keys 16ks..16ks+15 of the tile; logical k = 8*half + jj maps
-  // to key 16ks + 8(jj/4) + 4*half + jj%4.  A operand via two transposed reads.
-  auto pv = [&](const PAA_LDS char* vt, const u32x4_t (&pf)[4]) {
+  // O^T += V^T P^T for every row block.  PV k-step ks covers keys 16ks..16ks+15 of the tile; logical
+  // k = 8*half + jj maps to key 16ks + 8(jj/4) + 4*half + jj%4.  Each A operand (two transposed reads)
+  // feeds RB MFMAs.
+  auto pv = [&](const PAA_LDS char* vt, const u32x4_t (&pf)[RB][4]) {
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const u32x2_t lo = lds_read_tr16((const PAA_LDS uint16_t*)(vt + voff[db][0] + 16 * ks * T::kRowBytes));
         const u32x2_t hi = lds_read_tr16((const PAA_LDS uint16_t*)(vt + voff[db][1] + 16 * ks * T::kRowBytes));
-        acc[db] = mfma32x32x16(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pf[ks], acc[db]);
+        const u32x4_t vf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[rb][db] = mfma32x32x16(vf, pf[rb][ks], acc[rb][db]);
       }
     }
   };
 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  f32x16_t s_cur[2];
-  scores((const PAA_LDS char*)k_st0, s_cur);  // tile 0 is visible to every row
-  __syncthreads();                            // everyone is done with K stage 0 before it is refilled
+  f32x16_t s_cur[RB][2];
+  scores(kst(I0{}), s_cur);  // tile 0 is visible to every row
+  __syncthreads();           // everyone is done with K stage 0 before it is refilled
 
-  // One tile: loads of K_{j+2} and V_{j+1} are issued first; then the scores of tile j+1 (MFMA) are
-  // computed next to the softmax of tile j (VALU), then O += P_j V_j.  ST = j % 2 is a template
-  // constant so every LDS address is a register offset plus an immediate.
+  // Tile j (stage ST = j % STAGES, a template constant, so every LDS address is a register offset
+  // plus an immediate): loads of K_{j+STAGES} and V_{j+STAGES-1} go out first, into the stages that
+  // held K_j and V_{j-1}; then the scores of tile j+1 (MFMA) sit in one branch-free block with the
+  // exponentials of tile j (VALU) and O += P_j V_j.
   auto tile = [&](auto st_tag, int j) {
     constexpr int ST = decltype(st_tag)::value;
-    PAA_LDS char* k_this = ST == 0 ? (PAA_LDS char*)k_st0 : (PAA_LDS char*)k_st1;  // held K_j: free now
-    PAA_LDS char* k_next = ST == 0 ? (PAA_LDS char*)k_st1 : (PAA_LDS char*)k_st0;  // holds K_{j+1}
-    PAA_LDS char* v_this = ST == 0 ? (PAA_LDS char*)v_st0 : (PAA_LDS char*)v_st1;  // holds V_j
-    PAA_LDS char* v_next = ST == 0 ? (PAA_LDS char*)v_st1 : (PAA_LDS char*)v_st0;  // held V_{j-1}: free now
-    if (j + 2 < n_tiles) dma(kh, j + 2, k_this);
-    if (j + 1 < n_tiles) dma(vh, j + 1, v_next);
+    using Next = std::integral_constant<int, ST + 1>;
+    using Prev = std::integral_constant<int, ST + STAGES - 1>;
+    // near the end the loads repeat the last tile (cached, and never read): issuing them every time
+    // keeps the count of loads in flight fixed, so the waits below stay exact
+    dma(kh, min(j + STAGES, n_tiles - 1), kst(st_tag));
+    dma(vh, min(j + STAGES - 1, n_tiles - 1), vst(Prev{}));
     if (j < n_act) {
-      const float neg_ms = softmax_prep(j, s_cur);
-      // one branch-free block: scores of tile j+1 (computed even past the last active tile, where they
-      // are simply dropped), exponentials of tile j, then O += P_j V_j
-      f32x16_t s_nxt[2];
-      scores(k_next, s_nxt);
-      u32x4_t pf[4];
-      softmax_exp(s_cur, neg_ms, pf);
-      pv(v_this, pf);
+      float neg_ms[RB];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) s_cur[mb] = s_nxt[mb];
+      for (int rb = 0; rb < RB; ++rb) neg_ms[rb] = softmax_prep(j, rb, s_cur[rb]);
+      // scores of tile j+1 are computed even past the last active tile, where they are dropped
+      f32x16_t s_nxt[RB][2];
+      scores(kst(Next{}), s_nxt);
+      u32x4_t pf[RB][4];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) softmax_exp(rb, s_cur[rb], neg_ms[rb], pf[rb]);
+      pv(vst(st_tag), pf);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) s_cur[rb][mb] = s_nxt[rb][mb];
     }
-    // the next tiles have landed (own loads, then everyone's) and every wave is done with these stages
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // K_{j+2} and V_{j+1} have landed (own loads, then everyone's) and every wave is done with the
+    // stages the next tile refills
+    wait_vmcnt<C::kInFlightAfter>();
+    tile_barrier();
   };
 
-  for (int j = 0; j < n_tiles; j += 2) {
-    tile(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, j + 1);
-  }
+  for (int j = 0; j < n_tiles; j += STAGES) for_stages<0, STAGES>(tile, j, n_tiles);
+  wait_vmcnt<0>();  // no load may still be writing this workgroup's LDS when it exits
 
   // ---- epilogue: O = acc / l, LSE = scale * m + ln(l) ----
-  const float l_tot = l_run + swap_halves(l_run, half);
-  const float inv_l = 1.f / l_tot;
-  if (my_row < a.N) {
-    uint16_t* orow = a.o + (((size_t)b * a.H + head) * N + my_row) * D;
 #pragma unroll
-    for (int db = 0; db < kDBlocks; ++db) {
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = q0 + 32 * rb + l32;
+    const float l_tot = l_run[rb] + swap_halves(l_run[rb], half);
+    const float inv_l = 1.f / l_tot;
+    if (row < a.N) {
+      uint16_t* orow = a.o + (((size_t)b * a.H + head) * N + row) * D;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d0 = 32 * db + 8 * gq + 4 * half;
-        u32x2_t w = {pack_bf16x2(acc[db][4 * gq + 0] * inv_l, acc[db][4 * gq + 1] * inv_l),
-                     pack_bf16x2(acc[db][4 * gq + 2] * inv_l, acc[db][4 * gq + 3] * inv_l)};
-        *(u32x2_t*)(orow + d0) = w;
+      for (int db = 0; db < kDBlocks; ++db) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d0 = 32 * db + 8 * gq + 4 * half;
+          u32x2_t w = {pack_bf16x2(acc[rb][db][4 * gq + 0] * inv_l, acc[rb][db][4 * gq + 1] * inv_l),
+                       pack_bf16x2(acc[rb][db][4 * gq + 2] * inv_l, acc[rb][db][4 * gq + 3] * inv_l)};
+          *(u32x2_t*)(orow + d0) = w;
+        }
       }
+      if (a.lse != nullptr && half == 0)
+        a.lse[((size_t)b * a.H + head) * N + row] = a.scale * m_run[rb] + __logf(l_tot);
     }
-    if (a.lse != nullptr && half == 0)
-      a.lse[((size_t)b * a.H + head) * N + my_row] = a.scale * m_run + __logf(l_tot);
   }
 }
 
-template <int D, bool CAUSAL, int HPW>
+template <int D, bool CAUSAL, int HPW, int WAVES, int RB, int STAGES>
 hipError_t launch_prefill(const PrefillArgs& base, hipStream_t stream) {
   PrefillArgs a = base;
-  constexpr int kTileRows = (kWaves / HPW) * kRowsPerWave;
+  constexpr int kTileRows = (WAVES / HPW) * 32 * RB;
   a.n_qtiles = (a.N + kTileRows - 1) / kTileRows;
   a.units_per_qt = a.B * a.Hkv * ((a.H / a.Hkv) / HPW);
   const long long units = (long long)a.n_qtiles * a.units_per_qt;
   if (units > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, HPW>), dim3((unsigned)units), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, HPW, WAVES, RB, STAGES>), dim3((unsigned)units),
+                     dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL, int WAVES>
+hipError_t dispatch_group(const PrefillArgs& a, hipStream_t stream) {
+  constexpr int kStages = 2;
+  const int group = a.H / a.Hkv;
+  if constexpr (WAVES % 4 == 0)
+    if (group % 4 == 0) return launch_prefill<D, CAUSAL, 4, WAVES, 1, kStages>(a, stream);
+  if constexpr (WAVES % 2 == 0)
+    if (group % 2 == 0) return launch_prefill<D, CAUSAL, 2, WAVES, 1, kStages>(a, stream);
+  return launch_prefill<D, CAUSAL, 1, WAVES, 1, kStages>(a, stream);
+}
+
+// Workgroup shape.  Eight waves sharing each K/V tile halve the L2 -> LDS traffic per flop against
+// four, and win when the grid still has at least 4 workgroups per CU; for smaller grids (short
+// sequences) the critical path is the heaviest causal query tile, and four-wave workgroups (two per
+// CU) walk it faster.
 template <int D, bool CAUSAL>
 hipError_t dispatch_hpw(const PrefillArgs& a, hipStream_t stream) {
   const int group = a.H / a.Hkv;
-  if (group % 4 == 0) return launch_prefill<D, CAUSAL, 4>(a, stream);
-  if (group % 2 == 0) return launch_prefill<D, CAUSAL, 2>(a, stream);
-  return launch_prefill<D, CAUSAL, 1>(a, stream);
+  const int hpw = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+  const long long rows8 = (8 / hpw) * 32;
+  const long long units8 = (long long)a.B * a.Hkv * (group / hpw) * ((a.N + rows8 - 1) / rows8);
+  if (units8 >= 1024) return dispatch_group<D, CAUSAL, 8>(a, stream);
+  return dispatch_group<D, CAUSAL, 4>(a, stream);
 }
 
 }  // namespace
