@@ -171,38 +171,57 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeAr
   PAA_LDS uint16_t* vl = (PAA_LDS uint16_t*)lds_raw + wave * Lds::kPerWave;
 
   // ---- this workgroup's range of the concatenated page list ----
-  int part_pages = 0;
-  for (int s = threadIdx.x; s < a.S; s += nthreads) part_pages += pages_of(seq_len_clamped(a, s));
-  part_pages = wave_sum(part_pages);
-  if (lane == 0) red[wave] = part_pages;
+  __shared__ int total_sh;
   if (threadIdx.x == 0) found[0] = -1;
-  __syncthreads();
-  long long total = 0;
-  for (int w = 0; w < a.waves; ++w) total += red[w];
-  __syncthreads();
+  long long total;
+  int start, end;
   const int r = blockIdx.x;
-  if (r == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.ws_range[2 * a.S] = (int)total;  // for the reduce
-  const int start = range_begin(r, total, a.parts);
-  const int end = range_begin(r + 1, total, a.parts);
-  if (start >= end) return;  // an empty range (more ranges than pages); uniform across the workgroup
-
-  // the sequence holding global page `start`, and that sequence's first global page
-  int carry = 0;
-  for (int base = 0; base < a.S; base += nthreads) {
-    const int s = base + threadIdx.x;
+  if (a.S <= nthreads) {
+    // one scan gives both the total and the sequence holding the range's first page
+    const int s = threadIdx.x;
     const int v = s < a.S ? pages_of(seq_len_clamped(a, s)) : 0;
     const int incl = block_inclusive_scan(v, red);
-    if (v > 0 && carry + incl - v <= start && start < carry + incl) {
+    if (threadIdx.x == nthreads - 1) total_sh = incl;
+    __syncthreads();
+    total = total_sh;
+    start = range_begin(r, total, a.parts);
+    end = range_begin(r + 1, total, a.parts);
+    if (v > 0 && incl - v <= start && start < incl) {
       found[0] = s;
-      found[1] = carry + incl - v;
+      found[1] = incl - v;
     }
-    if (threadIdx.x == nthreads - 1) red[0] = incl;
     __syncthreads();
-    carry += red[0];
-    const bool done = found[0] >= 0;
+  } else {
+    int part_pages = 0;
+    for (int s = threadIdx.x; s < a.S; s += nthreads) part_pages += pages_of(seq_len_clamped(a, s));
+    part_pages = wave_sum(part_pages);
+    if (lane == 0) red[wave] = part_pages;
     __syncthreads();
-    if (done) break;
+    total = 0;
+    for (int w = 0; w < a.waves; ++w) total += red[w];
+    __syncthreads();
+    start = range_begin(r, total, a.parts);
+    end = range_begin(r + 1, total, a.parts);
+    // the sequence holding global page `start`, and that sequence's first global page
+    int carry = 0;
+    for (int base = 0; base < a.S && start < end; base += nthreads) {
+      const int s = base + threadIdx.x;
+      const int v = s < a.S ? pages_of(seq_len_clamped(a, s)) : 0;
+      const int incl = block_inclusive_scan(v, red);
+      if (v > 0 && carry + incl - v <= start && start < carry + incl) {
+        found[0] = s;
+        found[1] = carry + incl - v;
+      }
+      if (threadIdx.x == nthreads - 1) red[0] = incl;
+      __syncthreads();
+      carry += red[0];
+      const bool done = found[0] >= 0;
+      __syncthreads();
+      if (done) break;
+    }
   }
+  if (r == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.ws_range[2 * a.S] = (int)total;  // for the reduce
+  if (start >= end) return;  // an empty range (more ranges than pages); uniform across the workgroup
   const int s0 = found[0];
   const int c0 = found[1];
 
@@ -423,21 +442,43 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
         return -INFINITY;
       return a.ws_lse[(size_t)(first + j) * a.H + h];
     };
-    // max over the partials' LSE, 64 at a time
-    for (int c0 = 0; c0 < n; c0 += 64) mx = fmaxf(mx, c0 + lane < n ? lse_of(c0 + lane) : -INFINITY);
+    // max over the partials' LSE, 64 at a time (the first 64 are kept)
+    const float lse0 = lane < n ? lse_of(lane) : -INFINITY;
+    mx = lse0;
+    for (int c0 = 64; c0 < n; c0 += 64) mx = fmaxf(mx, c0 + lane < n ? lse_of(c0 + lane) : -INFINITY);
+    // the first kEarly partial rows are loaded in the same round trip as the LSEs above
+    constexpr int kEarly = 8;
+    float ov[kEarly][kPerLane];
+#pragma unroll
+    for (int u = 0; u < kEarly; ++u) {
+      const float* src = a.ws_o + ((size_t)(first + min(u, n - 1)) * a.H + h) * D;
+#pragma unroll
+      for (int i = 0; i < kPerLane; ++i) ov[u][i] = src[lane + 64 * i];
+    }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
     for (int c0 = 0; c0 < n && mx != -INFINITY; c0 += 64) {
       const int cnt = min(64, n - c0);
-      const float lc = lane < cnt ? lse_of(c0 + lane) : -INFINITY;
+      const float lc = c0 == 0 ? lse0 : (lane < cnt ? lse_of(c0 + lane) : -INFINITY);
       const float w = lc == -INFINITY ? 0.f : __expf(lc - mx);  // a partial without a visible key weighs 0
       float ws = w;
 #pragma unroll
       for (int m = 1; m < 64; m <<= 1) ws += __shfl_xor(ws, m);
       wsum += ws;
-      // four partials per round, loads issued together; a slot whose weight is 0 (empty range, or no
-      // visible key) may hold anything, so its values are replaced by 0 rather than multiplied by 0
-      for (int j0 = 0; j0 < cnt; j0 += 4) {
+      // a slot whose weight is 0 (empty range, or no visible key) may hold anything, so its values
+      // are replaced by 0 rather than multiplied by 0
+      int j0 = 0;
+      if (c0 == 0) {
+#pragma unroll
+        for (int u = 0; u < kEarly; ++u) {
+          const float wj = u < cnt ? __shfl(w, u) : 0.f;
+#pragma unroll
+          for (int i = 0; i < kPerLane; ++i) out[i] = fmaf(wj, wj == 0.f ? 0.f : ov[u][i], out[i]);
+        }
+        j0 = kEarly;
+      }
+      // the rest four at a time, loads issued together
+      for (; j0 < cnt; j0 += 4) {
         float v[4][kPerLane], wj[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
