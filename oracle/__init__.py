@@ -22,6 +22,7 @@ here is "parity unpinned".
 from .exact import (  # noqa: F401
     attention,
     attention_rows,
+    attention_window,
     paged_decode,
     paged_gather,
     softmax_probs,

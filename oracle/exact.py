@@ -29,8 +29,14 @@ Readings taken where the pages are silent (each repeated in the design doc):
   at page ``block_table[s, t // page_size]``, slot ``t % page_size``; slots at
   t >= L are never read.
 * An empty key set (L = 0) gives O = 0 and LSE = -inf (the empty sum).
+* Sliding window with global tokens ("Kernel Fusion and Custom Kernels",
+  section "4. FlashInfer", block-sparse masks: the Longformer pattern of a
+  sliding window plus global tokens), read under the causal mask: key j is
+  visible to query i iff j <= i and (i - j < window or j < n_global).  A
+  global token's own row is causal anyway, so "global tokens see everything"
+  adds nothing once the causal mask applies.
 
-The helpers ``_kv_head``, ``_scores``, ``_apply_causal``, ``_softmax`` and
+The helpers ``_kv_head``, ``_scores``, ``_apply_causal``, ``_window_mask``, ``_softmax`` and
 ``_page_slot`` are looked up at call time, so tests can plant a mistake in
 one of them (on the CPU) and check that a pin catches it.
 """
@@ -67,6 +73,14 @@ def _kv_head(h: int, H: int, Hkv: int) -> int:
 def _scores(q_rows: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
     """S = scale * Q K^T for a block of query rows [r, d] against keys [n, d]."""
     return scale * (q_rows @ k.T)
+
+
+def _window_mask(row_pos: np.ndarray, n_keys: int, window: int, n_global: int) -> np.ndarray:
+    """True where key j is hidden from query row_pos[r]: causal, then outside the window unless global."""
+    j = np.arange(n_keys)[None, :]
+    i = row_pos[:, None]
+    visible = (j <= i) & ((i - j < window) | (j < n_global))
+    return ~visible
 
 
 def _apply_causal(s: np.ndarray, row_pos: np.ndarray) -> None:
@@ -134,6 +148,33 @@ def attention(q, k, v, causal: bool, scale: float):
                 pos = np.arange(r0, r1) if causal else None
                 o[b, h, r0:r1], lse[b, h, r0:r1] = _attend(
                     q64[b, h, r0:r1], k64[b, g, :n_keys], v64[b, g, :n_keys], scale, pos)
+    return o, lse
+
+
+def attention_window(q, k, v, window: int, n_global: int, scale: float):
+    """Causal attention with a sliding window and global tokens; (O, LSE) in float64.
+
+    Key j is visible to query i iff j <= i and (i - j < window or j < n_global).
+    Every row sees at least its own key (window >= 1).
+    """
+    if window < 1 or n_global < 0:
+        raise ValueError("window must be >= 1 and n_global >= 0")
+    q64, k64, v64 = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, N, d = q64.shape
+    Hkv = k64.shape[1]
+    _check_heads(H, Hkv)
+    o = np.zeros((B, H, N, v64.shape[3]))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            g = _kv_head(h, H, Hkv)
+            for r0 in range(0, N, ROW_BLOCK):
+                r1 = min(N, r0 + ROW_BLOCK)
+                pos = np.arange(r0, r1)
+                s = _scores(q64[b, h, r0:r1], k64[b, g, :r1], scale)
+                s[_window_mask(pos, r1, window, n_global)] = -np.inf
+                p, m, l = _softmax(s)
+                o[b, h, r0:r1], lse[b, h, r0:r1] = p @ v64[b, g, :r1], m + np.log(l)
     return o, lse
 
 

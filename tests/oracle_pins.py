@@ -177,6 +177,83 @@ def pin_rows_equal_full():
             assert abs(rl[n] - lse[b, h, i]) < 1e-14
 
 
+# ----------------------------------------------------------------- sliding window + global tokens
+
+def _brute_window(q, k, v, window, n_global, scale):
+    """Windowed causal attention straight from the rule, with pure-Python loops and math.fsum."""
+    B, H, N, d = q.shape
+    o = np.zeros((B, H, N, d))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                keys = []
+                for j in range(N):
+                    if j > i:
+                        continue
+                    if i - j < window or j < n_global:
+                        keys.append(j)
+                s = [scale * math.fsum(float(q[b, h, i, c]) * float(k[b, h, j, c]) for c in range(d))
+                     for j in keys]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                tot = math.fsum(w)
+                for c in range(d):
+                    o[b, h, i, c] = math.fsum(w[n] * float(v[b, h, j, c]) for n, j in enumerate(keys)) / tot
+                lse[b, h, i] = mx + math.log(tot)
+    return o, lse
+
+
+def pin_window_brute_force_tiny():
+    """Sliding window + global tokens against the brute-force rule on tiny shapes (to 1e-12)."""
+    for N, d, window, n_global, seed in [(9, 3, 2, 0, 40), (9, 3, 3, 2, 41), (12, 4, 4, 1, 42), (6, 2, 1, 0, 43),
+                                         (10, 2, 20, 0, 44), (11, 3, 5, 11, 45)]:
+        q, k, v = _rand((1, 2, N, d), seed), _rand((1, 2, N, d), seed + 10), _rand((1, 2, N, d), seed + 20)
+        o, lse = oracle.attention_window(q, k, v, window, n_global, 0.7)
+        ob, lb = _brute_window(q, k, v, window, n_global, 0.7)
+        assert np.allclose(o, ob, rtol=0, atol=1e-12)
+        assert np.allclose(lse, lb, rtol=0, atol=1e-12)
+
+
+def pin_window_torch_sdpa_boolean_mask():
+    """Agreement with torch's CPU float64 SDPA given the window mask as a boolean matrix built by loops."""
+    import torch
+    import torch.nn.functional as F
+    for (N, d, window, n_global) in [(40, 8, 7, 3), (33, 16, 1, 0), (50, 8, 64, 0), (37, 4, 5, 37)]:
+        q, k, v = _rand((1, 2, N, d), N), _rand((1, 2, N, d), N + 1), _rand((1, 2, N, d), N + 2)
+        allowed = torch.zeros((N, N), dtype=torch.bool)
+        for i in range(N):
+            for j in range(i + 1):
+                allowed[i, j] = (i - j < window) or (j < n_global)
+        o, _ = oracle.attention_window(q, k, v, window, n_global, 0.3)
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                                             attn_mask=allowed, scale=0.3).numpy()
+        assert np.allclose(o, ref, rtol=0, atol=1e-10)
+
+
+def pin_window_one_is_identity():
+    """window = 1 with no global token: each query sees only its own key, O_i = V_i, LSE_i = scale q_i.k_i."""
+    q, k, v = _rand((1, 1, 13, 5), 46), _rand((1, 1, 13, 5), 47), _rand((1, 1, 13, 5), 48)
+    o, lse = oracle.attention_window(q, k, v, 1, 0, 0.45)
+    assert np.array_equal(o, v)
+    for i in range(13):
+        assert abs(lse[0, 0, i] - 0.45 * math.fsum(q[0, 0, i] * k[0, 0, i])) < 1e-13
+
+
+def pin_window_one_with_one_global_token():
+    """window = 1, one global token: query i >= 1 sees keys {0, i}, a two-term softmax in closed form."""
+    q, k, v = _rand((1, 1, 10, 4), 49), _rand((1, 1, 10, 4), 50), _rand((1, 1, 10, 4), 51)
+    o, lse = oracle.attention_window(q, k, v, 1, 1, 0.6)
+    for i in range(1, 10):
+        s0 = 0.6 * math.fsum(q[0, 0, i] * k[0, 0, 0])
+        si = 0.6 * math.fsum(q[0, 0, i] * k[0, 0, i])
+        mx = max(s0, si)
+        w0, wi = math.exp(s0 - mx), math.exp(si - mx)
+        assert np.allclose(o[0, 0, i], (w0 * v[0, 0, 0] + wi * v[0, 0, i]) / (w0 + wi), rtol=0, atol=1e-13)
+        assert abs(lse[0, 0, i] - (mx + math.log(w0 + wi))) < 1e-13
+    assert np.array_equal(o[0, 0, 0], v[0, 0, 0])
+
+
 # ----------------------------------------------------------------- decode pins
 
 def _golden_example():

@@ -42,6 +42,24 @@ def _mut_causal_flipped(s, row_pos):
     s[cols[None, :] < row_pos[:, None]] = -np.inf
 
 
+def _mut_window_inclusive(row_pos, n_keys, window, n_global):
+    j = np.arange(n_keys)[None, :]
+    i = row_pos[:, None]
+    return ~((j <= i) & ((i - j <= window) | (j < n_global)))
+
+
+def _mut_window_global_inclusive(row_pos, n_keys, window, n_global):
+    j = np.arange(n_keys)[None, :]
+    i = row_pos[:, None]
+    return ~((j <= i) & ((i - j < window) | (j <= n_global)))
+
+
+def _mut_window_not_causal(row_pos, n_keys, window, n_global):
+    j = np.arange(n_keys)[None, :]
+    i = row_pos[:, None]
+    return ~((np.abs(i - j) < window) | (j < n_global))
+
+
 # Each entry: (helper name in oracle.exact, planted replacement)
 MUTANTS = {
     "gqa_modulo_mapping": ("_kv_head", lambda h, H, Hkv: h % Hkv),
@@ -57,6 +75,9 @@ MUTANTS = {
     "lse_without_max": ("_softmax", _mut_softmax_lse_without_max),
     "page_block_slot_swapped": ("_page_slot", lambda t, ps: (t % ps, t // ps)),
     "page_off_by_one_token": ("_page_slot", lambda t, ps: ((t + 1) // ps, (t + 1) % ps)),
+    "window_off_by_one": ("_window_mask", _mut_window_inclusive),
+    "window_global_off_by_one": ("_window_mask", _mut_window_global_inclusive),
+    "window_not_causal": ("_window_mask", _mut_window_not_causal),
 }
 
 
