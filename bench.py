@@ -52,7 +52,8 @@ PMC_CALLS = 3              # calls of each workload in a counter pass
 
 PREFILL_DEFAULT = "causal_b4h16n1024d64"
 DECODE_DEFAULT = "paged_decode_s64h32kv8d128"
-PREFILL_MORE = ("causal_gqa_b2h32kv8n4096d128", "causal_gqa_long_b1h32kv8n16384d128")
+PREFILL_MORE = ("causal_gqa_b2h32kv8n4096d128", "causal_gqa_long_b1h32kv8n16384d128",
+                "window_gqa_b1h32kv8n16384d128_w4096_g64")
 
 
 # ----------------------------------------------------------------- algorithmic counts
@@ -162,7 +163,11 @@ class PrefillCase:
         self.paa = paa
 
     def __call__(self):
-        self.paa.attn_fwd(self.q, self.k, self.v, self.w.causal, self.a["scale"], out=self.o, lse=self.lse)
+        if self.w.window:
+            self.paa.attn_fwd_window(self.q, self.k, self.v, self.w.window, self.w.n_global, self.a["scale"],
+                                     out=self.o, lse=self.lse)
+        else:
+            self.paa.attn_fwd(self.q, self.k, self.v, self.w.causal, self.a["scale"], out=self.o, lse=self.lse)
 
 
 class DecodeCase:

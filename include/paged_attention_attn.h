@@ -67,6 +67,20 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              int causal, float scale, hipStream_t stream);
 
 /*
+ * attn_fwd_window — causal attention with a sliding window and global tokens,
+ * bf16 in/out: the block-sparse pattern of "Kernel Fusion and Custom
+ * Kernels", section "4. FlashInfer" (a Longformer-style sliding window plus
+ * global tokens), under the causal mask.  Key j is visible to query i iff
+ * j <= i and (i - j < window or j < n_global).  Key tiles that hold no visible
+ * key (between the global tokens and the left edge of a query tile's window)
+ * are never read.  Shapes, layouts, scale rules, GQA mapping, LSE and the
+ * arithmetic are those of attn_fwd; window must be >= 1 and n_global >= 0
+ * (ATTN_ERR_INVALID_SHAPE otherwise).  window >= N is the plain causal mask.
+ */
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+                    int d, int window, int n_global, float scale, hipStream_t stream);
+
+/*
  * attn_fwd_f32 — the same operation with fp32 inputs, outputs and arithmetic
  * throughout (no reduced-precision matrix instructions).  Shapes, masking,
  * head grouping and LSE as for attn_fwd; d must be 64 or 128.

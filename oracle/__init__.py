@@ -23,6 +23,7 @@ from .exact import (  # noqa: F401
     attention,
     attention_rows,
     attention_window,
+    attention_window_rows,
     paged_decode,
     paged_gather,
     softmax_probs,

@@ -178,6 +178,25 @@ def attention_window(q, k, v, window: int, n_global: int, scale: float):
     return o, lse
 
 
+def attention_window_rows(q, k, v, window: int, n_global: int, scale: float, rows):
+    """O and LSE of selected query rows ``(b, h, i)`` of :func:`attention_window`, one row at a time."""
+    if window < 1 or n_global < 0:
+        raise ValueError("window must be >= 1 and n_global >= 0")
+    q_, k_, v_ = np.asarray(q), np.asarray(k), np.asarray(v)
+    H, Hkv = q_.shape[1], k_.shape[1]
+    _check_heads(H, Hkv)
+    out_o, out_l = [], []
+    for b, h, i in rows:
+        g = _kv_head(int(h), H, Hkv)
+        i = int(i)
+        s = _scores(_as_f64(q_[b, h, i])[None, :], _as_f64(k_[b, g, :i + 1]), scale)
+        s[_window_mask(np.array([i]), i + 1, window, n_global)] = -np.inf
+        p, m, l = _softmax(s)
+        out_o.append((p @ _as_f64(v_[b, g, :i + 1]))[0])
+        out_l.append((m + np.log(l))[0])
+    return np.array(out_o), np.array(out_l)
+
+
 def attention_rows(q, k, v, causal: bool, scale: float, rows):
     """O and LSE of selected query rows only; ``rows`` is a sequence of (b, h, i).
 

@@ -9,6 +9,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     attn_fwd,
     attn_fwd_f32,
+    attn_fwd_window,
     attn_status_string,
     declared_functions,
     lib,

@@ -36,6 +36,8 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd.restype = i
         L.attn_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
         L.attn_fwd_f32.restype = i
+        L.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+        L.attn_fwd_window.restype = i
         L.paged_attn_decode_workspace_size.argtypes = [i, i, i, i, i]
         L.paged_attn_decode_workspace_size.restype = sz
         L.paged_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
@@ -86,7 +88,7 @@ def _require(t, name, dtype, ndim, device=None):
         raise ValueError(f"{name} must be contiguous (no implicit copies)")
 
 
-def _prefill(entry, dtype, q, k, v, causal, scale, out, lse):
+def _prefill(entry, dtype, q, k, v, causal, scale, out, lse, mask_args=None):
     _require(q, "q", dtype, 4)
     _require(k, "k", dtype, 4, q.device)
     _require(v, "v", dtype, 4, q.device)
@@ -106,14 +108,21 @@ def _prefill(entry, dtype, q, k, v, causal, scale, out, lse):
             raise ValueError("lse must be [B, H, N]")
     if scale is None:
         scale = d ** -0.5
-    _check(entry(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, N, d, int(bool(causal)),
-                 float(scale), _stream(q.device)))
+    mask = [int(bool(causal))] if mask_args is None else [int(x) for x in mask_args]
+    _check(entry(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, N, d, *mask, float(scale),
+                 _stream(q.device)))
     return out, lse
 
 
 def attn_fwd(q, k, v, causal: bool, scale: float | None = None, out=None, lse=None):
     """bf16 attention forward: q [B,H,N,d], k/v [B,Hkv,N,d] -> (out [B,H,N,d] bf16, lse [B,H,N] fp32 or None)."""
     return _prefill(lib().attn_fwd, torch.bfloat16, q, k, v, causal, scale, out, lse)
+
+
+def attn_fwd_window(q, k, v, window: int, n_global: int = 0, scale: float | None = None, out=None, lse=None):
+    """bf16 causal attention where key j is visible to query i iff j <= i and (i - j < window or j < n_global)."""
+    return _prefill(lib().attn_fwd_window, torch.bfloat16, q, k, v, True, scale, out, lse,
+                    mask_args=(window, n_global))
 
 
 def attn_fwd_f32(q, k, v, causal: bool, scale: float | None = None, out=None, lse=None):

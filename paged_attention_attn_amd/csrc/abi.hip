@@ -62,7 +62,16 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   const int rc = check_prefill(q, k, v, o, lse, B, H, Hkv, N, d, scale);
   if (rc != ATTN_OK) return rc;
   if (B == 0 || N == 0) return ATTN_OK;
-  return launch_status(paa::prefill_bf16(q, k, v, o, lse, B, H, Hkv, N, d, causal != 0, scale, stream));
+  return launch_status(paa::prefill_bf16(q, k, v, o, lse, B, H, Hkv, N, d, causal != 0, 0, 0, scale, stream));
+}
+
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+                    int d, int window, int n_global, float scale, hipStream_t stream) {
+  const int rc = check_prefill(q, k, v, o, lse, B, H, Hkv, N, d, scale);
+  if (rc != ATTN_OK) return rc;
+  if (window < 1 || n_global < 0) return ATTN_ERR_INVALID_SHAPE;
+  if (B == 0 || N == 0) return ATTN_OK;
+  return launch_status(paa::prefill_bf16(q, k, v, o, lse, B, H, Hkv, N, d, true, window, n_global, scale, stream));
 }
 
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Hkv, int N,

@@ -7,8 +7,9 @@
 
 namespace paa {
 
+// window <= 0 (or >= N) means the plain causal mask when causal is set
 hipError_t prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
-                        int N, int d, bool causal, float scale, hipStream_t stream);
+                        int N, int d, bool causal, int window, int n_global, float scale, hipStream_t stream);
 
 hipError_t prefill_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Hkv,
                        int N, int d, bool causal, float scale, hipStream_t stream);

@@ -115,6 +115,8 @@ struct PrefillArgs {
   float scale;       // softmax scale applied to Q.K
   float scale_log2;  // scale * log2(e)
   float rescale_raw; // kRescaleLog2 / scale_log2: the lazy rescale threshold in raw score units
+  int window;        // sliding window width (kMaskWindow only)
+  int n_global;      // leading keys visible to every later query (kMaskWindow only)
 };
 
 // WAVES waves per workgroup, RB blocks of 32 query rows per wave, STAGES-deep K and V rings in LDS.
@@ -129,11 +131,17 @@ struct PrefillCfg {
   static constexpr int kInFlightAfter = (STAGES - 2) * 2 * kBlocksPerWave;
 };
 
-template <int D, bool CAUSAL, int HPW, int WAVES, int RB, int STAGES>
+// Masks: none, causal (key j visible to query i iff j <= i), or causal with a sliding window and
+// global tokens (additionally i - j < window or j < n_global).
+enum : int { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2 };
+
+template <int D, int MASK, int HPW, int WAVES, int RB, int STAGES>
 __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_kernel(
     PrefillArgs a) {
   using T = TileLayout<D>;
   using C = PrefillCfg<D, WAVES, RB, STAGES>;
+  constexpr bool CAUSAL = MASK != kMaskNone;
+  constexpr bool WINDOW = MASK == kMaskWindow;
   constexpr int kWaveRows = C::kRowsPerWave;
   constexpr int kRowBlocks = WAVES / HPW;              // waves per head in a workgroup
   constexpr int kTileRows = kRowBlocks * kWaveRows;    // query rows per head in a workgroup
@@ -150,14 +158,14 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   __shared__ __attribute__((aligned(1024))) char v_st1[T::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char v_st2[T::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char v_st3[T::kTileBytes];
-  auto kst = [&](auto i_tag) -> PAA_LDS char* {
+  auto kst = [&](auto i_tag) __attribute__((always_inline)) -> PAA_LDS char* {
     constexpr int i = decltype(i_tag)::value % STAGES;
     if constexpr (i == 0) return (PAA_LDS char*)k_st0;
     else if constexpr (i == 1) return (PAA_LDS char*)k_st1;
     else if constexpr (i == 2) return (PAA_LDS char*)k_st2;
     else return (PAA_LDS char*)k_st3;
   };
-  auto vst = [&](auto i_tag) -> PAA_LDS char* {
+  auto vst = [&](auto i_tag) __attribute__((always_inline)) -> PAA_LDS char* {
     constexpr int i = decltype(i_tag)::value % STAGES;
     if constexpr (i == 0) return (PAA_LDS char*)v_st0;
     else if constexpr (i == 1) return (PAA_LDS char*)v_st1;
@@ -194,13 +202,25 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   const uint16_t* kh = a.k + ((size_t)b * a.Hkv + g) * N * D;
   const uint16_t* vh = a.v + ((size_t)b * a.Hkv + g) * N * D;
 
-  // ---- key tiles: the workgroup loads [0, n_tiles); this wave computes [0, n_act) ----
+  // ---- key tiles ----
+  // The workgroup visits key tiles [0, n_glob) and then [j_win, n_tiles) in order; iteration t
+  // is tile tile_of(t).  Without a window every tile up to the causal limit is visited.  With one,
+  // the tiles between the global tokens and the left edge of the workgroup's lowest row's window
+  // hold no visible key and are never loaded.  This wave computes iterations [0, n_act).
   const int kv_end = CAUSAL ? min(a.N, q0_tile + kTileRows) : a.N;
   const int n_tiles = (kv_end + kBc - 1) / kBc;
-  const int n_act = CAUSAL ? min(n_tiles, (q0 + kWaveRows - 1) / kBc + 1) : n_tiles;
+  int n_glob = 0, j_win = 0;
+  if constexpr (WINDOW) {
+    n_glob = min(n_tiles, (a.n_global + kBc - 1) / kBc);
+    j_win = max(n_glob, max(0, q0_tile - a.window + 1) / kBc);
+  }
+  const int n_iter = n_glob + (n_tiles - j_win);
+  auto tile_of = [&](int t) __attribute__((always_inline)) { return t < n_glob ? t : j_win + (t - n_glob); };
+  const int last_tile = CAUSAL ? min(n_tiles - 1, (q0 + kWaveRows - 1) / kBc) : n_tiles - 1;
+  const int n_act = last_tile < n_glob ? last_tile + 1 : n_glob + max(0, last_tile - j_win + 1);
 
   // ---- direct global -> LDS load of one tile of K or V; this wave fetches kBlocksPerWave 1 KB blocks ----
-  auto dma = [&](const uint16_t* src, int j, PAA_LDS char* dst) {
+  auto dma = [&](const uint16_t* src, int j, PAA_LDS char* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::kBlocksPerWave; ++i) {
       const int blk = wave * C::kBlocksPerWave + i;
@@ -213,11 +233,12 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   };
 
   // prologue loads: K_0 .. K_{STAGES-1} and V_0 .. V_{STAGES-2}
-  auto prologue = [&](auto i_tag, int j) {
+  auto prologue = [&](auto i_tag, int j) __attribute__((always_inline)) {
     dma(kh, j, kst(i_tag));
     if (decltype(i_tag)::value + 1 < STAGES) dma(vh, j, vst(i_tag));
   };
-  for_stages<0, STAGES>(prologue, 0, n_tiles);
+  auto prologue_t = [&](auto i_tag, int t) __attribute__((always_inline)) { prologue(i_tag, tile_of(t)); };
+  for_stages<0, STAGES>(prologue_t, 0, n_iter);
 
   // ---- Q fragments (B operand of S^T = K Q^T): row q0 + 32rb + l32, d = 16t + 8*half + 0..7 ----
   u32x4_t qf[RB][kKSteps];
@@ -252,7 +273,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
 
   // S^T of one tile for every row block: block (rb, mb) holds keys k0 + 32mb + 8(i/4) + 4*half + i%4
   // of query row q0 + 32rb + l32.  Each K fragment read from LDS feeds RB MFMAs.
-  auto scores = [&](const PAA_LDS char* kt, f32x16_t (&s)[RB][2]) {
+  auto scores = [&](const PAA_LDS char* kt, f32x16_t (&s)[RB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
@@ -279,19 +300,23 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
 
   // Softmax of tile j, first half, for row block rb: mask, row max, and a rescale of the state when
   // the reference maximum moves.  Returns -reference * scale_log2, the exponent shift of this tile.
-  auto softmax_prep = [&](int j, int rb, f32x16_t (&s)[2]) -> float {
+  auto softmax_prep = [&](int j, int rb, f32x16_t (&s)[2]) __attribute__((always_inline)) -> float {
     const int k0 = j * kBc;
     const int rq0 = q0 + 32 * rb;
-    // mask: causal keys after the row, and keys past the end of the sequence
-    const bool need_mask = (CAUSAL && (k0 + kBc - 1 > rq0)) || (k0 + kBc > a.N);
+    // mask: causal keys after the row, keys past the end of the sequence and, with a window, keys
+    // left of the row's window that are not global tokens
+    const bool need_window = WINDOW && (k0 <= rq0 + 31 - a.window) && (k0 + kBc - 1 >= a.n_global);
+    const bool need_mask = (CAUSAL && (k0 + kBc - 1 > rq0)) || (k0 + kBc > a.N) || need_window;
     if (need_mask) {
-      const int lim = CAUSAL ? min(rq0 + l32, a.N - 1) : a.N - 1;
+      const int row = rq0 + l32;
+      const int lim = CAUSAL ? min(row, a.N - 1) : a.N - 1;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + 32 * mb + 8 * (i / 4) + 4 * half + (i % 4);
-          if (key > lim) s[mb][i] = -INFINITY;
+          const bool out_of_window = WINDOW && row - key >= a.window && key >= a.n_global;
+          if (key > lim || out_of_window) s[mb][i] = -INFINITY;
         }
     }
     float tmax = -INFINITY;
@@ -316,7 +341,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
 
   // Softmax of tile j, second half (no branches, so it can interleave with MFMAs): probabilities
   // relative to the reference, their row sum, and the bf16 B operands of the PV product.
-  auto softmax_exp = [&](int rb, const f32x16_t (&s)[2], float neg_ms, u32x4_t (&pf)[4]) {
+  auto softmax_exp = [&](int rb, const f32x16_t (&s)[2], float neg_ms, u32x4_t (&pf)[4]) __attribute__((always_inline)) {
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -337,7 +362,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   // O^T += V^T P^T for every row block.  PV k-step ks covers keys 16ks..16ks+15 of the tile; logical
   // k = 8*half + jj maps to key 16ks + 8(jj/4) + 4*half + jj%4.  Each A operand (two transposed reads)
   // feeds RB MFMAs.
-  auto pv = [&](const PAA_LDS char* vt, const u32x4_t (&pf)[RB][4]) {
+  auto pv = [&](const PAA_LDS char* vt, const u32x4_t (&pf)[RB][4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db) {
 #pragma unroll
@@ -361,18 +386,18 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   // plus an immediate): loads of K_{j+STAGES} and V_{j+STAGES-1} go out first, into the stages that
   // held K_j and V_{j-1}; then the scores of tile j+1 (MFMA) sit in one branch-free block with the
   // exponentials of tile j (VALU) and O += P_j V_j.
-  auto tile = [&](auto st_tag, int j) {
+  auto tile = [&](auto st_tag, int j) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_tag)::value;
     using Next = std::integral_constant<int, ST + 1>;
     using Prev = std::integral_constant<int, ST + STAGES - 1>;
     // near the end the loads repeat the last tile (cached, and never read): issuing them every time
     // keeps the count of loads in flight fixed, so the waits below stay exact
-    dma(kh, min(j + STAGES, n_tiles - 1), kst(st_tag));
-    dma(vh, min(j + STAGES - 1, n_tiles - 1), vst(Prev{}));
+    dma(kh, tile_of(min(j + STAGES, n_iter - 1)), kst(st_tag));
+    dma(vh, tile_of(min(j + STAGES - 1, n_iter - 1)), vst(Prev{}));
     if (j < n_act) {
       float neg_ms[RB];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) neg_ms[rb] = softmax_prep(j, rb, s_cur[rb]);
+      for (int rb = 0; rb < RB; ++rb) neg_ms[rb] = softmax_prep(tile_of(j), rb, s_cur[rb]);
       // scores of tile j+1 are computed even past the last active tile, where they are dropped
       f32x16_t s_nxt[RB][2];
       scores(kst(Next{}), s_nxt);
@@ -391,7 +416,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
     tile_barrier();
   };
 
-  for (int j = 0; j < n_tiles; j += STAGES) for_stages<0, STAGES>(tile, j, n_tiles);
+  for (int j = 0; j < n_iter; j += STAGES) for_stages<0, STAGES>(tile, j, n_iter);
   wait_vmcnt<0>();  // no load may still be writing this workgroup's LDS when it exits
 
   // ---- epilogue: O = acc / l, LSE = scale * m + ln(l) ----
@@ -418,7 +443,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   }
 }
 
-template <int D, bool CAUSAL, int HPW, int WAVES, int RB, int STAGES>
+template <int D, int MASK, int HPW, int WAVES, int RB, int STAGES>
 hipError_t launch_prefill(const PrefillArgs& base, hipStream_t stream) {
   PrefillArgs a = base;
   constexpr int kTileRows = (WAVES / HPW) * 32 * RB;
@@ -426,40 +451,40 @@ hipError_t launch_prefill(const PrefillArgs& base, hipStream_t stream) {
   a.units_per_qt = a.B * a.Hkv * ((a.H / a.Hkv) / HPW);
   const long long units = (long long)a.n_qtiles * a.units_per_qt;
   if (units > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, HPW, WAVES, RB, STAGES>), dim3((unsigned)units),
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, MASK, HPW, WAVES, RB, STAGES>), dim3((unsigned)units),
                      dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, int WAVES>
+template <int D, int MASK, int WAVES>
 hipError_t dispatch_group(const PrefillArgs& a, hipStream_t stream) {
   constexpr int kStages = 2;
   const int group = a.H / a.Hkv;
   if constexpr (WAVES % 4 == 0)
-    if (group % 4 == 0) return launch_prefill<D, CAUSAL, 4, WAVES, 1, kStages>(a, stream);
+    if (group % 4 == 0) return launch_prefill<D, MASK, 4, WAVES, 1, kStages>(a, stream);
   if constexpr (WAVES % 2 == 0)
-    if (group % 2 == 0) return launch_prefill<D, CAUSAL, 2, WAVES, 1, kStages>(a, stream);
-  return launch_prefill<D, CAUSAL, 1, WAVES, 1, kStages>(a, stream);
+    if (group % 2 == 0) return launch_prefill<D, MASK, 2, WAVES, 1, kStages>(a, stream);
+  return launch_prefill<D, MASK, 1, WAVES, 1, kStages>(a, stream);
 }
 
 // Workgroup shape.  Eight waves sharing each K/V tile halve the L2 -> LDS traffic per flop against
 // four, and win when the grid still has at least 4 workgroups per CU; for smaller grids (short
 // sequences) the critical path is the heaviest causal query tile, and four-wave workgroups (two per
 // CU) walk it faster.
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 hipError_t dispatch_hpw(const PrefillArgs& a, hipStream_t stream) {
   const int group = a.H / a.Hkv;
   const int hpw = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
   const long long rows8 = (8 / hpw) * 32;
   const long long units8 = (long long)a.B * a.Hkv * (group / hpw) * ((a.N + rows8 - 1) / rows8);
-  if (units8 >= 1024) return dispatch_group<D, CAUSAL, 8>(a, stream);
-  return dispatch_group<D, CAUSAL, 4>(a, stream);
+  if (units8 >= 1024) return dispatch_group<D, MASK, 8>(a, stream);
+  return dispatch_group<D, MASK, 4>(a, stream);
 }
 
 }  // namespace
 
 hipError_t prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
-                        int N, int d, bool causal, float scale, hipStream_t stream) {
+                        int N, int d, bool causal, int window, int n_global, float scale, hipStream_t stream) {
   PrefillArgs a{};
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
@@ -473,8 +498,18 @@ hipError_t prefill_bf16(const void* q, const void* k, const void* v, void* o, fl
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
   a.rescale_raw = kRescaleLog2 / a.scale_log2;
-  if (d == 64) return causal ? dispatch_hpw<64, true>(a, stream) : dispatch_hpw<64, false>(a, stream);
-  return causal ? dispatch_hpw<128, true>(a, stream) : dispatch_hpw<128, false>(a, stream);
+  a.window = window;
+  a.n_global = n_global;
+  // a window that covers every earlier key is the plain causal mask
+  const int mask = !causal ? kMaskNone : (window > 0 && window < N ? kMaskWindow : kMaskCausal);
+  if (d == 64) {
+    if (mask == kMaskNone) return dispatch_hpw<64, kMaskNone>(a, stream);
+    if (mask == kMaskCausal) return dispatch_hpw<64, kMaskCausal>(a, stream);
+    return dispatch_hpw<64, kMaskWindow>(a, stream);
+  }
+  if (mask == kMaskNone) return dispatch_hpw<128, kMaskNone>(a, stream);
+  if (mask == kMaskCausal) return dispatch_hpw<128, kMaskCausal>(a, stream);
+  return dispatch_hpw<128, kMaskWindow>(a, stream);
 }
 
 }  // namespace paa

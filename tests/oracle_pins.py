@@ -254,6 +254,17 @@ def pin_window_one_with_one_global_token():
     assert np.array_equal(o[0, 0, 0], v[0, 0, 0])
 
 
+def pin_window_rows_equal_full():
+    """attention_window_rows returns exactly the selected rows of attention_window."""
+    q, k, v = _rand((1, 4, 70, 8), 52), _rand((1, 2, 70, 8), 53), _rand((1, 2, 70, 8), 54)
+    o, lse = oracle.attention_window(q, k, v, 9, 3, 0.4)
+    rows = [(0, 0, 0), (0, 3, 69), (0, 1, 8), (0, 2, 9), (0, 2, 40)]
+    ro, rl = oracle.attention_window_rows(q, k, v, 9, 3, 0.4, rows)
+    for n, (b, h, i) in enumerate(rows):
+        assert np.allclose(ro[n], o[b, h, i], rtol=0, atol=1e-14)
+        assert abs(rl[n] - lse[b, h, i]) < 1e-14
+
+
 # ----------------------------------------------------------------- decode pins
 
 def _golden_example():

@@ -25,8 +25,8 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = paa.declared_functions()
-    assert set(names) == {"attn_fwd", "attn_fwd_f32", "paged_attn_decode_workspace_size", "paged_attn_decode",
-                          "attn_status_string"}
+    assert set(names) == {"attn_fwd", "attn_fwd_f32", "attn_fwd_window", "paged_attn_decode_workspace_size",
+                          "paged_attn_decode", "attn_status_string"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -58,6 +58,15 @@ P = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails valid
 def test_prefill_validation(L, args, code):
     assert L.attn_fwd(*args, None) == code
     assert L.attn_fwd_f32(*args, None) == code
+
+
+def test_window_validation(L):
+    base = (P, P, P, P, None, 1, 2, 2, 8, 64)
+    assert L.attn_fwd_window(*base, 0, 0, 0.1, None) == SHAPE       # window must be >= 1
+    assert L.attn_fwd_window(*base, 4, -1, 0.1, None) == SHAPE      # n_global must be >= 0
+    assert L.attn_fwd_window(*base, 4, 0, 0.0, None) == SCALE
+    assert L.attn_fwd_window(None, P, P, P, None, 1, 2, 2, 8, 64, 4, 0, 0.1, None) == NULL
+    assert L.attn_fwd_window(P, P, P, P, None, 0, 2, 2, 8, 64, 4, 0, 0.1, None) == ATTN_OK  # empty batch
 
 
 def test_decode_validation(L):

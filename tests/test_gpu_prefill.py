@@ -151,3 +151,59 @@ def test_empty_and_argument_errors():
     q4 = torch.zeros((1, 4, 16, 64), dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(RuntimeError, match="invalid shape"):
         paa.attn_fwd(q4, k3, k3, True)
+
+
+# ---- sliding window + global tokens (attn_fwd_window) ----
+
+def _run_window(a, w, window, n_global):
+    q, k, v = dev_bf16(a["q"]), dev_bf16(a["k"]), dev_bf16(a["v"])
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
+    o, _ = paa.attn_fwd_window(q, k, v, window, n_global, a["scale"], lse=lse)
+    torch.cuda.synchronize()
+    return host_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+# window below one key tile, across tiles, with and without global tokens, window 1, window >= N
+WINDOW_SMALL = [
+    (1, 4, 2, 300, 64, 16, 0), (1, 4, 2, 300, 64, 16, 5), (2, 8, 2, 333, 128, 100, 0),
+    (1, 8, 2, 333, 128, 100, 70), (1, 4, 4, 257, 128, 1, 0), (1, 6, 2, 129, 64, 1, 1),
+    (1, 8, 1, 200, 128, 64, 64), (1, 2, 2, 90, 64, 500, 3), (1, 4, 1, 520, 128, 130, 2),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,window,n_global", WINDOW_SMALL)
+def test_window_small_full_parity(B, H, Hkv, N, d, window, n_global):
+    w = PrefillWorkload("win", B, H, Hkv, N, d, True)
+    _announce(f"attn_fwd_window B{B} H{H} Hkv{Hkv} N{N} d{d} window={window} n_global={n_global}")
+    a = prefill_inputs(w, seed=N + window)
+    o, lse = _run_window(a, w, window, n_global)
+    ro, rl = oracle.attention_window(a["q"], a["k"], a["v"], window, n_global, a["scale"])
+    assert_close_bf16(o, ro)
+    assert_close_lse(lse, rl)
+
+
+def test_window_covering_everything_equals_causal():
+    """window >= N is the plain causal mask: bitwise the same output as attn_fwd."""
+    w = PrefillWorkload("wc", 1, 8, 2, 640, 128, True)
+    a = prefill_inputs(w, seed=31)
+    q, k, v = dev_bf16(a["q"]), dev_bf16(a["k"]), dev_bf16(a["v"])
+    o1, _ = paa.attn_fwd(q, k, v, True, a["scale"])
+    o2, _ = paa.attn_fwd_window(q, k, v, 640, 0, a["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_window_full_size_sampled():
+    """B=1, H=32, Hkv=8, N=16384, d=128, window 4096, 64 global tokens: sampled rows against the oracle."""
+    w = WORKLOADS["window_gqa_b1h32kv8n16384d128_w4096_g64"]
+    _announce(w.name)
+    a = prefill_inputs(w, seed=0)
+    o, lse = _run_window(a, w, w.window, w.n_global)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rows = sample_rows(w.B, w.H, w.N, 120, seed=2)
+    rows += [(0, h, i) for h in (0, 31) for i in (4095, 4096, 4160, 8191, 16383)]
+    rows = sorted(set(rows))
+    ro, rl = oracle.attention_window_rows(a["q"], a["k"], a["v"], w.window, w.n_global, a["scale"], rows)
+    idx = tuple(np.array(rows).T)
+    assert_close_bf16(o[idx], ro)
+    assert_close_lse(lse[idx], rl)

@@ -53,3 +53,11 @@ def test_decode_layout_and_poison():
     assert len(used) == len(set(used))  # distinct physical pages
     unused = sorted(set(range(40)) - set(used))
     assert np.all(kc[unused] == BF16_NAN)
+
+
+def test_window_visible_pairs_by_counting():
+    """Visible-pair count of a windowed workload equals a direct count of the rule on a small case."""
+    w = PrefillWorkload("t", 1, 1, 1, 37, 8, causal=True, window=5, n_global=3)
+    want = sum(1 for i in range(37) for j in range(i + 1) if i - j < 5 or j < 3)
+    assert w.visible_pairs() == want
+    assert PrefillWorkload("c", 1, 1, 1, 37, 8, causal=True).visible_pairs() == 37 * 38 // 2

@@ -52,6 +52,8 @@ class PrefillWorkload:
     q_mult: float = 1.0          # power of two, so it commutes with bf16 rounding
     k_outlier_frac: float = 0.0  # fraction of K rows per (b, kv head) scaled up
     k_outlier_mult: float = 8.0
+    window: int = 0              # causal sliding window width (0: none)
+    n_global: int = 0            # leading keys every later query sees (with a window)
 
     @property
     def scale(self) -> float:
@@ -59,6 +61,11 @@ class PrefillWorkload:
 
     def visible_pairs(self) -> int:
         """Query-key pairs the mask leaves visible, per (b, h)."""
+        if self.window:
+            i = np.arange(self.N)
+            in_window = np.minimum(i + 1, self.window)
+            extra_global = np.clip(np.minimum(self.n_global, i - self.window + 1), 0, None)
+            return int(in_window.sum() + extra_global.sum())
         return self.N * (self.N + 1) // 2 if self.causal else self.N * self.N
 
 
@@ -92,6 +99,8 @@ WORKLOADS = {
         PrefillWorkload("causal_gqa_long_b1h32kv8n16384d128", 1, 32, 8, 16384, 128, causal=True,
                         q_mult=4.0, k_outlier_frac=0.01, k_outlier_mult=8.0),
         DecodeWorkload("paged_decode_s64h32kv8d128", 64, 32, 8, 128, 512, 8192, 16, 40000),
+        PrefillWorkload("window_gqa_b1h32kv8n16384d128_w4096_g64", 1, 32, 8, 16384, 128, causal=True,
+                        window=4096, n_global=64),
     ]
 }
 
