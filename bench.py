@@ -51,6 +51,8 @@ COPY_KERNEL_TAG = "neg_kernel"  # torch's elementwise negate, used as the plain 
 PMC_CALLS = 3              # calls of each workload in a counter pass
 
 PREFILL_DEFAULT = "causal_b4h16n1024d64"
+SMALL_DECODE = "paged_decode_s4h32kv8d128_short"  # launch-bound: eager calls against graph replays
+GRAPH_LAYERS = 32  # decode calls per step in that comparison, each with its own KV cache
 DECODE_DEFAULT = "paged_decode_s64h32kv8d128"
 PREFILL_MORE = ("causal_gqa_b2h32kv8n4096d128", "causal_gqa_long_b1h32kv8n16384d128",
                 "window_gqa_b1h32kv8n16384d128_w4096_g64")
@@ -296,6 +298,41 @@ def run_bench(args, torch, paa) -> dict:
     del scratch
     cold_ms = statistics.median(cold)
 
+    # ---- a decode step of many layers on a small batch, where launch overhead matters: one eager call per
+    # layer against one replay of a graph holding every layer's call ----
+    sw = WORKLOADS[SMALL_DECODE]
+    phases.start(f"decode {sw.name} x {GRAPH_LAYERS} layers: eager calls, then graph replays")
+    layers = [DecodeCase(torch, paa, sw, args.seed + i) for i in range(GRAPH_LAYERS)]
+    graph = paa.PagedDecodeGraph([dict(q=c.q, k_cache=c.kc, v_cache=c.vc, block_table=c.bt, seq_lens=c.lens,
+                                       scale=c.a["scale"], workspace=layers[0].ws, out=c.o, lse=c.lse)
+                                  for c in layers])
+
+    def loop_ms(fn, n=50):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def eager_step():
+        for c in layers:
+            c()
+
+    eager_ms = loop_ms(eager_step)
+    graph_ms = loop_ms(graph.replay)
+    graph.close()
+    sdb = sum(decode_bytes(c.w, c.a["seq_lens"]) for c in layers)
+    small = {"workload": sw.name, "layers": GRAPH_LAYERS, "eager_us_per_step": round(eager_ms * 1e3, 1),
+             "graph_us_per_step": round(graph_ms * 1e3, 1), "algorithmic_bytes": round(sdb),
+             "eager_gbs": round(sdb / (eager_ms * 1e-3) / 1e9, 1), "graph_gbs": round(sdb / (graph_ms * 1e-3) / 1e9, 1)}
+    _log(f"{sw.name} x {GRAPH_LAYERS}: eager {eager_ms * 1e3:.1f} us/step, graph replay {graph_ms * 1e3:.1f} us/step")
+    del layers, graph
+
     more = []
     if not args.no_more:
         for name in PREFILL_MORE:
@@ -343,6 +380,7 @@ def run_bench(args, torch, paa) -> dict:
                    "algorithmic_gb": round(db / 1e9, 5), "roofline": dec_roof,
                    "cold_ms": round(cold_ms, 5), "cold_value": round(db / (cold_ms * 1e-3) / 1e9, 2)},
         "prefill_more": more,
+        "decode_graph": small,
         "cpu_baseline": base,
         "phases": phases.names,
         "device": {"name": props.name, "cus": props.multi_processor_count},

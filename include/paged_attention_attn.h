@@ -6,7 +6,9 @@
  * ---------------------------------------
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
  *    library allocates nothing, frees nothing, keeps no per-call state,
- *    never synchronises the stream and never reads device data on the host.
+ *    never synchronises the stream and never reads device data on the host
+ *    (the decode-graph entry points below create and release driver graph
+ *    objects, and only when asked to).
  *    Every call only enqueues kernels on `stream` (0 = the null stream) and
  *    returns; results are ready when that stream reaches them.
  *  - Tensors are dense, row-major (C order) with the shapes given below.
@@ -132,6 +134,57 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, c
                       const int32_t* seq_lens, void* o, float* lse, int num_seqs, int H, int Hkv, int d, int page_size,
                       int max_pages_per_seq, int num_pages, float scale, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
+
+/*
+ * The decode step as a replayable graph ("Fast Attention Kernels and
+ * Operator Fusion", section "Fusion and CUDA Graphs with torch.compile": a
+ * graph records a fixed sequence of GPU operations and replays it with one
+ * submission, which needs stable addresses and shapes; it helps most where
+ * launch overhead matters, as in small-batch decode).
+ *
+ * attn_decode_call holds the arguments of one paged_attn_decode call (same
+ * meaning, layout and rules; the stream is the graph's).  A model's decode
+ * step makes one such call per layer.
+ *
+ * paged_attn_decode_graph_create — checks every call exactly as
+ * paged_attn_decode does, then captures the num_calls calls in order (each a
+ * split-KV kernel and a reduce kernel) on capture_stream, which must not be
+ * the null stream and must not be capturing already, and instantiates the
+ * graph.  Calls run one after another, so they may share a workspace.  On
+ * success *graph_out receives an opaque handle owned by the caller (release
+ * it with paged_attn_decode_graph_destroy); on any error *graph_out is NULL
+ * and nothing stays captured.  The graph holds the pointers and sizes given
+ * here: each replay reads the CURRENT contents of every q, cache, block_table
+ * and seq_lens and overwrites o, lse and the workspaces, so callers update
+ * those buffers in place between replays.  Creating a graph allocates host
+ * and driver resources; replaying it allocates nothing.
+ */
+typedef struct attn_decode_call {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* o;
+  float* lse;
+  int num_seqs, H, Hkv, d, page_size, max_pages_per_seq, num_pages;
+  float scale;
+  void* workspace;
+  size_t workspace_bytes;
+} attn_decode_call;
+
+int paged_attn_decode_graph_create(const attn_decode_call* calls, int num_calls, hipStream_t capture_stream,
+                                   void** graph_out);
+
+/* paged_attn_decode_graph_launch — one replay of the captured decode calls on
+ * `stream` (asynchronous, stream-ordered).  ATTN_ERR_NULL_POINTER for a NULL
+ * handle, ATTN_ERR_LAUNCH if the runtime rejects the launch. */
+int paged_attn_decode_graph_launch(void* graph, hipStream_t stream);
+
+/* paged_attn_decode_graph_destroy — releases a handle from
+ * paged_attn_decode_graph_create (NULL is accepted).  Replays already
+ * enqueued are not waited for: synchronise the stream first. */
+int paged_attn_decode_graph_destroy(void* graph);
 
 /* attn_status_string — a static, human-readable description of a status code. */
 const char* attn_status_string(int status);

@@ -7,6 +7,7 @@ The kernels are hand-written HIP in ``csrc/`` behind the C ABI declared in
 
 from ._binding import (  # noqa: F401
     LIB_PATH,
+    PagedDecodeGraph,
     attn_fwd,
     attn_fwd_f32,
     attn_fwd_window,

@@ -23,6 +23,16 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "paged_attention_attn.h"
 _lib = None
 
 
+class DecodeCall(ctypes.Structure):
+    """The C struct attn_decode_call: the arguments of one paged_attn_decode call."""
+    _fields_ = [("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p), ("num_seqs", ctypes.c_int), ("H", ctypes.c_int), ("Hkv", ctypes.c_int),
+                ("d", ctypes.c_int), ("page_size", ctypes.c_int), ("max_pages_per_seq", ctypes.c_int),
+                ("num_pages", ctypes.c_int), ("scale", ctypes.c_float), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
 def lib() -> ctypes.CDLL:
     """The loaded HIP library (loaded on first use; raises if it was never built)."""
     global _lib
@@ -42,6 +52,12 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_decode_workspace_size.restype = sz
         L.paged_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
         L.paged_attn_decode.restype = i
+        L.paged_attn_decode_graph_create.argtypes = [ctypes.POINTER(DecodeCall), i, vp, ctypes.POINTER(ctypes.c_void_p)]
+        L.paged_attn_decode_graph_create.restype = i
+        L.paged_attn_decode_graph_launch.argtypes = [vp, vp]
+        L.paged_attn_decode_graph_launch.restype = i
+        L.paged_attn_decode_graph_destroy.argtypes = [vp]
+        L.paged_attn_decode_graph_destroy.restype = i
         L.attn_status_string.argtypes = [i]
         L.attn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -134,14 +150,8 @@ def paged_attn_decode_workspace_size(num_seqs: int, H: int, d: int, page_size: i
     return int(lib().paged_attn_decode_workspace_size(num_seqs, H, d, page_size, max_pages_per_seq))
 
 
-def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, scale: float | None = None, num_pages=None,
-                      workspace=None, out=None, lse=None):
-    """Paged decode: q [S,H,d] bf16, caches [P,16,Hkv,d] bf16, block_table [S,max_pages] int32, seq_lens [S] int32.
-
-    Returns (out [S,H,d] bf16, lse [S,H] fp32 or None).  ``workspace`` is a
-    uint8 device tensor of at least paged_attn_decode_workspace_size() bytes
-    (allocated here when not given).
-    """
+def _decode_args(q, k_cache, v_cache, block_table, seq_lens, scale, num_pages, workspace, out, lse):
+    """Checks the decode tensors and fills in the defaults; returns the C argument list (without a stream)."""
     _require(q, "q", torch.bfloat16, 3)
     dev = q.device
     _require(k_cache, "k_cache", torch.bfloat16, 4, dev)
@@ -168,7 +178,72 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, scale: float |
         _require(lse, "lse", torch.float32, 2, dev)
     if scale is None:
         scale = d ** -0.5
-    _check(lib().paged_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
-                                   _ptr(out), _ptr(lse), S, H, Hkv, d, page_size, max_pages, int(num_pages),
-                                   float(scale), _ptr(workspace), workspace.numel(), _stream(dev)))
+    args = [_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse), S, H,
+            Hkv, d, page_size, max_pages, int(num_pages), float(scale), _ptr(workspace), workspace.numel()]
+    return args, workspace, out, lse
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, scale: float | None = None, num_pages=None,
+                      workspace=None, out=None, lse=None):
+    """Paged decode: q [S,H,d] bf16, caches [P,16,Hkv,d] bf16, block_table [S,max_pages] int32, seq_lens [S] int32.
+
+    Returns (out [S,H,d] bf16, lse [S,H] fp32 or None).  ``workspace`` is a
+    uint8 device tensor of at least paged_attn_decode_workspace_size() bytes
+    (allocated here when not given).
+    """
+    args, _, out, lse = _decode_args(q, k_cache, v_cache, block_table, seq_lens, scale, num_pages, workspace, out,
+                                     lse)
+    _check(lib().paged_attn_decode(*args, _stream(q.device)))
     return out, lse
+
+
+class PagedDecodeGraph:
+    """Decode calls captured once as a hipGraph (paged_attn_decode_graph_create) and replayed as one submission.
+
+    ``calls`` is a list of dicts, one per paged_attn_decode call in order (say one per layer of a
+    model's decode step), with the keyword names of :func:`paged_attn_decode` (q, k_cache, v_cache,
+    block_table, seq_lens, and optionally scale, num_pages, workspace, out, lse).  Their tensors are
+    the graph's fixed buffers: update the inputs in place between replays; every replay rewrites the
+    outputs (``self.outputs[i]`` is call i's (out, lse)).  Missing workspaces and outputs are
+    allocated here, at creation; a replay allocates nothing.
+    """
+
+    def __init__(self, calls, capture_stream=None):
+        structs, self.outputs, self._keep = [], [], []
+        for c in calls:
+            args, ws, out, lse = _decode_args(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"],
+                                              c.get("scale"), c.get("num_pages"), c.get("workspace"), c.get("out"),
+                                              c.get("lse"))
+            structs.append(DecodeCall(*[a.value if isinstance(a, ctypes.c_void_p) else a for a in args]))
+            self.outputs.append((out, lse))
+            self._keep.append((c, ws, out, lse))  # the graph holds their addresses
+        if not structs:
+            raise ValueError("at least one decode call is needed")
+        self.device = calls[0]["q"].device
+        self._stream = capture_stream if capture_stream is not None else torch.cuda.Stream(self.device)
+        arr = (DecodeCall * len(structs))(*structs)
+        handle = ctypes.c_void_p()
+        self._handle = None
+        _check(lib().paged_attn_decode_graph_create(arr, len(structs), ctypes.c_void_p(self._stream.cuda_stream),
+                                                    ctypes.byref(handle)))
+        self._handle = handle
+
+    def replay(self, stream=None):
+        """Enqueue one replay on ``stream`` (default: the current stream); returns the list of (out, lse)."""
+        if self._handle is None:
+            raise RuntimeError("graph not available")
+        s = _stream(self.device) if stream is None else ctypes.c_void_p(stream.cuda_stream)
+        _check(lib().paged_attn_decode_graph_launch(self._handle, s))
+        return self.outputs
+
+    def close(self):
+        if self._handle is not None:
+            torch.cuda.synchronize(self.device)
+            _check(lib().paged_attn_decode_graph_destroy(self._handle))
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown
+            pass

@@ -155,6 +155,83 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, c
                                               (int)w.slots, stream));
 }
 
+// ---- the decode step as a replayable hipGraph ----
+
+namespace {
+struct DecodeGraph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+// The same checks as paged_attn_decode, for one call of a graph (nothing is launched).
+int check_decode_call(const attn_decode_call& c) {
+  if (c.num_seqs < 0 || c.H < 1 || c.Hkv < 1 || c.H % c.Hkv != 0 || c.max_pages_per_seq < 0 || c.num_pages < 0)
+    return ATTN_ERR_INVALID_SHAPE;
+  if (c.d != 64 && c.d != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  if (c.page_size != 16) return ATTN_ERR_UNSUPPORTED_PAGE_SIZE;
+  if (c.H / c.Hkv > 16) return ATTN_ERR_UNSUPPORTED_GROUP;
+  if (!scale_ok(c.scale)) return ATTN_ERR_INVALID_SCALE;
+  if (c.num_seqs == 0) return ATTN_OK;
+  if (!c.q || !c.k_cache || !c.v_cache || (!c.block_table && c.max_pages_per_seq > 0) || !c.seq_lens || !c.o ||
+      !c.workspace)
+    return ATTN_ERR_NULL_POINTER;
+  if (c.workspace_bytes < paged_attn_decode_workspace_size(c.num_seqs, c.H, c.d, c.page_size, c.max_pages_per_seq))
+    return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  return ATTN_OK;
+}
+}  // namespace
+
+int paged_attn_decode_graph_create(const attn_decode_call* calls, int num_calls, hipStream_t capture_stream,
+                                   void** graph_out) {
+  if (graph_out == nullptr) return ATTN_ERR_NULL_POINTER;
+  *graph_out = nullptr;
+  if (calls == nullptr || capture_stream == nullptr) return ATTN_ERR_NULL_POINTER;  // the null stream cannot be captured
+  if (num_calls < 1) return ATTN_ERR_INVALID_SHAPE;
+  // every argument check happens before capture begins
+  for (int i = 0; i < num_calls; ++i) {
+    const int rc = check_decode_call(calls[i]);
+    if (rc != ATTN_OK) return rc;
+  }
+  // one-time kernel attributes are set outside the capture
+  for (int i = 0; i < num_calls; ++i)
+    if (paa::decode_setup(calls[i].d) != hipSuccess) return ATTN_ERR_LAUNCH;
+  if (hipStreamBeginCapture(capture_stream, hipStreamCaptureModeThreadLocal) != hipSuccess) return ATTN_ERR_LAUNCH;
+  int rc = ATTN_OK;
+  for (int i = 0; i < num_calls && rc == ATTN_OK; ++i) {
+    const attn_decode_call& c = calls[i];
+    rc = paged_attn_decode(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, c.o, c.lse, c.num_seqs, c.H, c.Hkv,
+                           c.d, c.page_size, c.max_pages_per_seq, c.num_pages, c.scale, c.workspace,
+                           c.workspace_bytes, capture_stream);
+  }
+  hipGraph_t graph = nullptr;
+  const hipError_t end = hipStreamEndCapture(capture_stream, &graph);  // always end the capture
+  if (rc != ATTN_OK || end != hipSuccess || graph == nullptr) {
+    if (graph != nullptr) hipGraphDestroy(graph);
+    return rc != ATTN_OK ? rc : ATTN_ERR_LAUNCH;
+  }
+  hipGraphExec_t exec = nullptr;
+  if (hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess) {
+    hipGraphDestroy(graph);
+    return ATTN_ERR_LAUNCH;
+  }
+  *graph_out = new DecodeGraph{graph, exec};
+  return ATTN_OK;
+}
+
+int paged_attn_decode_graph_launch(void* graph, hipStream_t stream) {
+  if (graph == nullptr) return ATTN_ERR_NULL_POINTER;
+  return hipGraphLaunch(static_cast<DecodeGraph*>(graph)->exec, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int paged_attn_decode_graph_destroy(void* graph) {
+  if (graph == nullptr) return ATTN_OK;
+  DecodeGraph* g = static_cast<DecodeGraph*>(graph);
+  const hipError_t e1 = hipGraphExecDestroy(g->exec);
+  const hipError_t e2 = hipGraphDestroy(g->graph);
+  delete g;
+  return e1 == hipSuccess && e2 == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "success";
@@ -166,7 +243,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_MISALIGNED: return "misaligned pointer: tensors need 16-byte, lse/tables 4-byte alignment";
     case ATTN_ERR_TOO_LARGE: return "sizes too large for the launch grid or 64-bit offsets";
     case ATTN_ERR_UNSUPPORTED_GROUP: return "unsupported grouping: at most 16 query heads per KV head in decode";
-    case ATTN_ERR_LAUNCH: return "kernel launch failed (hipGetLastError)";
+    case ATTN_ERR_LAUNCH: return "kernel launch or graph operation failed (HIP runtime error)";
     case ATTN_ERR_INVALID_SCALE: return "invalid scale: it must be a finite positive number";
     default: return "unknown status code";
   }

@@ -19,6 +19,8 @@ hipError_t prefill_f32(const float* q, const float* k, const float* v, float* o,
 // (never of seq_lens).  decode_max_parts(H) bounds decode_parts(...) for every
 // Hkv that divides H with at most 16 query heads per KV head.
 int decode_max_parts(int H);
+// One-time per-process setup of the decode kernels (no launch); done before any graph capture.
+hipError_t decode_setup(int d);
 int decode_parts(int num_seqs, int H, int Hkv, int max_pages_per_seq);
 
 hipError_t paged_decode_bf16(const void* q, const void* k_cache, const void* v_cache, const int* block_table,

@@ -49,6 +49,7 @@ constexpr int kPage = 16;         // tokens per page (the ABI accepts only 16)
 constexpr int kStepTokens = 32;   // 2 pages per MFMA k-step over tokens
 constexpr int kMaxWaves = 8;      // KV heads (waves) per workgroup
 constexpr int kTargetWaves = 2048;  // waves per launch: 8 per CU on 256 CUs
+constexpr int kReduceSplitSlots = 16;  // partials per row from which the reduce gives a row 4 waves
 
 template <int D>
 struct DecodeLds {
@@ -413,16 +414,26 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeAr
   }
 }
 
-// One wave per (sequence, head): merge the partials of that row.  The
+// WPR waves per (sequence, head) merge the partials of that row.  The
 // sequence's partials sit in slots first..last; slot j came from range j - s,
 // and a range with no pages (possible when there are more ranges than pages)
-// wrote nothing, so it is skipped.
-template <int D>
+// wrote nothing, so it is skipped.  Every wave takes the max LSE over all the
+// row's slots; with WPR > 1 the slots are then cut into WPR consecutive
+// pieces, one per wave, and the waves' weighted sums are added in LDS in wave
+// order (a fixed order: the result does not depend on timing).  Several waves
+// per row pay off when there are few rows and many slots per row (a small
+// batch of long sequences), where one wave would walk its slots one round
+// trip at a time.
+template <int D, int WPR>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
+  static_assert(WPR == 1 || WPR == 4, "one row per wave, or one row per workgroup");
   constexpr int kPerLane = D / 64;
-  const int row = blockIdx.x * 4 + threadIdx.x / 64;
+  constexpr int kBatch = 8;  // partial rows loaded together
+  const int wave = threadIdx.x / 64;
+  const int row = blockIdx.x * (4 / WPR) + wave / WPR;
+  const int piece = wave % WPR;
   const int lane = threadIdx.x % 64;
-  if (row >= a.S * a.H) return;
+  if (row >= a.S * a.H) return;  // with WPR == 4 the whole workgroup leaves together
   const int s = row / a.H;
   const int h = row % a.H;
   const int L = seq_len_clamped(a, s);
@@ -436,30 +447,31 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
     const int first = min(max(a.ws_range[2 * s], 0), a.slots - 1);
     const int last = min(max(a.ws_range[2 * s + 1], first), a.slots - 1);
     const int n = last - first + 1;
+    const int per = (n + WPR - 1) / WPR;
+    const int lo = min(piece * per, n);
+    const int hi = min(lo + per, n);
     auto lse_of = [&](int j) -> float {  // LSE of slot first + j, -inf for an empty range
       const int r = first + j - s;
       if (r < 0 || r >= a.parts || range_begin(r, total, a.parts) >= range_begin(r + 1, total, a.parts))
         return -INFINITY;
       return a.ws_lse[(size_t)(first + j) * a.H + h];
     };
-    // max over the partials' LSE, 64 at a time (the first 64 are kept)
-    const float lse0 = lane < n ? lse_of(lane) : -INFINITY;
-    mx = lse0;
-    for (int c0 = 64; c0 < n; c0 += 64) mx = fmaxf(mx, c0 + lane < n ? lse_of(c0 + lane) : -INFINITY);
-    // the first kEarly partial rows are loaded in the same round trip as the LSEs above
-    constexpr int kEarly = 8;
-    float ov[kEarly][kPerLane];
+    // this wave's first 64 LSEs and first kBatch partial rows are loaded in the same round trip as the
+    // LSEs of the max below
+    const float lse_lo = lo + lane < hi ? lse_of(lo + lane) : -INFINITY;
+    float ov[kBatch][kPerLane];
 #pragma unroll
-    for (int u = 0; u < kEarly; ++u) {
-      const float* src = a.ws_o + ((size_t)(first + min(u, n - 1)) * a.H + h) * D;
+    for (int u = 0; u < kBatch; ++u) {
+      const float* src = a.ws_o + ((size_t)(first + min(lo + u, n - 1)) * a.H + h) * D;
 #pragma unroll
       for (int i = 0; i < kPerLane; ++i) ov[u][i] = src[lane + 64 * i];
     }
+    for (int c0 = 0; c0 < n; c0 += 64) mx = fmaxf(mx, c0 + lane < n ? lse_of(c0 + lane) : -INFINITY);
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
-    for (int c0 = 0; c0 < n && mx != -INFINITY; c0 += 64) {
-      const int cnt = min(64, n - c0);
-      const float lc = c0 == 0 ? lse0 : (lane < cnt ? lse_of(c0 + lane) : -INFINITY);
+    for (int c0 = lo; c0 < hi && mx != -INFINITY; c0 += 64) {
+      const int cnt = min(64, hi - c0);
+      const float lc = c0 == lo ? lse_lo : (lane < cnt ? lse_of(c0 + lane) : -INFINITY);
       const float w = lc == -INFINITY ? 0.f : __expf(lc - mx);  // a partial without a visible key weighs 0
       float ws = w;
 #pragma unroll
@@ -468,20 +480,19 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
       // a slot whose weight is 0 (empty range, or no visible key) may hold anything, so its values
       // are replaced by 0 rather than multiplied by 0
       int j0 = 0;
-      if (c0 == 0) {
+      if (c0 == lo) {
 #pragma unroll
-        for (int u = 0; u < kEarly; ++u) {
+        for (int u = 0; u < kBatch; ++u) {
           const float wj = u < cnt ? __shfl(w, u) : 0.f;
 #pragma unroll
           for (int i = 0; i < kPerLane; ++i) out[i] = fmaf(wj, wj == 0.f ? 0.f : ov[u][i], out[i]);
         }
-        j0 = kEarly;
+        j0 = kBatch;
       }
-      // the rest four at a time, loads issued together
-      for (; j0 < cnt; j0 += 4) {
-        float v[4][kPerLane], wj[4];
+      for (; j0 < cnt; j0 += kBatch) {
+        float v[kBatch][kPerLane], wj[kBatch];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kBatch; ++u) {
           const int j = min(j0 + u, cnt - 1);
           wj[u] = j0 + u < cnt ? __shfl(w, j) : 0.f;
           const float* src = a.ws_o + ((size_t)(first + c0 + j) * a.H + h) * D;
@@ -489,11 +500,30 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
           for (int i = 0; i < kPerLane; ++i) v[u][i] = src[lane + 64 * i];
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < kBatch; ++u)
 #pragma unroll
           for (int i = 0; i < kPerLane; ++i) out[i] = fmaf(wj[u], wj[u] == 0.f ? 0.f : v[u][i], out[i]);
       }
     }
+  }
+  if constexpr (WPR > 1) {
+    __shared__ float red_o[WPR][D];
+    __shared__ float red_w[WPR];
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) red_o[piece][lane + 64 * i] = out[i];
+    if (lane == 0) red_w[piece] = wsum;
+    __syncthreads();
+    if (piece != 0) return;
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+      float acc = red_o[0][lane + 64 * i];
+#pragma unroll
+      for (int p = 1; p < WPR; ++p) acc += red_o[p][lane + 64 * i];
+      out[i] = acc;
+    }
+    wsum = red_w[0];
+#pragma unroll
+    for (int p = 1; p < WPR; ++p) wsum += red_w[p];
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   uint16_t* orow = a.o + (size_t)row * D;
@@ -511,25 +541,38 @@ int waves_for(int Hkv) {
   return 1;
 }
 
+// Raise the partial kernel's dynamic LDS limit to the largest slice, once per process
+// (thread-safe static initialisation).
+template <int D>
+hipError_t setup_decode() {
+  static const hipError_t attr = hipFuncSetAttribute((const void*)decode_partial_kernel<D>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     kMaxWaves * DecodeLds<D>::kPerWave * 2);
+  return attr;
+}
+
 template <int D>
 hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {
   a.waves = waves_for(a.Hkv);
   const int lds_bytes = a.waves * DecodeLds<D>::kPerWave * 2;
-  // allow the largest slice once; thread-safe static initialisation
-  static const hipError_t attr = hipFuncSetAttribute((const void*)decode_partial_kernel<D>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     kMaxWaves * DecodeLds<D>::kPerWave * 2);
+  const hipError_t attr = setup_decode<D>();
   if (attr != hipSuccess) return attr;
   dim3 grid1((unsigned)a.parts, (unsigned)(a.Hkv / a.waves));
   hipLaunchKernelGGL(decode_partial_kernel<D>, grid1, dim3(64 * a.waves), lds_bytes, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long rows = (long long)a.S * a.H;
-  hipLaunchKernelGGL(decode_reduce_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+  // slots per row average parts / S + 1: with many, a workgroup per row splits them over its 4 waves
+  if (a.parts >= kReduceSplitSlots * a.S)
+    hipLaunchKernelGGL((decode_reduce_kernel<D, 4>), dim3((unsigned)rows), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_reduce_kernel<D, 1>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t decode_setup(int d) { return d == 64 ? setup_decode<64>() : setup_decode<128>(); }
 
 int decode_max_parts(int H) {
   // Hkv >= H / 16 (at most 16 query heads per KV head), so kTargetWaves / Hkv <= 16 * kTargetWaves / H

@@ -26,7 +26,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = paa.declared_functions()
     assert set(names) == {"attn_fwd", "attn_fwd_f32", "attn_fwd_window", "paged_attn_decode_workspace_size",
-                          "paged_attn_decode", "attn_status_string"}
+                          "paged_attn_decode", "paged_attn_decode_graph_create", "paged_attn_decode_graph_launch",
+                          "paged_attn_decode_graph_destroy", "attn_status_string"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -91,6 +92,38 @@ def test_decode_validation(L):
     assert call(scale=float("nan")) == SCALE
     assert call(S=0) == ATTN_OK
     assert call(S=0, q=None, ws=None) == ATTN_OK  # empty: pointers unused
+
+
+def test_decode_graph_validation(L):
+    """Argument errors come back before any capture begins (no GPU needed)."""
+    ws = paa.paged_attn_decode_workspace_size(4, 8, 128, 16, 10)
+    handle = ctypes.c_void_p(0x1234)
+    S = ctypes.c_void_p(0x20000)  # a stand-in stream handle: never used, every call fails validation first
+
+    def call(**kw):
+        a = dict(q=0x10000, k_cache=0x10000, v_cache=0x10000, block_table=0x10000, seq_lens=0x10000, o=0x10000,
+                 lse=None, num_seqs=4, H=8, Hkv=2, d=128, page_size=16, max_pages_per_seq=10, num_pages=100,
+                 scale=0.1, workspace=0x10000, workspace_bytes=ws)
+        a.update(kw)
+        return _binding.DecodeCall(**a)
+
+    def create(calls, stream=S):
+        arr = (_binding.DecodeCall * len(calls))(*calls)
+        return L.paged_attn_decode_graph_create(arr, len(calls), stream, ctypes.byref(handle))
+
+    assert create([call()], stream=None) == NULL
+    assert handle.value is None  # cleared on error
+    assert create([call(), call(page_size=32)]) == PAGE  # every call is checked
+    assert create([call(d=96)]) == HEAD_DIM
+    assert create([call(workspace_bytes=ws - 1)]) == WS
+    assert create([call(scale=-1.0)]) == SCALE
+    assert create([call(block_table=None)]) == NULL
+    arr = (_binding.DecodeCall * 1)(call())
+    assert L.paged_attn_decode_graph_create(arr, 0, S, ctypes.byref(handle)) == SHAPE
+    assert L.paged_attn_decode_graph_create(None, 1, S, ctypes.byref(handle)) == NULL
+    assert L.paged_attn_decode_graph_create(arr, 1, S, None) == NULL
+    assert L.paged_attn_decode_graph_launch(None, None) == NULL
+    assert L.paged_attn_decode_graph_destroy(None) == ATTN_OK
 
 
 def test_workspace_linear_in_length(L):

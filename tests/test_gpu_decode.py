@@ -186,3 +186,94 @@ def test_decode_repeated_calls_reuse_workspace():
         ro, rl = _oracle(a)
         assert_close_bf16(host_f64(o), ro)
         assert_close_lse(lse.cpu().numpy().astype(np.float64), rl)
+
+
+def test_decode_graph_replays_match_eager_and_oracle():
+    """A captured decode step replayed four times, with new queries and lengths written in place by eager
+    work between replays: every replay equals an eager call bitwise and the oracle within tolerance."""
+    w = DecodeWorkload("graph", 6, 32, 8, 128, 100, 2000, 16, 1000)
+    a = decode_inputs(w, seed=41)
+    q, kc, vc = dev_bf16(a["q"]), dev_bf16(a["k_cache"]), dev_bf16(a["v_cache"])
+    bt, lens = dev_i32(a["block_table"]), dev_i32(a["seq_lens"])
+    lse = torch.empty((6, 32), dtype=torch.float32, device="cuda:0")
+    g = paa.PagedDecodeGraph([dict(q=q, k_cache=kc, v_cache=vc, block_table=bt, seq_lens=lens, scale=a["scale"],
+                                   lse=lse)])
+    rng = np.random.default_rng(42)
+    try:
+        for it in range(4):
+            new_q = rng.standard_normal(a["q"].shape).astype(np.float32)
+            from workloads import f32_to_bf16_bits
+            q_bits = f32_to_bf16_bits(new_q)
+            new_lens = np.array([rng.integers(0, L + 1) for L in a["seq_lens"]], dtype=np.int32)  # within the pages
+            q.copy_(dev_bf16(q_bits))
+            lens.copy_(dev_i32(new_lens))
+            torch.cuda.synchronize()
+            (o_g, l_g), = g.replay()
+            torch.cuda.synchronize()
+            o_g, l_g = o_g.clone(), l_g.clone()
+            l_e = torch.empty_like(lse)
+            o_e, _ = paa.paged_attn_decode(q, kc, vc, bt, lens, a["scale"], lse=l_e)
+            torch.cuda.synchronize()
+            assert torch.equal(o_g.view(torch.int16), o_e.view(torch.int16)), f"replay {it}"
+            assert torch.equal(l_g, l_e), f"replay {it}"
+            ro, rl = oracle.paged_decode(q_bits, a["k_cache"], a["v_cache"], a["block_table"], new_lens, a["scale"])
+            assert_close_bf16(host_f64(o_g), ro)
+            assert_close_lse(l_g.cpu().numpy().astype(np.float64), rl)
+    finally:
+        g.close()
+
+
+def test_decode_graph_full_workload_matches_eager():
+    """The 64-sequence workload captured once: replay equals the eager call bitwise."""
+    w = WORKLOADS["paged_decode_s64h32kv8d128"]
+    a = decode_inputs(w, seed=0)
+    q, kc, vc = dev_bf16(a["q"]), dev_bf16(a["k_cache"]), dev_bf16(a["v_cache"])
+    bt, lens = dev_i32(a["block_table"]), dev_i32(a["seq_lens"])
+    g = paa.PagedDecodeGraph([dict(q=q, k_cache=kc, v_cache=vc, block_table=bt, seq_lens=lens, scale=a["scale"])])
+    try:
+        o_g = g.replay()[0][0].clone()
+        o_g2 = g.replay()[0][0]
+        torch.cuda.synchronize()
+        o_e, _ = paa.paged_attn_decode(q, kc, vc, bt, lens, a["scale"])
+        torch.cuda.synchronize()
+        assert torch.equal(o_g.view(torch.int16), o_e.view(torch.int16))
+        assert torch.equal(o_g2.view(torch.int16), o_e.view(torch.int16))
+    finally:
+        g.close()
+
+
+def test_decode_graph_layers_in_one_submission():
+    """Several decode calls (the layers of one decode step, with their own caches, head dims and group sizes,
+    sharing one workspace as consecutive calls on one stream may) captured into one graph: every call's
+    output equals its eager call bitwise and the oracle within tolerance, over two replays."""
+    shapes = [(128, 32, 8), (64, 8, 8), (128, 16, 1), (128, 32, 8), (64, 6, 2)]
+    lens = [1, 17, 300, 0, 1000, 64]
+    inputs = [decode_inputs(DecodeWorkload("layer", len(lens), H, Hkv, d, 1, 1024, 16, 400), seed=60 + i,
+                            seq_lens=lens) for i, (d, H, Hkv) in enumerate(shapes)]
+    ws_bytes = max(paa.paged_attn_decode_workspace_size(len(lens), H, d, 16, a["block_table"].shape[1])
+                   for (d, H, _), a in zip(shapes, inputs))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda:0")
+    layers = [dict(q=dev_bf16(a["q"]), k_cache=dev_bf16(a["k_cache"]), v_cache=dev_bf16(a["v_cache"]),
+                   block_table=dev_i32(a["block_table"]), seq_lens=dev_i32(a["seq_lens"]), scale=a["scale"],
+                   workspace=ws, lse=torch.empty((len(lens), H), dtype=torch.float32, device="cuda:0"))
+              for (d, H, _), a in zip(shapes, inputs)]
+    _announce(f"decode graph of {len(layers)} calls")
+    g = paa.PagedDecodeGraph(layers)
+    try:
+        for rep in range(2):
+            g.replay()
+            torch.cuda.synchronize()
+            outs = [(o.clone(), l.clone()) for o, l in g.outputs]
+            for i, (c, a) in enumerate(zip(layers, inputs)):
+                l_e = torch.empty_like(c["lse"])
+                o_e, _ = paa.paged_attn_decode(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"],
+                                               c["scale"], lse=l_e)
+                torch.cuda.synchronize()
+                o_g, l_g = outs[i]
+                assert torch.equal(o_g.view(torch.int16), o_e.view(torch.int16)), f"replay {rep} call {i}"
+                assert torch.equal(l_g, l_e), f"replay {rep} call {i}"
+                ro, rl = _oracle(a)
+                assert_close_bf16(host_f64(o_g), ro)
+                assert_close_lse(l_g.cpu().numpy().astype(np.float64), rl)
+    finally:
+        g.close()

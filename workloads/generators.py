@@ -99,6 +99,7 @@ WORKLOADS = {
         PrefillWorkload("causal_gqa_long_b1h32kv8n16384d128", 1, 32, 8, 16384, 128, causal=True,
                         q_mult=4.0, k_outlier_frac=0.01, k_outlier_mult=8.0),
         DecodeWorkload("paged_decode_s64h32kv8d128", 64, 32, 8, 128, 512, 8192, 16, 40000),
+        DecodeWorkload("paged_decode_s4h32kv8d128_short", 4, 32, 8, 128, 256, 1024, 16, 512),
         PrefillWorkload("window_gqa_b1h32kv8n16384d128_w4096_g64", 1, 32, 8, 16384, 128, causal=True,
                         window=4096, n_global=64),
     ]
