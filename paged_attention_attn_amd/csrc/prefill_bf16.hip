@@ -43,6 +43,7 @@
 //    dispatcher spreads over the 8 XCDs) differ in their (batch, KV head), so
 //    each XCD's L2 keeps serving the same K/V heads.
 
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -117,6 +118,7 @@ struct PrefillArgs {
   float rescale_raw; // kRescaleLog2 / scale_log2: the lazy rescale threshold in raw score units
   int window;        // sliding window width (kMaskWindow only)
   int n_global;      // leading keys visible to every later query (kMaskWindow only)
+  int mirror;        // 1 when the whole grid is resident at once: pair heavy and light units (see below)
 };
 
 // WAVES waves per workgroup, RB blocks of 32 query rows per wave, STAGES-deep K and V rings in LDS.
@@ -183,7 +185,15 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   const int colhalf = (lane / 16) % 2;
 
   // ---- work unit: heaviest query tiles first ----
-  const int unit = blockIdx.x;
+  // When the grid is larger than what the chip holds at once, workgroups start as others finish
+  // and heaviest-first keeps the tail short.  When the whole grid is resident at once, the
+  // dispatcher gives each CU workgroups a fixed distance apart in launch order, so the second half
+  // of the grid is laid out in reverse: workgroup u of the first half (heavy) and workgroup
+  // u + units/2 (light) then carry complementary causal work.
+  const int units = a.n_qtiles * a.units_per_qt;
+  const int half_units = units / 2;
+  const int unit = (a.mirror && (int)blockIdx.x >= half_units) ? units - 1 + half_units - (int)blockIdx.x
+                                                                : (int)blockIdx.x;
   const int qt = a.n_qtiles - 1 - unit / a.units_per_qt;
   int rest = unit % a.units_per_qt;
   const int group = a.H / a.Hkv;
@@ -443,6 +453,317 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Ping-pong variant: 8 waves in two groups of 4 (waves w and w + 4 share a SIMD).  A wave's
+// work per key tile is an MFMA phase (scores of tile i, and O += P V of tile i - 1) and a VALU
+// phase (mask, row max and exponentials of tile i).  A single wave cannot overlap its own MFMA
+// and VALU work, but a SIMD overlaps an MFMA wave with a VALU wave, so group B runs one phase
+// behind group A: in every period one group is in its MFMA phase and the other in its VALU
+// phase, and a workgroup barrier ends each period.  Stage s of the LDS ring holds K_s and
+// V_{s-1}; both groups read it in periods 2s (A) and 2s + 1 (B), and its refill with stage
+// s + STAGES goes out at the start of period 2s + 2.
+template <int D, int MASK, int HPW, int STAGES>
+__global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
+  constexpr int WAVES = 8;
+  using T = TileLayout<D>;
+  constexpr bool CAUSAL = MASK != kMaskNone;
+  constexpr bool WINDOW = MASK == kMaskWindow;
+  constexpr int kRowBlocks = WAVES / HPW;              // waves per head in a workgroup
+  constexpr int kTileRows = kRowBlocks * 32;           // query rows per head in a workgroup
+  constexpr int kKSteps = D / 16;
+  constexpr int kDBlocks = D / 32;
+  constexpr int kBlocksPerWave = T::kBlocks / WAVES;   // 1 KB loads per wave per K or V tile
+  constexpr int kLoadsPerStage = 2 * kBlocksPerWave;
+  static_assert(T::kBlocks % WAVES == 0, "tile rows must split evenly over the waves");
+  static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
+
+  __shared__ __attribute__((aligned(1024))) char k_st0[T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_st1[T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_st2[T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_st3[T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_st0[T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_st1[T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_st2[T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_st3[T::kTileBytes];
+  auto kst = [&](auto i_tag) __attribute__((always_inline)) -> PAA_LDS char* {
+    constexpr int i = decltype(i_tag)::value % STAGES;
+    if constexpr (i == 0) return (PAA_LDS char*)k_st0;
+    else if constexpr (i == 1) return (PAA_LDS char*)k_st1;
+    else if constexpr (i == 2) return (PAA_LDS char*)k_st2;
+    else return (PAA_LDS char*)k_st3;
+  };
+  auto vst = [&](auto i_tag) __attribute__((always_inline)) -> PAA_LDS char* {
+    constexpr int i = decltype(i_tag)::value % STAGES;
+    if constexpr (i == 0) return (PAA_LDS char*)v_st0;
+    else if constexpr (i == 1) return (PAA_LDS char*)v_st1;
+    else if constexpr (i == 2) return (PAA_LDS char*)v_st2;
+    else return (PAA_LDS char*)v_st3;
+  };
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform, so phase branches are scalar
+  const int grp = wave / 4;   // 0: group A (leads), 1: group B (one phase behind)
+  const int lane = tid % 64;
+  const int half = lane / 32;
+  const int l32 = lane % 32;
+  const int gi = lane % 16;
+  const int colhalf = (lane / 16) % 2;
+
+  // ---- work unit (as in the four-wave kernel) ----
+  const int units = a.n_qtiles * a.units_per_qt;
+  const int half_units = units / 2;
+  const int unit = (a.mirror && (int)blockIdx.x >= half_units) ? units - 1 + half_units - (int)blockIdx.x
+                                                                : (int)blockIdx.x;
+  const int qt = a.n_qtiles - 1 - unit / a.units_per_qt;
+  int rest = unit % a.units_per_qt;
+  const int group = a.H / a.Hkv;
+  const int subgroups = group / HPW;
+  const int hsub = rest % subgroups;
+  rest /= subgroups;
+  const int g = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+
+  const int head = g * group + hsub * HPW + wave / kRowBlocks;
+  const int q0_tile = qt * kTileRows;
+  const int q0 = q0_tile + (wave % kRowBlocks) * 32;
+
+  const size_t N = a.N;
+  const uint16_t* qh = a.q + ((size_t)b * a.H + head) * N * D;
+  const uint16_t* kh = a.k + ((size_t)b * a.Hkv + g) * N * D;
+  const uint16_t* vh = a.v + ((size_t)b * a.Hkv + g) * N * D;
+
+  // ---- key tiles: iteration t is tile tile_of(t); this wave computes iterations [0, n_act) ----
+  const int kv_end = CAUSAL ? min(a.N, q0_tile + kTileRows) : a.N;
+  const int n_tiles = (kv_end + kBc - 1) / kBc;
+  int n_glob = 0, j_win = 0;
+  if constexpr (WINDOW) {
+    n_glob = min(n_tiles, (a.n_global + kBc - 1) / kBc);
+    j_win = max(n_glob, max(0, q0_tile - a.window + 1) / kBc);
+  }
+  const int n_iter = n_glob + (n_tiles - j_win);
+  auto tile_of = [&](int t) __attribute__((always_inline)) { return t < n_glob ? t : j_win + (t - n_glob); };
+  const int last_tile = CAUSAL ? min(n_tiles - 1, (q0 + 31) / kBc) : n_tiles - 1;
+  const int n_act = last_tile < n_glob ? last_tile + 1 : n_glob + max(0, last_tile - j_win + 1);
+
+  auto dma = [&](const uint16_t* src, int j, PAA_LDS char* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kBlocksPerWave; ++i) {
+      const int blk = wave * kBlocksPerWave + i;
+      const int r = blk * T::kRowsPerBlock + lane / T::kCpr;
+      const int c = (lane % T::kCpr) ^ swz<D>(r);
+      const int key = min(j * kBc + r, a.N - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)key * D + c * 8), (PAA_LDS void*)(dst + blk * 1024),
+                                       16, 0, 0);
+    }
+  };
+  // stage s: K of iteration s and V of iteration s - 1; iterations past the end repeat the last
+  // one (the buffer is free and never read), so every stage issues the same number of loads
+  auto issue_stage = [&](auto s_tag, int s) __attribute__((always_inline)) {
+    using Prev = std::integral_constant<int, decltype(s_tag)::value + STAGES - 1>;
+    dma(kh, tile_of(min(s, n_iter - 1)), kst(s_tag));
+    dma(vh, tile_of(min(max(s - 1, 0), n_iter - 1)), vst(Prev{}));
+  };
+
+  // ---- Q fragments first (their loads then retire before the ring's) ----
+  u32x4_t qf[kKSteps];
+  {
+    const int row = q0 + l32;
+#pragma unroll
+    for (int t = 0; t < kKSteps; ++t) {
+      if (row < a.N)
+        qf[t] = *(const u32x4_t*)(qh + (size_t)row * D + 16 * t + 8 * half);
+      else
+        qf[t] = u32x4_t{0, 0, 0, 0};
+    }
+  }
+  // prologue: stage 0 (K_0 only), then stages 1 .. STAGES-1
+  dma(kh, tile_of(0), kst(std::integral_constant<int, 0>{}));
+  auto prologue = [&](auto s_tag, int s) __attribute__((always_inline)) { issue_stage(s_tag, s); };
+  for_stages<1, STAGES>(prologue, 0, STAGES);
+
+  int koff[kKSteps];
+#pragma unroll
+  for (int t = 0; t < kKSteps; ++t) koff[t] = l32 * T::kRowBytes + (((2 * t + half) ^ swz<D>(l32)) * 16);
+  int voff[kDBlocks][2];
+#pragma unroll
+  for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = 4 * half + gi / 4 + 8 * e;
+      const int col = 32 * db + 16 * colhalf + 4 * (gi % 4);
+      voff[db][e] = r * T::kRowBytes + (((col / 8) ^ swz<D>(r)) * 16) + (col % 8) * 2;
+    }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16_t acc[kDBlocks];
+#pragma unroll
+  for (int db = 0; db < kDBlocks; ++db)
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  f32x16_t s[2];
+  u32x4_t pf[4];
+
+  // MFMA phase of iteration i: S^T of iteration i (stage i's K) and O += P_{i-1} V_{i-1} (stage i's V)
+  auto m_phase = [&](auto u_tag, int i) __attribute__((always_inline)) {
+    using U = decltype(u_tag);
+    using Prev = std::integral_constant<int, U::value + STAGES - 1>;
+    const PAA_LDS char* kt = kst(U{});
+    const PAA_LDS char* vt = vst(Prev{});
+    // each block keeps its LDS reads a few ahead of its MFMAs (not all hoisted to the top, which
+    // would take more registers than the wave has)
+    if (i < n_act) {
+#pragma unroll
+      for (int t = 0; t < kKSteps; ++t)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const u32x4_t kf = *(const PAA_LDS u32x4_t*)(kt + koff[t] + mb * 32 * T::kRowBytes);
+          s[mb] = t == 0 ? mfma32x32x16(kf, qf[t], f32x16_t{}) : mfma32x32x16(kf, qf[t], s[mb]);
+        }
+      constexpr int kLead = 4;
+      __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+      for (int k = 0; k < 2 * kKSteps - kLead; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);
+    }
+    if (i >= 1 && i - 1 < n_act) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db) {
+          const u32x2_t lo = lds_read_tr16((const PAA_LDS uint16_t*)(vt + voff[db][0] + 16 * ks * T::kRowBytes));
+          const u32x2_t hi = lds_read_tr16((const PAA_LDS uint16_t*)(vt + voff[db][1] + 16 * ks * T::kRowBytes));
+          acc[db] = mfma32x32x16(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pf[ks], acc[db]);
+        }
+      constexpr int kLead = 4;  // MFMAs whose two reads go out ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLead, 1);
+#pragma unroll
+      for (int k = 0; k < 4 * kDBlocks - kLead; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kLead, 1);
+    }
+  };
+
+  // VALU phase of iteration i: mask, row max, lazy rescale, exponentials, row sum, bf16 P
+  auto v_phase = [&](int i) __attribute__((always_inline)) {
+    if (i < 0 || i >= n_act) return;
+    const int k0 = tile_of(i) * kBc;
+    const bool need_window = WINDOW && (k0 <= q0 + 31 - a.window) && (k0 + kBc - 1 >= a.n_global);
+    const bool need_mask = (CAUSAL && (k0 + kBc - 1 > q0)) || (k0 + kBc > a.N) || need_window;
+    if (need_mask) {
+      const int row = q0 + l32;
+      const int lim = CAUSAL ? min(row, a.N - 1) : a.N - 1;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + 32 * mb + 8 * (e / 4) + 4 * half + (e % 4);
+          const bool out_of_window = WINDOW && row - key >= a.window && key >= a.n_global;
+          if (key > lim || out_of_window) s[mb][e] = -INFINITY;
+        }
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[mb][e]);
+    tmax = fmaxf(tmax, swap_halves(tmax, half));
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + a.rescale_raw) != 0) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_run - m_new) * a.scale_log2);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
+    }
+    const float neg_ms = m_run == -INFINITY ? 0.f : -m_run * a.scale_log2;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      float p[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        p[e] = fast_exp2(fmaf(s[mb][e], a.scale_log2, neg_ms));
+        ps[e % 4] += p[e];
+      }
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh)
+        pf[2 * mb + sh] = u32x4_t{pack_bf16x2(p[8 * sh + 0], p[8 * sh + 1]), pack_bf16x2(p[8 * sh + 2], p[8 * sh + 3]),
+                                  pack_bf16x2(p[8 * sh + 4], p[8 * sh + 5]), pack_bf16x2(p[8 * sh + 6], p[8 * sh + 7])};
+    }
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+
+  // Q and stage 0 have landed (loads after them: stages 1 .. STAGES-1)
+  wait_vmcnt<(STAGES - 1) * kLoadsPerStage>();
+  tile_barrier();
+
+  // Periods 2i and 2i + 1 use stage i (u = i % STAGES).  Each group runs its own copy of the loop
+  // (same barriers, in the same number), so the state flows straight from one phase to the next.
+  auto run = [&](auto grp_tag) __attribute__((always_inline)) {
+    constexpr bool kLead = decltype(grp_tag)::value == 0;
+    auto period_pair = [&](auto u_tag, int i) __attribute__((always_inline)) {
+      using U = decltype(u_tag);
+      using Refill = std::integral_constant<int, U::value + STAGES - 1>;  // stage i - 1 + STAGES
+      if (i >= 1) issue_stage(Refill{}, i - 1 + STAGES);
+      if constexpr (kLead) m_phase(U{}, i); else v_phase(i - 1);
+      tile_barrier();
+      if constexpr (kLead) v_phase(i); else m_phase(U{}, i);
+      wait_vmcnt<(STAGES - 2) * kLoadsPerStage>();  // stage i + 1 has landed
+      tile_barrier();
+    };
+    for (int i0 = 0; i0 <= n_iter; i0 += STAGES) for_stages<0, STAGES>(period_pair, i0, n_iter + 1);
+  };
+  if (grp == 0)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, 1>{});
+  wait_vmcnt<0>();  // no load may still be writing this workgroup's LDS when it exits
+
+  // ---- epilogue: O = acc / l, LSE = scale * m + ln(l) ----
+  const int row = q0 + l32;
+  const float l_tot = l_run + swap_halves(l_run, half);
+  const float inv_l = 1.f / l_tot;
+  if (row < a.N) {
+    uint16_t* orow = a.o + (((size_t)b * a.H + head) * N + row) * D;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = 32 * db + 8 * gq + 4 * half;
+        u32x2_t w = {pack_bf16x2(acc[db][4 * gq + 0] * inv_l, acc[db][4 * gq + 1] * inv_l),
+                     pack_bf16x2(acc[db][4 * gq + 2] * inv_l, acc[db][4 * gq + 3] * inv_l)};
+        *(u32x2_t*)(orow + d0) = w;
+      }
+    }
+    if (a.lse != nullptr && half == 0) a.lse[((size_t)b * a.H + head) * N + row] = a.scale * m_run + __logf(l_tot);
+  }
+}
+
+// Workgroups of one kernel instantiation the current device holds at once (CUs x workgroups per
+// CU), 0 if unknown; queried once per device.
+template <typename Kernel>
+long long resident_workgroups(Kernel kernel, int threads) {
+  static std::atomic<long long> cached[16];  // zero: not yet known
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 16) {
+    const long long c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+  const long long c = (long long)cus * per_cu;
+  if (dev < 16) cached[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
 template <int D, int MASK, int HPW, int WAVES, int RB, int STAGES>
 hipError_t launch_prefill(const PrefillArgs& base, hipStream_t stream) {
   PrefillArgs a = base;
@@ -451,9 +772,33 @@ hipError_t launch_prefill(const PrefillArgs& base, hipStream_t stream) {
   a.units_per_qt = a.B * a.Hkv * ((a.H / a.Hkv) / HPW);
   const long long units = (long long)a.n_qtiles * a.units_per_qt;
   if (units > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, MASK, HPW, WAVES, RB, STAGES>), dim3((unsigned)units),
-                     dim3(64 * WAVES), 0, stream, a);
+  const auto kernel = prefill_bf16_kernel<D, MASK, HPW, WAVES, RB, STAGES>;
+  a.mirror = MASK != kMaskNone && units <= resident_workgroups(kernel, 64 * WAVES) ? 1 : 0;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)units), dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D, int MASK, int HPW, int STAGES>
+hipError_t launch_prefill_pp(const PrefillArgs& base, hipStream_t stream) {
+  PrefillArgs a = base;
+  constexpr int kTileRows = (8 / HPW) * 32;
+  a.n_qtiles = (a.N + kTileRows - 1) / kTileRows;
+  a.units_per_qt = a.B * a.Hkv * ((a.H / a.Hkv) / HPW);
+  const long long units = (long long)a.n_qtiles * a.units_per_qt;
+  if (units > 0x7fffffffLL) return hipErrorInvalidValue;
+  const auto kernel = prefill_pp_kernel<D, MASK, HPW, STAGES>;
+  a.mirror = MASK != kMaskNone && units <= resident_workgroups(kernel, 512) ? 1 : 0;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)units), dim3(512), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int MASK>
+hipError_t dispatch_pp(const PrefillArgs& a, hipStream_t stream) {
+  constexpr int kStages = 2;
+  const int group = a.H / a.Hkv;
+  if (group % 4 == 0) return launch_prefill_pp<D, MASK, 4, kStages>(a, stream);
+  if (group % 2 == 0) return launch_prefill_pp<D, MASK, 2, kStages>(a, stream);
+  return launch_prefill_pp<D, MASK, 1, kStages>(a, stream);
 }
 
 template <int D, int MASK, int WAVES>
@@ -477,7 +822,13 @@ hipError_t dispatch_hpw(const PrefillArgs& a, hipStream_t stream) {
   const int hpw = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
   const long long rows8 = (8 / hpw) * 32;
   const long long units8 = (long long)a.B * a.Hkv * (group / hpw) * ((a.N + rows8 - 1) / rows8);
-  if (units8 >= 1024) return dispatch_group<D, MASK, 8>(a, stream);
+  if (units8 >= 1024) {
+    // d = 128: the MFMA and VALU halves of a tile are of similar length, and the ping-pong
+    // kernel overlaps them across the two waves of each SIMD.  d = 64: the exponentials
+    // dominate, and the lock-step kernel is as fast.
+    if constexpr (D == 128) return dispatch_pp<D, MASK>(a, stream);
+    else return dispatch_group<D, MASK, 8>(a, stream);
+  }
   return dispatch_group<D, MASK, 4>(a, stream);
 }
 

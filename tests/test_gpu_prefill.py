@@ -207,3 +207,32 @@ def test_window_full_size_sampled():
     idx = tuple(np.array(rows).T)
     assert_close_bf16(o[idx], ro)
     assert_close_lse(lse[idx], rl)
+
+
+# Grids large enough (at least 1024 eight-wave units) for the d=128 ping-pong kernel, with a
+# ragged sequence end and every head-grouping branch; sampled rows include the last rows and
+# the first rows of each 64-row block boundary around the tail.
+PINGPONG = [(4, 32, 8, 2000, True, 0, 0), (4, 32, 8, 2000, False, 0, 0), (8, 16, 8, 1999, True, 0, 0),
+            (32, 8, 8, 1000, True, 0, 0), (4, 32, 8, 2000, True, 300, 17)]
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,causal,window,n_global", PINGPONG)
+def test_bf16_pingpong_grids_sampled(B, H, Hkv, N, causal, window, n_global):
+    w = PrefillWorkload("pingpong", B, H, Hkv, N, 128, causal)
+    _announce(f"pingpong B{B} H{H} Hkv{Hkv} N{N} causal{causal} window{window} g{n_global}")
+    a = prefill_inputs(w, seed=N + H)
+    if window:
+        o, lse = _run_window(a, w, window, n_global)
+    else:
+        o, lse = _run_bf16(a, w)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rows = sample_rows(B, H, N, 96, seed=3)
+    rows += [(B - 1, h, i) for h in (0, H - 1) for i in (0, 63, 64, N - 65, N - 64, N - 2, N - 1)]
+    rows = sorted(set(rows))
+    if window:
+        ro, rl = oracle.attention_window_rows(a["q"], a["k"], a["v"], window, n_global, a["scale"], rows)
+    else:
+        ro, rl = oracle.attention_rows(a["q"], a["k"], a["v"], causal, a["scale"], rows)
+    idx = tuple(np.array(rows).T)
+    assert_close_bf16(o[idx], ro)
+    assert_close_lse(lse[idx], rl)
