@@ -24,8 +24,10 @@ from .exact import (  # noqa: F401
     attention_rows,
     attention_window,
     attention_window_rows,
+    paged_append,
     paged_decode,
     paged_gather,
+    paged_prefill,
     softmax_probs,
     bf16_bits_to_f64,
 )

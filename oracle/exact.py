@@ -29,6 +29,13 @@ Readings taken where the pages are silent (each repeated in the design doc):
   at page ``block_table[s, t // page_size]``, slot ``t % page_size``; slots at
   t >= L are never read.
 * An empty key set (L = 0) gives O = 0 and LSE = -inf (the empty sum).
+* Chunked prefill over a paged cache: a sequence holds ctx tokens in its pages
+  and brings a chunk of new tokens (queries, keys, values).  The chunk's keys and
+  values are appended at positions ctx, ctx + 1, ...; chunk query i sits at
+  position ctx + i and sees positions 0 .. ctx + i (the causal mask aligned at
+  the end, so that a chunk of one token is a decode step and a chunk with no
+  context is causal prefill).  Chunk tokens are packed [T, heads, d] with
+  sequence s owning rows q_start[s] .. q_start[s+1]-1.
 * Sliding window with global tokens ("Kernel Fusion and Custom Kernels",
   section "4. FlashInfer", block-sparse masks: the Longformer pattern of a
   sliding window plus global tokens), read under the causal mask: key j is
@@ -36,8 +43,8 @@ Readings taken where the pages are silent (each repeated in the design doc):
   global token's own row is causal anyway, so "global tokens see everything"
   adds nothing once the causal mask applies.
 
-The helpers ``_kv_head``, ``_scores``, ``_apply_causal``, ``_window_mask``, ``_softmax`` and
-``_page_slot`` are looked up at call time, so tests can plant a mistake in
+The helpers ``_kv_head``, ``_scores``, ``_apply_causal``, ``_window_mask``, ``_softmax``,
+``_page_slot`` and ``_chunk_positions`` are looked up at call time, so tests can plant a mistake in
 one of them (on the CPU) and check that a pin catches it.
 """
 
@@ -255,3 +262,67 @@ def paged_decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, seqs=
             o_h, l_h = _attend(q64[s, h][None, :], kk[:, g], vv[:, g], scale, None)
             o[n, h], lse[n, h] = o_h[0], l_h[0]
     return o, lse
+
+
+def _chunk_positions(ctx: int, n: int) -> np.ndarray:
+    """Logical positions of a chunk's n tokens in a sequence that already holds ctx tokens."""
+    return ctx + np.arange(n)
+
+
+def paged_append(k_cache, v_cache, k_new, v_new, block_table, ctx_lens, q_start):
+    """The caches after each sequence's chunk of new tokens has been appended.
+
+    Sequence s already holds ctx_lens[s] tokens; its chunk is rows q_start[s] ..
+    q_start[s+1]-1 of k_new / v_new ([T, Hkv, d]).  Chunk token i goes to logical
+    position ctx_lens[s] + i, which lives at page block_table[s, pos // page_size],
+    slot pos % page_size (the block-table translation of "Fast Attention Kernels and
+    Operator Fusion", section "Paged Attention Kernels"; appending to a cache is one of
+    the features listed in "Kernel Fusion and Custom Kernels", section "4. FlashInfer").
+    Returns new arrays of the caches' dtype; the inputs are left unchanged.
+    """
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    page_size = kc.shape[1]
+    k_new, v_new = np.asarray(k_new), np.asarray(v_new)
+    for s in range(len(ctx_lens)):
+        lo, hi = int(q_start[s]), int(q_start[s + 1])
+        pos = _chunk_positions(int(ctx_lens[s]), hi - lo)
+        blk, slot = _page_slot(pos, page_size)
+        pages = np.asarray(block_table)[s][blk]
+        kc[pages, slot] = k_new[lo:hi]
+        vc[pages, slot] = v_new[lo:hi]
+    return kc, vc
+
+
+def paged_prefill(q, k_new, v_new, k_cache, v_cache, block_table, ctx_lens, q_start, scale: float, seqs=None):
+    """Chunked prefill over a paged KV cache, with the chunk's keys/values appended.
+
+    q [T, H, d] holds the chunks' queries, sequence s owning rows q_start[s] ..
+    q_start[s+1]-1 (q_start has S + 1 entries); k_new, v_new [T, Hkv, d] are the same
+    tokens' keys and values.  After :func:`paged_append`, chunk query i of sequence s
+    sits at position ctx_lens[s] + i and attends, causally, over positions 0 .. ctx_lens[s] + i
+    of its sequence: the cached context, then the chunk's own keys up to itself.
+    Returns (O [T, H, d], LSE [T, H], k_cache_after, v_cache_after); O and LSE are
+    float64 and cover the rows of the sequences in ``seqs`` (default: all), in order.
+    """
+    q64 = _as_f64(q)
+    T, H, d = q64.shape
+    Hkv = np.asarray(k_cache).shape[2]
+    _check_heads(H, Hkv)
+    kc, vc = paged_append(k_cache, v_cache, k_new, v_new, block_table, ctx_lens, q_start)
+    seqs = range(len(ctx_lens)) if seqs is None else list(seqs)
+    o, lse = [], []
+    for s in seqs:
+        lo, hi = int(q_start[s]), int(q_start[s + 1])
+        ctx = int(ctx_lens[s])
+        kk, vv = paged_gather(kc, vc, np.asarray(block_table)[s], ctx + hi - lo)
+        o_s = np.zeros((hi - lo, H, np.asarray(v_cache).shape[3]))
+        l_s = np.zeros((hi - lo, H))
+        pos = _chunk_positions(ctx, hi - lo)
+        for h in range(H):
+            g = _kv_head(h, H, Hkv)
+            o_s[:, h], l_s[:, h] = _attend(q64[lo:hi, h], kk[:, g], vv[:, g], scale, pos)
+        o.append(o_s)
+        lse.append(l_s)
+    o = np.concatenate(o) if o else np.zeros((0, H, d))
+    lse = np.concatenate(lse) if lse else np.zeros((0, H))
+    return o, lse, kc, vc

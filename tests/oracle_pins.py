@@ -350,4 +350,145 @@ def pin_decode_page_permutation_invariance():
     assert np.all(np.isfinite(o1)) and np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+# ---------------------------------------------------------- chunked paged prefill pins
+
+def _chunked_case(ctxs, qlens, H, Hkv, d, num_pages, seed, ps=16):
+    """Sequences with ctx tokens placed by hand in shuffled pages (NaN elsewhere) and chunks of new tokens."""
+    rng = np.random.default_rng(seed)
+    S = len(ctxs)
+    max_pages = max((c + n + ps - 1) // ps for c, n in zip(ctxs, qlens))
+    perm = rng.permutation(num_pages)
+    bt = np.full((S, max_pages), -1, dtype=np.int32)
+    kc = np.full((num_pages, ps, Hkv, d), np.nan)
+    vc = np.full((num_pages, ps, Hkv, d), np.nan)
+    ctx_k, ctx_v, used = [], [], 0
+    for s, (c, n) in enumerate(zip(ctxs, qlens)):
+        npg = (c + n + ps - 1) // ps
+        bt[s, :npg] = perm[used:used + npg]
+        used += npg
+        kk, vv = rng.standard_normal((c, Hkv, d)), rng.standard_normal((c, Hkv, d))
+        for t in range(c):
+            kc[bt[s, t // ps], t % ps] = kk[t]
+            vc[bt[s, t // ps], t % ps] = vv[t]
+        ctx_k.append(kk)
+        ctx_v.append(vv)
+    T = sum(qlens)
+    q_start = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = rng.standard_normal((T, H, d))
+    k_new, v_new = rng.standard_normal((T, Hkv, d)), rng.standard_normal((T, Hkv, d))
+    return dict(q=q, k_new=k_new, v_new=v_new, kc=kc, vc=vc, bt=bt, ctx=np.array(ctxs, dtype=np.int32),
+                q_start=q_start, ctx_k=ctx_k, ctx_v=ctx_v)
+
+
+def _run_chunked(c, scale):
+    return oracle.paged_prefill(c["q"], c["k_new"], c["v_new"], c["kc"], c["vc"], c["bt"], c["ctx"], c["q_start"],
+                                scale)
+
+
+def pin_chunked_prefill_torch_sdpa():
+    """Each sequence against torch's CPU float64 SDPA over its context followed by its chunk (joined by
+    plain concatenation), with the end-aligned causal mask built by loops as a boolean matrix."""
+    import torch
+    import torch.nn.functional as F
+    for ctxs, qlens, H, Hkv, d, seed in [([0, 20, 37], [5, 16, 1], 4, 2, 8, 40), ([70, 3], [33, 64], 6, 3, 16, 41),
+                                         ([16], [17], 2, 2, 4, 42)]:
+        c = _chunked_case(ctxs, qlens, H, Hkv, d, 40, seed)
+        o, lse, _, _ = _run_chunked(c, 0.37)
+        for s, (ctx, n) in enumerate(zip(ctxs, qlens)):
+            lo = int(c["q_start"][s])
+            kfull = np.concatenate([c["ctx_k"][s], c["k_new"][lo:lo + n]])  # [ctx + n, Hkv, d]
+            vfull = np.concatenate([c["ctx_v"][s], c["v_new"][lo:lo + n]])
+            allowed = torch.zeros((n, ctx + n), dtype=torch.bool)
+            for i in range(n):
+                for j in range(ctx + i + 1):
+                    allowed[i, j] = True
+            qt = torch.from_numpy(c["q"][lo:lo + n].transpose(1, 0, 2)[None].copy())
+            kt = torch.from_numpy(kfull.transpose(1, 0, 2)[None].copy())
+            vt = torch.from_numpy(vfull.transpose(1, 0, 2)[None].copy())
+            ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=allowed, scale=0.37, enable_gqa=True)
+            ref = ref[0].numpy().transpose(1, 0, 2)
+            assert np.allclose(o[lo:lo + n], ref, rtol=0, atol=1e-10)
+            assert np.all(np.isfinite(lse[lo:lo + n]))
+
+
+def pin_append_block_table_worked_example():
+    """The pages' table [17, 4, 29, 8] with 40 tokens cached and a chunk of 9: the chunk lands at the hand-derived
+    locations (token 47 at block 29 slot 15, token 48 at block 8 slot 0), and nothing else changes."""
+    ex = _golden_example()
+    table, ps = ex["physical_blocks"], ex["page_size"]
+    Hkv, d, ctx, n = 2, 4, 40, 9
+    kk, vv, kc, vc = _pool_from_table(table, ctx, Hkv, d, 32, ps, 43)
+    k_new, v_new = _rand((n, Hkv, d), 44), _rand((n, Hkv, d), 45)
+    bt = np.array([table], dtype=np.int32)
+    kc2, vc2 = oracle.paged_append(kc, vc, k_new, v_new, bt, np.array([ctx]), np.array([0, n]))
+    where = {t: (page, slot) for t, page, slot in ex["token_locations"]}
+    for t in (47, 48):
+        page, slot = where[t]
+        assert np.array_equal(kc2[page, slot], k_new[t - ctx]) and np.array_equal(vc2[page, slot], v_new[t - ctx])
+    changed = ~((kc2 == kc) | (np.isnan(kc2) & np.isnan(kc)))
+    assert changed.sum() == n * Hkv * d
+    assert np.array_equal(kc2[29, 8:16], k_new[:8]) and np.array_equal(kc2[8, 0], k_new[8])
+    assert np.array_equal(kc2[17], kc[17], equal_nan=True) and np.array_equal(kc2[4], kc[4], equal_nan=True)
+    assert np.array_equal(kc, _pool_from_table(table, ctx, Hkv, d, 32, ps, 43)[2], equal_nan=True)  # input untouched
+
+
+def pin_chunk_of_one_token_is_decode():
+    """A chunk of one token is a decode step: it equals decode over the appended cache with L = ctx + 1."""
+    ctxs = [0, 15, 16, 33]
+    c = _chunked_case(ctxs, [1] * 4, 4, 2, 8, 20, 46)
+    o, lse, kc2, vc2 = _run_chunked(c, 0.41)
+    od, ld = oracle.paged_decode(c["q"], kc2, vc2, c["bt"], c["ctx"] + 1, 0.41)
+    assert np.allclose(o, od, rtol=0, atol=1e-14) and np.allclose(lse, ld, rtol=0, atol=1e-14)
+
+
+def pin_chunk_without_context_is_causal_prefill():
+    """With nothing cached, a chunk is causal prefill over its own tokens."""
+    c = _chunked_case([0], [29], 4, 2, 8, 8, 47)
+    o, lse, _, _ = _run_chunked(c, 0.3)
+    op, lp = oracle.attention(c["q"].transpose(1, 0, 2)[None], c["k_new"].transpose(1, 0, 2)[None],
+                              c["v_new"].transpose(1, 0, 2)[None], True, 0.3)
+    assert np.allclose(o, op[0].transpose(1, 0, 2), rtol=0, atol=1e-13)
+    assert np.allclose(lse, lp[0].T, rtol=0, atol=1e-13)
+
+
+def pin_chunking_does_not_change_results():
+    """A sequence prefilled as one chunk, or as two chunks where the second sees the first through the cache,
+    gives the same outputs for the second chunk's tokens and the same cache."""
+    H, Hkv, d, n1, n2 = 4, 2, 8, 23, 27
+    c = _chunked_case([0], [n1 + n2], H, Hkv, d, 10, 48)
+    o, lse, kc_a, vc_a = _run_chunked(c, 0.5)
+    # first chunk alone, then the second with ctx = n1
+    o1, _, kc1, vc1 = oracle.paged_prefill(c["q"][:n1], c["k_new"][:n1], c["v_new"][:n1], c["kc"], c["vc"], c["bt"],
+                                           np.array([0]), np.array([0, n1]), 0.5)
+    o2, l2, kc2, vc2 = oracle.paged_prefill(c["q"][n1:], c["k_new"][n1:], c["v_new"][n1:], kc1, vc1, c["bt"],
+                                            np.array([n1]), np.array([0, n2]), 0.5)
+    assert np.allclose(o2, o[n1:], rtol=0, atol=1e-13) and np.allclose(l2, lse[n1:], rtol=0, atol=1e-13)
+    assert np.allclose(o1, o[:n1], rtol=0, atol=1e-13)
+    assert np.array_equal(kc2, kc_a, equal_nan=True) and np.array_equal(vc2, vc_a, equal_nan=True)
+
+
+def pin_chunked_prefill_brute_force_tiny():
+    """Agreement with an fsum loop that walks the block table token by token (to 1e-12)."""
+    ps = 16
+    for ctxs, qlens, seed in [([3], [2], 49), ([16, 0], [1, 3], 50), ([31], [4], 51)]:
+        H, Hkv, d = 2, 1, 3
+        c = _chunked_case(ctxs, qlens, H, Hkv, d, 6, seed)
+        o, lse, _, _ = _run_chunked(c, 0.7)
+        for s, (ctx, n) in enumerate(zip(ctxs, qlens)):
+            lo = int(c["q_start"][s])
+            for i in range(n):
+                for h in range(H):
+                    def key(t):
+                        if t < ctx:
+                            return c["kc"][c["bt"][s, t // ps], t % ps, 0], c["vc"][c["bt"][s, t // ps], t % ps, 0]
+                        return c["k_new"][lo + t - ctx, 0], c["v_new"][lo + t - ctx, 0]
+                    sc = [0.7 * math.fsum(c["q"][lo + i, h] * key(t)[0]) for t in range(ctx + i + 1)]
+                    m = max(sc)
+                    w = [math.exp(x - m) for x in sc]
+                    l = math.fsum(w)
+                    want = [math.fsum(w[t] * key(t)[1][e] for t in range(ctx + i + 1)) / l for e in range(d)]
+                    assert np.allclose(o[lo + i, h], want, rtol=0, atol=1e-12)
+                    assert abs(lse[lo + i, h] - (m + math.log(l))) < 1e-12
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

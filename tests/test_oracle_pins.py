@@ -78,6 +78,9 @@ MUTANTS = {
     "window_off_by_one": ("_window_mask", _mut_window_inclusive),
     "window_global_off_by_one": ("_window_mask", _mut_window_global_inclusive),
     "window_not_causal": ("_window_mask", _mut_window_not_causal),
+    "chunk_aligned_at_start": ("_chunk_positions", lambda ctx, n: np.arange(n)),
+    "chunk_positions_off_by_one": ("_chunk_positions", lambda ctx, n: ctx + 1 + np.arange(n)),
+    "chunk_positions_reversed": ("_chunk_positions", lambda ctx, n: ctx + np.arange(n)[::-1]),
 }
 
 
