@@ -52,7 +52,9 @@ PMC_CALLS = 3              # calls of each workload in a counter pass
 
 PREFILL_DEFAULT = "causal_b4h16n1024d64"
 SMALL_DECODE = "paged_decode_s4h32kv8d128_short"  # launch-bound: eager calls against graph replays
-GRAPH_LAYERS = 32  # decode calls per step in that comparison, each with its own KV cache
+CHUNKED = "chunked_prefill_s16h32kv8d128_ctx0to4096_q512"  # chunked prefill over a paged cache, with append
+GRAPH_LAYERS = 32
+PREWARM_S = 0.25  # untimed calls of the step before its W warm-up steps (see prewarm)  # decode calls per step in that comparison, each with its own KV cache
 DECODE_DEFAULT = "paged_decode_s64h32kv8d128"
 PREFILL_MORE = ("causal_gqa_b2h32kv8n4096d128", "causal_gqa_long_b1h32kv8n16384d128",
                 "window_gqa_b1h32kv8n16384d128_w4096_g64")
@@ -77,6 +79,21 @@ def decode_bytes(w, lens) -> float:
     kv = float(lens.sum()) * w.Hkv * w.d * 2 * 2
     qo = 2.0 * len(lens) * w.H * w.d * 2
     return kv + qo + 4.0 * len(lens) * w.H + 4.0 * float((-(-lens // w.page_size)).sum()) + 4.0 * len(lens)
+
+
+def chunked_flops(w, ctx_lens) -> float:
+    """4 d H per visible (query, key) pair; chunk query i of a sequence with ctx cached tokens sees ctx + i + 1."""
+    q = w.q_len
+    pairs = sum(q * int(c) + q * (q + 1) // 2 for c in ctx_lens)
+    return 4.0 * w.d * w.H * pairs
+
+
+def chunked_bytes(w, ctx_lens) -> float:
+    """Compulsory bytes: Q, O, the chunk's K/V read once, the context's K/V read once, the chunk's K/V
+    written to the cache, LSE written."""
+    T = w.num_seqs * w.q_len
+    ctx = int(sum(int(c) for c in ctx_lens))
+    return 2.0 * (2 * T * w.H * w.d + 2 * T * w.Hkv * w.d + 2 * ctx * w.Hkv * w.d + 2 * T * w.Hkv * w.d) + 4.0 * T * w.H
 
 
 def source_digest() -> str:
@@ -119,8 +136,22 @@ def to_dev_i32(torch, x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to("cuda:0")
 
 
+def prewarm(torch, fn, seconds=0.2):
+    """Call fn for ``seconds`` of wall time before anything is timed: after idle gaps (input set-up on
+    the host) the GPU clock takes tens of milliseconds of load to return to its steady value."""
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def timed(torch, fn, iters, warmup):
-    """Median and mean (ms) of event-timed calls of fn on the current stream."""
+    """Median and mean (ms) of event-timed calls of fn on the current stream (after a pre-warm)."""
+    prewarm(torch, fn, 0.1)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -192,6 +223,26 @@ class DecodeCase:
                                    workspace=self.ws, out=self.o, lse=self.lse)
 
 
+class ChunkedCase:
+    def __init__(self, torch, paa, w, seed):
+        from workloads import chunked_prefill_inputs
+        self.w = w
+        self.a = a = chunked_prefill_inputs(w, seed=seed)
+        self.q = to_dev_bf16(torch, a["q"])
+        self.kn, self.vn = to_dev_bf16(torch, a["k_new"]), to_dev_bf16(torch, a["v_new"])
+        self.kc, self.vc = to_dev_bf16(torch, a["k_cache"]), to_dev_bf16(torch, a["v_cache"])
+        self.bt, self.ctx = to_dev_i32(torch, a["block_table"]), to_dev_i32(torch, a["ctx_lens"])
+        self.qs = to_dev_i32(torch, a["q_start"])
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((self.q.shape[0], w.H), dtype=torch.float32, device="cuda:0")
+        self.paa = paa
+
+    def __call__(self):
+        # the same chunk appended again each call: the cache holds the same values afterwards
+        self.paa.paged_prefill(self.q, self.kn, self.vn, self.kc, self.vc, self.bt, self.ctx, self.qs,
+                               max_q_len=self.a["max_q_len"], scale=self.a["scale"], out=self.o, lse=self.lse)
+
+
 # ----------------------------------------------------------------- CPU baseline (oracle)
 
 def cpu_baseline(pc, dc, min_seconds=10.0):
@@ -252,6 +303,12 @@ def run_bench(args, torch, paa) -> dict:
 
     # ---- W untimed steps, then exactly K timed steps, synchronised on both sides ----
     phases.start(f"step: prefill {pw.name} + decode {dw.name}")
+
+    def step():
+        pc()
+        dc()
+
+    prewarm(torch, step, PREWARM_S)
     for _ in range(args.warmup):
         pc()
         dc()
@@ -308,6 +365,7 @@ def run_bench(args, torch, paa) -> dict:
                                   for c in layers])
 
     def loop_ms(fn, n=50):
+        prewarm(torch, fn, 0.1)
         for _ in range(5):
             fn()
         torch.cuda.synchronize()
@@ -332,6 +390,18 @@ def run_bench(args, torch, paa) -> dict:
              "eager_gbs": round(sdb / (eager_ms * 1e-3) / 1e9, 1), "graph_gbs": round(sdb / (graph_ms * 1e-3) / 1e9, 1)}
     _log(f"{sw.name} x {GRAPH_LAYERS}: eager {eager_ms * 1e3:.1f} us/step, graph replay {graph_ms * 1e3:.1f} us/step")
     del layers, graph
+
+    # ---- chunked prefill over a paged cache, with the chunk appended ----
+    cc = ChunkedCase(torch, paa, WORKLOADS[CHUNKED], args.seed)
+    phases.start(f"chunked prefill {CHUNKED}")
+    med, mean = timed(torch, cc, 20, 3)
+    c_tf = chunked_flops(cc.w, cc.a["ctx_lens"]) / (mean * 1e-3) / 1e12
+    chunked = {"workload": CHUNKED, "ms": round(mean, 4), "ms_median": round(med, 4), "value": round(c_tf, 2),
+               "unit": "TFLOP/s", "algorithmic_gflop": round(chunked_flops(cc.w, cc.a["ctx_lens"]) / 1e9, 3),
+               "algorithmic_mb": round(chunked_bytes(cc.w, cc.a["ctx_lens"]) / 1e6, 3),
+               "roofline": roofline("mfma", c_tf, PEAK_BF16_TFLOPS, "TFLOP/s", read_traffic(CHUNKED))}
+    _log(f"{CHUNKED}: {mean:.4f} ms, {c_tf:.1f} TFLOP/s")
+    del cc
 
     more = []
     if not args.no_more:
@@ -359,6 +429,7 @@ def run_bench(args, torch, paa) -> dict:
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "prewarm_s": PREWARM_S,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -380,6 +451,7 @@ def run_bench(args, torch, paa) -> dict:
                    "algorithmic_gb": round(db / 1e9, 5), "roofline": dec_roof,
                    "cold_ms": round(cold_ms, 5), "cold_value": round(db / (cold_ms * 1e-3) / 1e9, 2)},
         "prefill_more": more,
+        "chunked_prefill": chunked,
         "decode_graph": small,
         "cpu_baseline": base,
         "phases": phases.names,
@@ -401,6 +473,7 @@ def run_pmc_pass(args, torch, paa) -> dict:
     cases = [DecodeCase(torch, paa, WORKLOADS[args.decode_workload], args.seed),
              PrefillCase(torch, paa, WORKLOADS[args.prefill_workload], args.seed)]
     cases += [PrefillCase(torch, paa, WORKLOADS[n], args.seed) for n in PREFILL_MORE]
+    cases.append(ChunkedCase(torch, paa, WORKLOADS[CHUNKED], args.seed))
     for c in cases:
         phases.start(c.w.name)
         for _ in range(PMC_CALLS):

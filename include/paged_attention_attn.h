@@ -91,6 +91,50 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                  int d, int causal, float scale, hipStream_t stream);
 
 /*
+ * paged_prefill — chunked prefill over a paged KV cache, appending the chunk.
+ * A batch of sequences each brings a chunk of new tokens; sequence s already
+ * holds ctx_lens[s] tokens in the paged cache ("Fast Attention Kernels and
+ * Operator Fusion", section "Paged Attention Kernels").  In one launch the
+ * chunk's keys and values are appended to the cache at positions ctx_lens[s],
+ * ctx_lens[s] + 1, ... (the append operation listed in "Kernel Fusion and
+ * Custom Kernels", section "4. FlashInfer"; the KV-cache update fused into the
+ * attention pass, as in the fusion list of "Fast Attention Kernels and
+ * Operator Fusion") and chunk query i, at position ctx_lens[s] + i, attends
+ * over positions 0 .. ctx_lens[s] + i of its sequence (the causal mask aligned
+ * at the end: a one-token chunk is a decode step, a chunk without context is
+ * causal prefill).
+ *
+ *   q           [T, H, d] bf16 — the chunks' queries, back to back: sequence s
+ *               owns rows q_start[s] .. q_start[s+1]-1
+ *   k_new       [T, Hkv, d] bf16 — the same tokens' keys
+ *   v_new       [T, Hkv, d] bf16 — the same tokens' values
+ *   k_cache     [num_pages, page_size, Hkv, d] bf16 — read (context) and written (append)
+ *   v_cache     [num_pages, page_size, Hkv, d] bf16 — read (context) and written (append)
+ *   block_table [num_seqs, max_pages_per_seq] int32 — physical page ids; must
+ *               already cover positions up to ctx_lens[s] + chunk length - 1
+ *   ctx_lens    [num_seqs] int32 — tokens already cached per sequence
+ *   q_start     [num_seqs + 1] int32 — chunk row offsets (nondecreasing, q_start[0] = 0)
+ *   o           [T, H, d] bf16 (written)
+ *   lse         [T, H] fp32 (written; may be NULL)
+ *   max_q_len   host upper bound on every chunk length (sizes the grid)
+ * page_size must be 16, d 64 or 128, scale finite and positive,
+ * max_pages_per_seq and num_pages at least 1.  num_seqs == 0 or max_q_len == 0
+ * is a valid empty call (pointers may be NULL).  The caller keeps its own
+ * lengths: after the call sequence s holds ctx_lens[s] + chunk length tokens.
+ * Device-side rules (the length arrays and the table are never read on the
+ * host): chunk lengths are at most max_q_len (rows beyond are neither computed
+ * nor appended) and ctx_lens[s] + chunk length <= max_pages_per_seq *
+ * page_size; a page id outside [0, num_pages) is clamped for reading (the
+ * result is then unspecified) and is never written; pages one sequence
+ * appends to must not be read by another in the same call.  No workspace, no
+ * atomics: the result is deterministic.  Arithmetic as attn_fwd.
+ */
+int paged_prefill(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                  const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_start, void* o, float* lse,
+                  int num_seqs, int H, int Hkv, int d, int page_size, int max_pages_per_seq, int num_pages,
+                  int max_q_len, float scale, hipStream_t stream);
+
+/*
  * paged_attn_decode_workspace_size — bytes of device workspace that
  * paged_attn_decode needs for these shapes (0 on invalid shapes).  It is
  * about (P + num_seqs) * H * (d + 1) * 4 bytes, where P <= 32768 / H is the

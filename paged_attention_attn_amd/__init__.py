@@ -1,4 +1,4 @@
-"""Exact attention forward and paged-KV decode on AMD Instinct MI355X (gfx950).
+"""Exact attention forward, chunked prefill and decode over a paged KV cache on AMD Instinct MI355X (gfx950).
 
 The kernels are hand-written HIP in ``csrc/`` behind the C ABI declared in
 ``include/paged_attention_attn.h``; this package is the thin Python binding
@@ -16,4 +16,5 @@ from ._binding import (  # noqa: F401
     lib,
     paged_attn_decode,
     paged_attn_decode_workspace_size,
+    paged_prefill,
 )

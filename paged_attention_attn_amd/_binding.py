@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_decode_workspace_size.restype = sz
         L.paged_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
         L.paged_attn_decode.restype = i
+        L.paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+        L.paged_prefill.restype = i
         L.paged_attn_decode_graph_create.argtypes = [ctypes.POINTER(DecodeCall), i, vp, ctypes.POINTER(ctypes.c_void_p)]
         L.paged_attn_decode_graph_create.restype = i
         L.paged_attn_decode_graph_launch.argtypes = [vp, vp]
@@ -144,6 +146,50 @@ def attn_fwd_window(q, k, v, window: int, n_global: int = 0, scale: float | None
 def attn_fwd_f32(q, k, v, causal: bool, scale: float | None = None, out=None, lse=None):
     """fp32 attention forward with the same shapes as :func:`attn_fwd`."""
     return _prefill(lib().attn_fwd_f32, torch.float32, q, k, v, causal, scale, out, lse)
+
+
+def paged_prefill(q, k_new, v_new, k_cache, v_cache, block_table, ctx_lens, q_start, max_q_len: int | None = None,
+                  scale: float | None = None, num_pages=None, out=None, lse=None):
+    """Chunked prefill over a paged cache, appending the chunk (C: paged_prefill).
+
+    q [T, H, d], k_new / v_new [T, Hkv, d] bf16 hold the chunks back to back (sequence s owns rows
+    q_start[s] .. q_start[s+1]-1); k_cache / v_cache [num_pages, 16, Hkv, d] bf16 are updated in place;
+    block_table [S, max_pages], ctx_lens [S], q_start [S + 1] int32 on the same device.  max_q_len
+    bounds every chunk length (default T, known without reading the device).  Returns (O, LSE).
+    """
+    _require(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _require(k_new, "k_new", torch.bfloat16, 3, dev)
+    _require(v_new, "v_new", torch.bfloat16, 3, dev)
+    _require(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _require(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _require(block_table, "block_table", torch.int32, 2, dev)
+    _require(ctx_lens, "ctx_lens", torch.int32, 1, dev)
+    _require(q_start, "q_start", torch.int32, 1, dev)
+    T, H, d = q.shape
+    P, page_size, Hkv, dk = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or dk != d:
+        raise ValueError("k_cache and v_cache must both be [num_pages, page_size, Hkv, d]")
+    if tuple(k_new.shape) != (T, Hkv, d) or tuple(v_new.shape) != (T, Hkv, d):
+        raise ValueError("k_new and v_new must be [T, Hkv, d] with T and d of q and Hkv of the caches")
+    S = ctx_lens.shape[0]
+    if block_table.shape[0] != S or q_start.shape[0] != S + 1:
+        raise ValueError("block_table needs one row and q_start S + 1 entries for the S sequences of ctx_lens")
+    if max_q_len is None:
+        max_q_len = T
+    if num_pages is None:
+        num_pages = P
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out, "out", torch.bfloat16, 3, dev)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, 2, dev)
+    if scale is None:
+        scale = d ** -0.5
+    _check(lib().paged_prefill(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                               _ptr(ctx_lens), _ptr(q_start), _ptr(out), _ptr(lse), S, H, Hkv, d, page_size,
+                               block_table.shape[1], int(num_pages), int(max_q_len), float(scale), _stream(dev)))
+    return out, lse
 
 
 def paged_attn_decode_workspace_size(num_seqs: int, H: int, d: int, page_size: int, max_pages_per_seq: int) -> int:

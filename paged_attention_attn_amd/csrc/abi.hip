@@ -157,6 +157,32 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, c
 
 // ---- the decode step as a replayable hipGraph ----
 
+int paged_prefill(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                  const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_start, void* o, float* lse,
+                  int num_seqs, int H, int Hkv, int d, int page_size, int max_pages_per_seq, int num_pages,
+                  int max_q_len, float scale, hipStream_t stream) {
+  if (num_seqs < 0 || max_q_len < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || max_pages_per_seq < 1 || num_pages < 1)
+    return ATTN_ERR_INVALID_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  if (page_size != 16) return ATTN_ERR_UNSUPPORTED_PAGE_SIZE;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_SCALE;
+  if (num_seqs == 0 || max_q_len == 0) return ATTN_OK;
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !block_table || !ctx_lens || !q_start || !o)
+    return ATTN_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(o, 16) || !aligned(lse, 4) || !aligned(block_table, 4) ||
+      !aligned(ctx_lens, 4) || !aligned(q_start, 4))
+    return ATTN_ERR_MISALIGNED;
+  // positions (context + chunk) are ints on the device; the grid is one dimension
+  if ((long long)max_pages_per_seq * page_size > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
+  if (elems(num_pages, page_size, Hkv, d) < 0 || elems(num_seqs, max_pages_per_seq, 1, 1) < 0)
+    return ATTN_ERR_TOO_LARGE;
+  if ((long long)num_seqs * H * ((max_q_len + 31) / 32) > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
+  return launch_status(paa::paged_prefill_bf16(q, k_new, v_new, k_cache, v_cache, block_table, ctx_lens, q_start, o,
+                                               lse, num_seqs, H, Hkv, d, max_pages_per_seq, num_pages, max_q_len,
+                                               scale, stream));
+}
+
 namespace {
 struct DecodeGraph {
   hipGraph_t graph;

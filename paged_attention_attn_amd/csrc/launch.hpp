@@ -8,6 +8,11 @@
 namespace paa {
 
 // window <= 0 (or >= N) means the plain causal mask when causal is set
+// Chunked prefill over a paged KV cache, appending the chunk (see paged_prefill in the C header).
+hipError_t paged_prefill_bf16(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const int* block_table, const int* ctx_lens, const int* q_start, void* o, float* lse,
+                              int num_seqs, int H, int Hkv, int d, int max_pages, int num_pages, int max_q_len,
+                              float scale, hipStream_t stream);
 hipError_t prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
                         int N, int d, bool causal, int window, int n_global, float scale, hipStream_t stream);
 

@@ -119,6 +119,16 @@ struct PrefillArgs {
   int window;        // sliding window width (kMaskWindow only)
   int n_global;      // leading keys visible to every later query (kMaskWindow only)
   int mirror;        // 1 when the whole grid is resident at once: pair heavy and light units (see below)
+  // chunked prefill over a paged cache (kMaskPaged only): q, o [T, H, d] and k, v (the chunk's new
+  // keys and values) [T, Hkv, d] hold the sequences' chunks back to back, sequence s owning rows
+  // q_start[s] .. q_start[s+1]-1; its first ctx_lens[s] positions are in the caches
+  // [num_pages, 16, Hkv, d], where the chunk is appended
+  const int* bt;
+  const int* ctx_lens;
+  const int* q_start;
+  uint16_t* kc;
+  uint16_t* vc;
+  int max_pages, num_pages;
 };
 
 // WAVES waves per workgroup, RB blocks of 32 query rows per wave, STAGES-deep K and V rings in LDS.
@@ -133,9 +143,11 @@ struct PrefillCfg {
   static constexpr int kInFlightAfter = (STAGES - 2) * 2 * kBlocksPerWave;
 };
 
-// Masks: none, causal (key j visible to query i iff j <= i), or causal with a sliding window and
-// global tokens (additionally i - j < window or j < n_global).
-enum : int { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2 };
+// Masks: none, causal (key j visible to query i iff j <= i), causal with a sliding window and
+// global tokens (additionally i - j < window or j < n_global), or a chunk of new tokens over a paged
+// cache (chunk query i at position ctx + i sees positions 0 .. ctx + i).
+enum : int { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2, kMaskPaged = 3 };
+constexpr int kPageTokens = 16;  // tokens per cache page (the only page size the library accepts)
 
 template <int D, int MASK, int HPW, int WAVES, int RB, int STAGES>
 __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_kernel(
@@ -144,6 +156,8 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   using C = PrefillCfg<D, WAVES, RB, STAGES>;
   constexpr bool CAUSAL = MASK != kMaskNone;
   constexpr bool WINDOW = MASK == kMaskWindow;
+  constexpr bool PAGED = MASK == kMaskPaged;
+  static_assert(!PAGED || STAGES == 2, "the paged page-id prefetch assumes two stages");
   constexpr int kWaveRows = C::kRowsPerWave;
   constexpr int kRowBlocks = WAVES / HPW;              // waves per head in a workgroup
   constexpr int kTileRows = kRowBlocks * kWaveRows;    // query rows per head in a workgroup
@@ -207,17 +221,35 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   const int q0_tile = qt * kTileRows;
   const int q0 = q0_tile + (wave % kRowBlocks) * kWaveRows;  // first row of this wave; block rb starts at q0 + 32rb
 
+  // Geometry of this unit: n_q query rows, n_k keys, query row i at key position qoff + i.  The
+  // rows of Q / O / LSE and of K / V are q_stride / kv_stride elements apart.
   const size_t N = a.N;
-  const uint16_t* qh = a.q + ((size_t)b * a.H + head) * N * D;
-  const uint16_t* kh = a.k + ((size_t)b * a.Hkv + g) * N * D;
-  const uint16_t* vh = a.v + ((size_t)b * a.Hkv + g) * N * D;
+  int n_q = a.N, n_k = a.N, qoff = 0;
+  size_t q_base, kv_base, q_stride = D, kv_stride = D;
+  if constexpr (PAGED) {
+    const int lo = a.q_start[b];
+    n_q = a.q_start[b + 1] - lo;
+    qoff = max(a.ctx_lens[b], 0);
+    n_k = qoff + n_q;
+    if (q0_tile >= n_q) return;  // the whole workgroup: this sequence's chunk is shorter
+    q_base = (size_t)lo * a.H * D + (size_t)head * D;
+    q_stride = (size_t)a.H * D;
+    kv_base = (size_t)lo * a.Hkv * D + (size_t)g * D;  // chunk row 0 of k / v
+    kv_stride = (size_t)a.Hkv * D;
+  } else {
+    q_base = ((size_t)b * a.H + head) * N * D;
+    kv_base = ((size_t)b * a.Hkv + g) * N * D;
+  }
+  const uint16_t* qh = a.q + q_base;
+  const uint16_t* kh = a.k + kv_base;
+  const uint16_t* vh = a.v + kv_base;
 
   // ---- key tiles ----
   // The workgroup visits key tiles [0, n_glob) and then [j_win, n_tiles) in order; iteration t
   // is tile tile_of(t).  Without a window every tile up to the causal limit is visited.  With one,
   // the tiles between the global tokens and the left edge of the workgroup's lowest row's window
   // hold no visible key and are never loaded.  This wave computes iterations [0, n_act).
-  const int kv_end = CAUSAL ? min(a.N, q0_tile + kTileRows) : a.N;
+  const int kv_end = CAUSAL ? min(n_k, qoff + q0_tile + kTileRows) : n_k;
   const int n_tiles = (kv_end + kBc - 1) / kBc;
   int n_glob = 0, j_win = 0;
   if constexpr (WINDOW) {
@@ -226,29 +258,56 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   }
   const int n_iter = n_glob + (n_tiles - j_win);
   auto tile_of = [&](int t) __attribute__((always_inline)) { return t < n_glob ? t : j_win + (t - n_glob); };
-  const int last_tile = CAUSAL ? min(n_tiles - 1, (q0 + kWaveRows - 1) / kBc) : n_tiles - 1;
+  const int last_tile = CAUSAL ? min(n_tiles - 1, (qoff + q0 + kWaveRows - 1) / kBc) : n_tiles - 1;
   const int n_act = last_tile < n_glob ? last_tile + 1 : n_glob + max(0, last_tile - j_win + 1);
 
   // ---- direct global -> LDS load of one tile of K or V; this wave fetches kBlocksPerWave 1 KB blocks ----
-  auto dma = [&](const uint16_t* src, int j, PAA_LDS char* dst) __attribute__((always_inline)) {
+  // Paged: the rows this wave fetches lie in one cache page (kWavePage of the tile's four), whose id
+  // `page` the caller looked up; positions before qoff come from the cache, the rest from the chunk.
+  const int wave_page = (wave * C::kBlocksPerWave * T::kRowsPerBlock) / kPageTokens;
+  auto dma_src = [&](const uint16_t* src, uint16_t* cache, int key, int page, int c) __attribute__((always_inline))
+      -> const uint16_t* {
+    if constexpr (PAGED) {
+      if (key < qoff) return cache + (((size_t)page * kPageTokens + key % kPageTokens) * a.Hkv + g) * D + c * 8;
+      return src + (size_t)(key - qoff) * kv_stride + c * 8;
+    } else {
+      return src + (size_t)key * D + c * 8;
+    }
+  };
+  auto dma = [&](const uint16_t* src, uint16_t* cache, int j, int page, PAA_LDS char* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::kBlocksPerWave; ++i) {
       const int blk = wave * C::kBlocksPerWave + i;
       const int r = blk * T::kRowsPerBlock + lane / T::kCpr;  // tile row written by this lane
       const int c = (lane % T::kCpr) ^ swz<D>(r);             // data chunk stored at this lane's position
-      const int key = min(j * kBc + r, a.N - 1);  // rows past the end repeat a valid row; they are masked
-      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)key * D + c * 8), (PAA_LDS void*)(dst + blk * 1024),
+      const int key = min(j * kBc + r, n_k - 1);  // rows past the end repeat a valid row; they are masked
+      __builtin_amdgcn_global_load_lds((const void*)dma_src(src, cache, key, page, c), (PAA_LDS void*)(dst + blk * 1024),
                                        16, 0, 0);
+    }
+  };
+  // cache page holding this wave's rows of tile j (0 when not paged); an id outside the pool is
+  // clamped into it, so no access leaves the pool (such a table gives unspecified results)
+  auto page_of = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (PAGED) {
+      const int blk = min((j * kBc) / kPageTokens + wave_page, a.max_pages - 1);
+      return min(max(a.bt[(size_t)b * a.max_pages + blk], 0), a.num_pages - 1);
+    } else {
+      return 0;
     }
   };
 
   // prologue loads: K_0 .. K_{STAGES-1} and V_0 .. V_{STAGES-2}
   auto prologue = [&](auto i_tag, int j) __attribute__((always_inline)) {
-    dma(kh, j, kst(i_tag));
-    if (decltype(i_tag)::value + 1 < STAGES) dma(vh, j, vst(i_tag));
+    const int page = page_of(j);
+    dma(kh, a.kc, j, page, kst(i_tag));
+    if (decltype(i_tag)::value + 1 < STAGES) dma(vh, a.vc, j, page, vst(i_tag));
   };
   auto prologue_t = [&](auto i_tag, int t) __attribute__((always_inline)) { prologue(i_tag, tile_of(t)); };
   for_stages<0, STAGES>(prologue_t, 0, n_iter);
+  // page ids for the first refills (K of iteration STAGES, V of iteration STAGES - 1), then one
+  // iteration ahead of use inside the loop
+  int page_k = page_of(tile_of(min(STAGES, n_iter - 1)));
+  int page_v = page_of(tile_of(min(STAGES - 1, n_iter - 1)));
 
   // ---- Q fragments (B operand of S^T = K Q^T): row q0 + 32rb + l32, d = 16t + 8*half + 0..7 ----
   u32x4_t qf[RB][kKSteps];
@@ -257,8 +316,8 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
     const int row = q0 + 32 * rb + l32;
 #pragma unroll
     for (int t = 0; t < kKSteps; ++t) {
-      if (row < a.N)
-        qf[rb][t] = *(const u32x4_t*)(qh + (size_t)row * D + 16 * t + 8 * half);
+      if (row < n_q)
+        qf[rb][t] = *(const u32x4_t*)(qh + (size_t)row * q_stride + 16 * t + 8 * half);
       else
         qf[rb][t] = u32x4_t{0, 0, 0, 0};
     }
@@ -312,14 +371,14 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   // the reference maximum moves.  Returns -reference * scale_log2, the exponent shift of this tile.
   auto softmax_prep = [&](int j, int rb, f32x16_t (&s)[2]) __attribute__((always_inline)) -> float {
     const int k0 = j * kBc;
-    const int rq0 = q0 + 32 * rb;
+    const int rq0 = qoff + q0 + 32 * rb;  // key position of the block's first query row
     // mask: causal keys after the row, keys past the end of the sequence and, with a window, keys
     // left of the row's window that are not global tokens
     const bool need_window = WINDOW && (k0 <= rq0 + 31 - a.window) && (k0 + kBc - 1 >= a.n_global);
-    const bool need_mask = (CAUSAL && (k0 + kBc - 1 > rq0)) || (k0 + kBc > a.N) || need_window;
+    const bool need_mask = (CAUSAL && (k0 + kBc - 1 > rq0)) || (k0 + kBc > n_k) || need_window;
     if (need_mask) {
       const int row = rq0 + l32;
-      const int lim = CAUSAL ? min(row, a.N - 1) : a.N - 1;
+      const int lim = CAUSAL ? min(row, n_k - 1) : n_k - 1;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -402,8 +461,12 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
     using Prev = std::integral_constant<int, ST + STAGES - 1>;
     // near the end the loads repeat the last tile (cached, and never read): issuing them every time
     // keeps the count of loads in flight fixed, so the waits below stay exact
-    dma(kh, tile_of(min(j + STAGES, n_iter - 1)), kst(st_tag));
-    dma(vh, tile_of(min(j + STAGES - 1, n_iter - 1)), vst(Prev{}));
+    dma(kh, a.kc, tile_of(min(j + STAGES, n_iter - 1)), page_k, kst(st_tag));
+    dma(vh, a.vc, tile_of(min(j + STAGES - 1, n_iter - 1)), page_v, vst(Prev{}));
+    if constexpr (PAGED) {  // next iteration's ids; the load retires with this tile's DMA wait
+      page_v = page_k;
+      page_k = page_of(tile_of(min(j + STAGES + 1, n_iter - 1)));
+    }
     if (j < n_act) {
       float neg_ms[RB];
 #pragma unroll
@@ -435,8 +498,8 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
     const int row = q0 + 32 * rb + l32;
     const float l_tot = l_run[rb] + swap_halves(l_run[rb], half);
     const float inv_l = 1.f / l_tot;
-    if (row < a.N) {
-      uint16_t* orow = a.o + (((size_t)b * a.H + head) * N + row) * D;
+    if (row < n_q) {
+      uint16_t* orow = a.o + q_base + (size_t)row * q_stride;
 #pragma unroll
       for (int db = 0; db < kDBlocks; ++db) {
 #pragma unroll
@@ -447,8 +510,35 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
           *(u32x2_t*)(orow + d0) = w;
         }
       }
-      if (a.lse != nullptr && half == 0)
-        a.lse[((size_t)b * a.H + head) * N + row] = a.scale * m_run[rb] + __logf(l_tot);
+      if (a.lse != nullptr && half == 0) {
+        const size_t li = PAGED ? q_base / D + (size_t)row * a.H : ((size_t)b * a.H + head) * N + row;
+        a.lse[li] = a.scale * m_run[rb] + __logf(l_tot);
+      }
+    }
+  }
+
+  // ---- paged: append this workgroup's chunk rows (its KV head) to the caches ----
+  // One workgroup per (sequence, KV head, query tile) does it, the one holding the head group's
+  // first query heads, so every new row is written exactly once.  No workgroup of this launch
+  // reads cache positions at or past ctx (they read the chunk from k / v), so the writes race
+  // with nothing.  A row whose page id is outside the pool is not written.
+  if constexpr (PAGED) {
+    if (hsub == 0) {
+      constexpr int kChunks = D / 8;  // 16-byte pieces per row
+      const int rows = min(kTileRows, n_q - q0_tile);
+      for (int e = tid; e < 2 * rows * kChunks; e += 64 * WAVES) {
+        const bool is_v = e >= rows * kChunks;
+        const int f = is_v ? e - rows * kChunks : e;
+        const int i = q0_tile + f / kChunks;  // chunk row
+        const int c = f % kChunks;
+        const int pos = qoff + i;
+        const int blk = pos / kPageTokens;
+        const int page = blk < a.max_pages ? a.bt[(size_t)b * a.max_pages + blk] : -1;
+        if (page < 0 || page >= a.num_pages) continue;
+        const u32x4_t val = *(const u32x4_t*)((is_v ? vh : kh) + (size_t)i * kv_stride + c * 8);
+        uint16_t* dst = (is_v ? a.vc : a.kc) + (((size_t)page * kPageTokens + pos % kPageTokens) * a.Hkv + g) * D + c * 8;
+        *(u32x4_t*)dst = val;
+      }
     }
   }
 }
@@ -832,7 +922,45 @@ hipError_t dispatch_hpw(const PrefillArgs& a, hipStream_t stream) {
   return dispatch_group<D, MASK, 4>(a, stream);
 }
 
+// Chunked prefill over a paged cache: the lock-step kernel (eight waves when the grid is large).
+template <int D>
+hipError_t dispatch_paged(const PrefillArgs& a, hipStream_t stream) {
+  const int group = a.H / a.Hkv;
+  const int hpw = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+  const long long rows8 = (8 / hpw) * 32;
+  const long long units8 = (long long)a.B * a.Hkv * (group / hpw) * ((a.N + rows8 - 1) / rows8);
+  if (units8 >= 1024) return dispatch_group<D, kMaskPaged, 8>(a, stream);
+  return dispatch_group<D, kMaskPaged, 4>(a, stream);
+}
+
 }  // namespace
+
+hipError_t paged_prefill_bf16(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const int* block_table, const int* ctx_lens, const int* q_start, void* o, float* lse,
+                              int num_seqs, int H, int Hkv, int d, int max_pages, int num_pages, int max_q_len,
+                              float scale, hipStream_t stream) {
+  PrefillArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k_new;
+  a.v = (const uint16_t*)v_new;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.B = num_seqs;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.N = max_q_len;  // sizes the grid; each sequence's own chunk length is read on the device
+  a.scale = scale;
+  a.scale_log2 = scale * kLog2e;
+  a.rescale_raw = kRescaleLog2 / a.scale_log2;
+  a.bt = block_table;
+  a.ctx_lens = ctx_lens;
+  a.q_start = q_start;
+  a.kc = (uint16_t*)k_cache;
+  a.vc = (uint16_t*)v_cache;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  return d == 64 ? dispatch_paged<64>(a, stream) : dispatch_paged<128>(a, stream);
+}
 
 hipError_t prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
                         int N, int d, bool causal, int window, int n_global, float scale, hipStream_t stream) {

@@ -25,7 +25,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = paa.declared_functions()
-    assert set(names) == {"attn_fwd", "attn_fwd_f32", "attn_fwd_window", "paged_attn_decode_workspace_size",
+    assert set(names) == {"attn_fwd", "attn_fwd_f32", "attn_fwd_window", "paged_attn_decode_workspace_size", "paged_prefill",
                           "paged_attn_decode", "paged_attn_decode_graph_create", "paged_attn_decode_graph_launch",
                           "paged_attn_decode_graph_destroy", "attn_status_string"}
     for n in names:
@@ -139,3 +139,33 @@ def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         _binding.lib()
+
+
+def test_paged_prefill_validation(L):
+    """Argument errors of the chunked paged prefill come back on the host; empty calls are valid."""
+    # q, k_new, v_new, k_cache, v_cache, block_table, ctx_lens, q_start, o, lse
+    ptrs = [P] * 8 + [P, None]
+
+    def call(num_seqs=2, H=8, Hkv=2, d=128, page_size=16, max_pages=4, num_pages=10, max_q_len=33, scale=0.1,
+             p=None):
+        return L.paged_prefill(*(p or ptrs), num_seqs, H, Hkv, d, page_size, max_pages, num_pages, max_q_len, scale,
+                               None)
+
+    assert call(H=6, Hkv=4) == SHAPE
+    assert call(num_seqs=-1) == SHAPE
+    assert call(max_q_len=-1) == SHAPE
+    assert call(max_pages=0) == SHAPE
+    assert call(num_pages=0) == SHAPE
+    assert call(d=96) == HEAD_DIM
+    assert call(page_size=32) == PAGE
+    assert call(scale=float("nan")) == SCALE
+    assert call(p=[None] * 10, num_seqs=0) == ATTN_OK  # empty batch
+    assert call(p=[None] * 10, max_q_len=0) == ATTN_OK  # empty chunks
+    for i in range(9):  # every pointer but lse is required
+        p = list(ptrs)
+        p[i] = None
+        assert call(p=p) == NULL, i
+    p = list(ptrs)
+    p[3] = ctypes.c_void_p(0x10008)  # k_cache not 16-byte aligned
+    assert call(p=p) == ALIGN
+    assert call(max_pages=1 << 28) == LARGE

@@ -1,0 +1,158 @@
+"""GPU parity of paged_prefill (chunked prefill over a paged cache with the chunk appended), through
+the C ABI, against the float64 oracle; the caches after the call are compared bit for bit."""
+
+from __future__ import annotations
+
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_attention_attn_amd as paa
+from gpu_util import assert_close_bf16, assert_close_lse, dev_bf16, dev_i32, host_f64
+from workloads import BF16_NAN, WORKLOADS, ChunkedPrefillWorkload, chunked_prefill_inputs, f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _announce(msg):
+    print(f"[gpu] {msg}", file=sys.stderr, flush=True)
+
+
+def _to_dev(a):
+    return {"q": dev_bf16(a["q"]), "k_new": dev_bf16(a["k_new"]), "v_new": dev_bf16(a["v_new"]),
+            "k_cache": dev_bf16(a["k_cache"]), "v_cache": dev_bf16(a["v_cache"]),
+            "block_table": dev_i32(a["block_table"]), "ctx_lens": dev_i32(a["ctx_lens"]),
+            "q_start": dev_i32(a["q_start"])}
+
+
+def _run(a, max_q_len=None):
+    t = _to_dev(a)
+    H = a["q"].shape[1]
+    lse = torch.empty((a["q"].shape[0], H), dtype=torch.float32, device="cuda:0")
+    o, _ = paa.paged_prefill(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["block_table"],
+                             t["ctx_lens"], t["q_start"], max_q_len=max_q_len, scale=a["scale"], lse=lse)
+    torch.cuda.synchronize()
+    kc = t["k_cache"].view(torch.int16).cpu().numpy().view(np.uint16)
+    vc = t["v_cache"].view(torch.int16).cpu().numpy().view(np.uint16)
+    return host_f64(o), lse.cpu().numpy().astype(np.float64), kc, vc
+
+
+def _oracle(a, seqs=None):
+    return oracle.paged_prefill(a["q"], a["k_new"], a["v_new"], a["k_cache"], a["v_cache"], a["block_table"],
+                                a["ctx_lens"], a["q_start"], a["scale"], seqs=seqs)
+
+
+def _check_all(a, max_q_len=None):
+    o, lse, kc, vc = _run(a, max_q_len)
+    ro, rl, rkc, rvc = _oracle(a)
+    assert_close_bf16(o, ro)
+    assert_close_lse(lse, rl)
+    # the append is a copy of bf16 bit patterns: the caches must match exactly (NaN slots included)
+    assert np.array_equal(kc, rkc) and np.array_equal(vc, rvc)
+
+
+# (ctx lengths, chunk lengths) per case: contexts and chunks on and off page (16) and tile (64)
+# boundaries, empty contexts, one-token chunks, an empty chunk, a chunk longer than one query tile
+SMALL = [
+    ([0, 5, 16, 64, 100], [37, 1, 16, 64, 129], 8, 2, 128),
+    ([33, 0, 200], [200, 0, 7], 4, 4, 64),
+    ([511, 17], [1, 300], 16, 4, 128),
+    ([1000], [65], 6, 2, 64),
+    ([0, 0, 0, 0], [128, 127, 129, 1], 2, 1, 128),
+]
+
+
+@pytest.mark.parametrize("ctxs,qlens,H,Hkv,d", SMALL)
+def test_paged_prefill_small_full_parity(ctxs, qlens, H, Hkv, d):
+    w = ChunkedPrefillWorkload("small", len(ctxs), H, Hkv, d, 0, 0, 1, num_pages=400)
+    _announce(f"paged prefill ctx{ctxs} q{qlens} H{H} Hkv{Hkv} d{d}")
+    a = chunked_prefill_inputs(w, seed=sum(ctxs) + d, ctx_lens=ctxs, q_lens=qlens)
+    _check_all(a)
+
+
+def test_paged_prefill_loose_max_q_len():
+    """A max_q_len far above every chunk only adds workgroups that leave at once."""
+    w = ChunkedPrefillWorkload("loose", 3, 8, 2, 128, 0, 0, 1, num_pages=200)
+    _announce("paged prefill, loose max_q_len")
+    a = chunked_prefill_inputs(w, seed=5, ctx_lens=[40, 0, 300], q_lens=[9, 70, 3])
+    _check_all(a, max_q_len=1000)
+
+
+def test_paged_prefill_block_table_worked_example():
+    """The pages' table [17, 4, 29, 8]: 40 cached tokens and a chunk of 9 land at block 29 slots 8-15 and block 8
+    slot 0 (positions 40..48), and the chunk's outputs match the oracle."""
+    with open(os.path.join(GOLDEN, "block_table_example.json")) as f:
+        ex = json.load(f)
+    table = ex["physical_blocks"]
+    w = ChunkedPrefillWorkload("golden", 1, 8, 2, 128, 0, 0, 1, num_pages=32)
+    _announce("paged prefill, golden block table")
+    full = chunked_prefill_inputs(w, seed=9, ctx_lens=[0], q_lens=[49])  # 49 tokens' q, k, v
+    ctx = 40
+    k_pool = np.full_like(full["k_cache"], BF16_NAN)
+    v_pool = k_pool.copy()
+    for t in range(ctx):  # the context, placed through the table by hand
+        k_pool[table[t // 16], t % 16] = full["k_new"][t]
+        v_pool[table[t // 16], t % 16] = full["v_new"][t]
+    b = {"q": full["q"][ctx:], "k_new": full["k_new"][ctx:], "v_new": full["v_new"][ctx:], "k_cache": k_pool,
+         "v_cache": v_pool, "block_table": np.array([table], dtype=np.int32),
+         "ctx_lens": np.array([ctx], dtype=np.int32), "q_start": np.array([0, 9], dtype=np.int32), "scale": w.scale}
+    o, lse, kc, vc = _run(b)
+    assert np.array_equal(kc[29, 8:16], full["k_new"][40:48]) and np.array_equal(kc[8, 0], full["k_new"][48])
+    assert np.array_equal(vc[29, 8:16], full["v_new"][40:48]) and np.array_equal(vc[8, 0], full["v_new"][48])
+    ro, rl, rkc, _ = _oracle(b)
+    assert np.array_equal(kc, rkc)
+    assert_close_bf16(o, ro)
+    assert_close_lse(lse, rl)
+
+
+def test_chunks_then_decode_match_one_pass():
+    """A sequence prefilled in three chunks through the cache, then a decode step, against the oracle over the
+    whole sequence: every chunk's rows equal causal prefill rows, and decode sees the appended cache."""
+    H, Hkv, d, n = 8, 2, 128, 300
+    w = ChunkedPrefillWorkload("chunks", 1, H, Hkv, d, 0, 0, 1, num_pages=64)
+    a = chunked_prefill_inputs(w, seed=11, ctx_lens=[0], q_lens=[n])
+    t = _to_dev(a)
+    _announce("three chunks, then decode")
+    bounds = [0, 70, 71, 300]
+    outs = []
+    for c0, c1 in zip(bounds[:-1], bounds[1:]):
+        o, _ = paa.paged_prefill(t["q"][c0:c1], t["k_new"][c0:c1], t["v_new"][c0:c1], t["k_cache"], t["v_cache"],
+                                 t["block_table"], dev_i32(np.array([c0])), dev_i32(np.array([0, c1 - c0])),
+                                 scale=a["scale"])
+        outs.append(o)
+    torch.cuda.synchronize()
+    ro, rl, rkc, rvc = _oracle(a)  # one chunk of n with no context
+    got = np.concatenate([host_f64(o) for o in outs])
+    assert_close_bf16(got, ro)
+    kc = t["k_cache"].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(kc, rkc)
+    # decode one more query over the n cached tokens
+    qb = f32_to_bf16_bits(np.random.default_rng(12).standard_normal((1, H, d)).astype(np.float32))
+    od, _ = paa.paged_attn_decode(dev_bf16(qb), t["k_cache"], t["v_cache"], t["block_table"],
+                                  dev_i32(np.array([n])), a["scale"])
+    torch.cuda.synchronize()
+    rod, _ = oracle.paged_decode(qb, rkc, rvc, a["block_table"], [n], a["scale"])
+    assert_close_bf16(host_f64(od), rod)
+
+
+def test_paged_prefill_full_workload_sampled():
+    """16 sequences, contexts U[0, 4096], chunks of 512, H=32, Hkv=8, d=128: three sequences against the
+    oracle in full, every output finite, the whole cache against the oracle's append."""
+    w = WORKLOADS["chunked_prefill_s16h32kv8d128_ctx0to4096_q512"]
+    _announce(w.name)
+    a = chunked_prefill_inputs(w, seed=0)
+    o, lse, kc, vc = _run(a, a["max_q_len"])
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    seqs = [0, int(np.argmax(a["ctx_lens"])), w.num_seqs - 1]
+    ro, rl, rkc, rvc = _oracle(a, seqs=seqs)
+    rows = np.concatenate([np.arange(a["q_start"][s], a["q_start"][s + 1]) for s in seqs])
+    assert_close_bf16(o[rows], ro)
+    assert_close_lse(lse[rows], rl)
+    assert np.array_equal(kc, rkc) and np.array_equal(vc, rvc)

@@ -9,6 +9,8 @@ from .generators import (  # noqa: F401
     WORKLOADS,
     PrefillWorkload,
     DecodeWorkload,
+    ChunkedPrefillWorkload,
+    chunked_prefill_inputs,
     f32_to_bf16_bits,
     bf16_bits_to_f32,
     prefill_inputs,

@@ -90,6 +90,29 @@ class DecodeWorkload:
         return -(-self.L_hi // self.page_size)
 
 
+@dataclass(frozen=True)
+class ChunkedPrefillWorkload:
+    """A batch of sequences, each with ctx tokens cached in pages and a chunk of q_len new tokens."""
+    name: str
+    num_seqs: int
+    H: int
+    Hkv: int
+    d: int
+    ctx_lo: int
+    ctx_hi: int
+    q_len: int
+    page_size: int = 16
+    num_pages: int = 40000
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def max_pages_per_seq(self) -> int:
+        return -(-(self.ctx_hi + self.q_len) // self.page_size)
+
+
 WORKLOADS = {
     w.name: w
     for w in [
@@ -100,6 +123,8 @@ WORKLOADS = {
                         q_mult=4.0, k_outlier_frac=0.01, k_outlier_mult=8.0),
         DecodeWorkload("paged_decode_s64h32kv8d128", 64, 32, 8, 128, 512, 8192, 16, 40000),
         DecodeWorkload("paged_decode_s4h32kv8d128_short", 4, 32, 8, 128, 256, 1024, 16, 512),
+        ChunkedPrefillWorkload("chunked_prefill_s16h32kv8d128_ctx0to4096_q512", 16, 32, 8, 128, 0, 4096, 512,
+                               num_pages=6000),
         PrefillWorkload("window_gqa_b1h32kv8n16384d128_w4096_g64", 1, 32, 8, 16384, 128, causal=True,
                         window=4096, n_global=64),
     ]
@@ -185,3 +210,50 @@ def decode_inputs(w: DecodeWorkload, seed: int = 0, poison: bool = True, seq_len
         v_pool[pages, t % ps] = vv
     return {"q": q, "k_cache": k_pool, "v_cache": v_pool, "block_table": bt,
             "seq_lens": lens, "scale": w.scale, "max_pages_per_seq": max_pages}
+
+
+def chunked_prefill_inputs(w: ChunkedPrefillWorkload, seed: int = 0, poison: bool = True, ctx_lens=None,
+                           q_lens=None):
+    """Chunked-prefill inputs.
+
+    Draw order: context lengths (uniform integers in [ctx_lo, ctx_hi]), one permutation of the
+    ``num_pages`` physical page ids, then per sequence the context K [ctx, Hkv, d] and V, then the
+    chunks' Q [T, H, d], K [T, Hkv, d] and V [T, Hkv, d] (T = the sum of the chunk lengths, each
+    ``q_len`` unless ``q_lens`` is given).  Sequence s takes the next ceil((ctx_s + q_len_s) /
+    page_size) ids of the permutation as its block table (room for the chunk to be appended);
+    unused table entries are -1.  With ``poison`` every slot no context token occupies holds
+    bfloat16 NaN, including the slots the chunk will be appended to.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    S, ps = w.num_seqs, w.page_size
+    drawn = rng.integers(w.ctx_lo, w.ctx_hi, endpoint=True, size=S)
+    ctx = np.asarray(drawn if ctx_lens is None else ctx_lens, dtype=np.int32)
+    ql = np.full(S, w.q_len, dtype=np.int32) if q_lens is None else np.asarray(q_lens, dtype=np.int32)
+    perm = rng.permutation(w.num_pages)
+    need = -(-(ctx.astype(np.int64) + ql) // ps)
+    max_pages = max(1, int(need.max()) if S else 1)
+    if int(need.sum()) > w.num_pages:
+        raise ValueError("page pool too small for the drawn lengths")
+    bt = np.full((S, max_pages), -1, dtype=np.int32)
+    cursor = 0
+    for s in range(S):
+        n = int(need[s])
+        bt[s, :n] = perm[cursor:cursor + n]
+        cursor += n
+    fill = BF16_NAN if poison else np.uint16(0)
+    k_pool = np.full((w.num_pages, ps, w.Hkv, w.d), fill, dtype=np.uint16)
+    v_pool = np.full((w.num_pages, ps, w.Hkv, w.d), fill, dtype=np.uint16)
+    for s in range(S):
+        L = int(ctx[s])
+        kk = f32_to_bf16_bits(rng.standard_normal((L, w.Hkv, w.d), dtype=np.float32))
+        vv = f32_to_bf16_bits(rng.standard_normal((L, w.Hkv, w.d), dtype=np.float32))
+        t = np.arange(L)
+        k_pool[bt[s, t // ps], t % ps] = kk
+        v_pool[bt[s, t // ps], t % ps] = vv
+    T = int(ql.sum())
+    q = f32_to_bf16_bits(rng.standard_normal((T, w.H, w.d), dtype=np.float32))
+    k_new = f32_to_bf16_bits(rng.standard_normal((T, w.Hkv, w.d), dtype=np.float32))
+    v_new = f32_to_bf16_bits(rng.standard_normal((T, w.Hkv, w.d), dtype=np.float32))
+    q_start = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    return {"q": q, "k_new": k_new, "v_new": v_new, "k_cache": k_pool, "v_cache": v_pool, "block_table": bt,
+            "ctx_lens": ctx, "q_start": q_start, "scale": w.scale, "max_q_len": int(ql.max()) if S else 0}
