@@ -21,6 +21,8 @@ here is "parity unpinned".
 
 from .exact import (  # noqa: F401
     attention,
+    attention_fp8,
+    attention_fp8_rows,
     attention_rows,
     attention_window,
     attention_window_rows,
@@ -30,4 +32,5 @@ from .exact import (  # noqa: F401
     paged_prefill,
     softmax_probs,
     bf16_bits_to_f64,
+    e4m3_bits_to_f64,
 )

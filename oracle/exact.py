@@ -326,3 +326,47 @@ def paged_prefill(q, k_new, v_new, k_cache, v_cache, block_table, ctx_lens, q_st
     o = np.concatenate(o) if o else np.zeros((0, H, d))
     lse = np.concatenate(lse) if lse else np.zeros((0, H))
     return o, lse, kc, vc
+
+
+def e4m3_bits_to_f64(x: np.ndarray) -> np.ndarray:
+    """Exact float64 value of OCP FP8 E4M3 (the "fn" variant: no infinities) numbers given as bytes.
+
+    Sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+    subnormals m/8 * 2^-6; the all-ones pattern S.1111.111 is NaN; the largest finite value
+    is 1.75 * 2^8 = 448.
+    """
+    b = np.asarray(x, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = b & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    out = sign * mag
+    return np.where((e == 15) & (m == 7), np.nan, out)
+
+
+def _dequant_fp8(q8, k8, vt8, q_scale, k_scale, v_scale):
+    """Values of the fp8 inputs: Q [B,H,N,d], K [B,Hkv,N,d], V from its transpose [B,Hkv,d,N]."""
+    q = e4m3_bits_to_f64(q8) * float(q_scale)
+    k = e4m3_bits_to_f64(k8) * float(k_scale)
+    v = np.swapaxes(e4m3_bits_to_f64(vt8), -1, -2) * float(v_scale)
+    return q, k, v
+
+
+def attention_fp8(q8, k8, vt8, causal: bool, scale: float, q_scale: float, k_scale: float, v_scale: float):
+    """Exact attention of FP8 inputs with per-tensor scales (the FP8 variant named in "Kernel Fusion and
+    Custom Kernels", section "3. FlashAttention: The Milestone of Fusion", v3).
+
+    q8 [B,H,N,d], k8 [B,Hkv,N,d] and vt8 [B,Hkv,d,N] (V transposed) are e4m3 bytes; the inputs are
+    their values times q_scale, k_scale and v_scale.  The result is :func:`attention` of those values
+    in float64 (any rounding of intermediate values, such as of the probabilities, is the method's
+    approximation, not part of this definition).
+    """
+    q, k, v = _dequant_fp8(q8, k8, vt8, q_scale, k_scale, v_scale)
+    return attention(q, k, v, causal, scale)
+
+
+def attention_fp8_rows(q8, k8, vt8, causal: bool, scale: float, q_scale: float, k_scale: float, v_scale: float,
+                       rows):
+    """O and LSE of selected rows (b, h, i) of :func:`attention_fp8`."""
+    q, k, v = _dequant_fp8(q8, k8, vt8, q_scale, k_scale, v_scale)
+    return attention_rows(q, k, v, causal, scale, rows)

@@ -491,4 +491,60 @@ def pin_chunked_prefill_brute_force_tiny():
                     assert abs(lse[lo + i, h] - (m + math.log(l))) < 1e-12
 
 
+# ------------------------------------------------------------------------------ fp8 pins
+
+def pin_e4m3_decode_matches_torch():
+    """All 256 E4M3 codes decode to torch's float8_e4m3fn values (NaN codes to NaN)."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(oracle.e4m3_bits_to_f64(codes), want, equal_nan=True)
+
+
+def pin_e4m3_decode_closed_forms():
+    """Hand-decoded E4M3 codes: 1, 448 (largest), 2^-6 (smallest normal), 2^-9 and 7 * 2^-9 (subnormals),
+    -2, signed zero and NaN."""
+    codes = np.array([0x38, 0x7E, 0x08, 0x01, 0x07, 0xC0, 0x00, 0x80, 0x7F, 0xFF], dtype=np.uint8)
+    got = oracle.e4m3_bits_to_f64(codes)
+    want = [1.0, 448.0, 2.0 ** -6, 2.0 ** -9, 7 * 2.0 ** -9, -2.0, 0.0, -0.0]
+    assert np.array_equal(got[:8], want) and np.signbit(got[7]) and np.all(np.isnan(got[8:]))
+
+
+def _fp8_case(B, H, Hkv, N, d, seed):
+    from workloads import quantize_e4m3
+    rng = np.random.default_rng(seed)
+    q8, qs = quantize_e4m3(rng.standard_normal((B, H, N, d)))
+    k8, ks = quantize_e4m3(rng.standard_normal((B, Hkv, N, d)))
+    v8, vs = quantize_e4m3(rng.standard_normal((B, Hkv, N, d)))
+    return q8, k8, np.ascontiguousarray(np.swapaxes(v8, -1, -2)), qs, ks, vs
+
+
+def pin_fp8_attention_torch_sdpa():
+    """FP8 attention equals torch's CPU float64 SDPA over the inputs decoded by torch (float8_e4m3fn), scaled, with
+    V taken back from its transpose by torch."""
+    import torch
+    import torch.nn.functional as F
+    for (B, H, Hkv, N, d, causal, seed) in [(1, 4, 2, 16, 16, True, 60), (2, 2, 2, 24, 8, False, 61),
+                                            (1, 6, 3, 33, 16, True, 62)]:
+        q8, k8, vt8, qs, ks, vs = _fp8_case(B, H, Hkv, N, d, seed)
+        o, _ = oracle.attention_fp8(q8, k8, vt8, causal, 0.3, qs, ks, vs)
+
+        def dec(x):
+            return torch.from_numpy(x.copy()).view(torch.float8_e4m3fn).to(torch.float64)
+        ref = F.scaled_dot_product_attention(dec(q8) * qs, dec(k8) * ks, dec(vt8).transpose(-1, -2) * vs,
+                                             is_causal=causal, scale=0.3, enable_gqa=True).numpy()
+        assert np.allclose(o, ref, rtol=0, atol=1e-10)
+
+
+def pin_fp8_scales_enter_linearly():
+    """Doubling q_scale equals doubling the softmax scale; doubling v_scale doubles O and leaves LSE alone."""
+    q8, k8, vt8, qs, ks, vs = _fp8_case(1, 2, 1, 20, 8, 63)
+    o, lse = oracle.attention_fp8(q8, k8, vt8, True, 0.2, qs, ks, vs)
+    o2, lse2 = oracle.attention_fp8(q8, k8, vt8, True, 0.4, qs, ks, vs)
+    o3, lse3 = oracle.attention_fp8(q8, k8, vt8, True, 0.2, 2 * qs, ks, vs)
+    o4, lse4 = oracle.attention_fp8(q8, k8, vt8, True, 0.2, qs, ks, 2 * vs)
+    assert np.allclose(o2, o3, rtol=0, atol=1e-13) and np.allclose(lse2, lse3, rtol=0, atol=1e-13)
+    assert np.allclose(o4, 2 * o, rtol=0, atol=1e-13) and np.array_equal(lse4, lse)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

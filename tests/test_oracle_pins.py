@@ -60,6 +60,18 @@ def _mut_window_not_causal(row_pos, n_keys, window, n_global):
     return ~((np.abs(i - j) < window) | (j < n_global))
 
 
+def _mut_e4m3_bias8(x):
+    b = np.asarray(x, dtype=np.uint8).astype(np.int64)
+    e, m = (b >> 3) & 15, b & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -7, (1.0 + m / 8.0) * np.exp2(e - 8.0))
+    return np.where(b >> 7, -mag, mag)
+
+
+def _mut_dequant_no_transpose(q8, k8, vt8, q_scale, k_scale, v_scale):
+    return (A.e4m3_bits_to_f64(q8) * q_scale, A.e4m3_bits_to_f64(k8) * k_scale,
+            A.e4m3_bits_to_f64(vt8) * v_scale)
+
+
 # Each entry: (helper name in oracle.exact, planted replacement)
 MUTANTS = {
     "gqa_modulo_mapping": ("_kv_head", lambda h, H, Hkv: h % Hkv),
@@ -81,6 +93,8 @@ MUTANTS = {
     "chunk_aligned_at_start": ("_chunk_positions", lambda ctx, n: np.arange(n)),
     "chunk_positions_off_by_one": ("_chunk_positions", lambda ctx, n: ctx + 1 + np.arange(n)),
     "chunk_positions_reversed": ("_chunk_positions", lambda ctx, n: ctx + np.arange(n)[::-1]),
+    "fp8_exponent_bias_8": ("e4m3_bits_to_f64", _mut_e4m3_bias8),
+    "fp8_v_not_transposed": ("_dequant_fp8", _mut_dequant_no_transpose),
 }
 
 

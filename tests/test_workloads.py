@@ -61,3 +61,24 @@ def test_window_visible_pairs_by_counting():
     want = sum(1 for i in range(37) for j in range(i + 1) if i - j < 5 or j < 3)
     assert w.visible_pairs() == want
     assert PrefillWorkload("c", 1, 1, 1, 37, 8, causal=True).visible_pairs() == 37 * 38 // 2
+
+
+def test_e4m3_encoder_matches_torch_rounding():
+    """The input quantizer rounds like torch's float8_e4m3fn cast (nearest, ties to even) within +-448."""
+    import torch
+    from workloads import f32_to_e4m3_bits, quantize_e4m3
+    x = np.random.default_rng(3).standard_normal(50000).astype(np.float32) * 40
+    x[:6] = [0.0, -0.0, 448.0, -448.0, 2.0 ** -9, 3 * 2.0 ** -10]  # zero, extremes, a subnormal, a tie
+    want = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = f32_to_e4m3_bits(x)
+    assert np.array_equal(got[1:], want[1:]) and got[0] == 0
+    q, s = quantize_e4m3(x)
+    assert abs(s * 448.0 - np.abs(x).max()) <= 1e-6 * np.abs(x).max()
+
+
+def test_fp8_workload_layout():
+    from workloads import PrefillWorkload, prefill_inputs
+    w = PrefillWorkload("t", 1, 4, 2, 48, 64, True, dtype="fp8")
+    a = prefill_inputs(w, seed=1)
+    assert a["q8"].shape == (1, 4, 48, 64) and a["k8"].shape == (1, 2, 48, 64) and a["vt8"].shape == (1, 2, 64, 48)
+    assert a["q8"].dtype == np.uint8 and a["vt8"].flags["C_CONTIGUOUS"]

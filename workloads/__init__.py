@@ -12,6 +12,8 @@ from .generators import (  # noqa: F401
     ChunkedPrefillWorkload,
     chunked_prefill_inputs,
     f32_to_bf16_bits,
+    f32_to_e4m3_bits,
+    quantize_e4m3,
     bf16_bits_to_f32,
     prefill_inputs,
     decode_inputs,

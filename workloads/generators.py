@@ -34,6 +34,42 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return r
 
 
+E4M3_MAX = 448.0
+
+
+def _e4m3_table():
+    """Finite non-negative OCP E4M3 values and their codes, ascending (bias 7, 3 mantissa bits,
+    exponent field 0 for subnormals, S.1111.111 reserved for NaN)."""
+    vals, codes = [], []
+    for e in range(16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                continue
+            vals.append(m / 8.0 * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+            codes.append((e << 3) | m)
+    return np.array(vals), np.array(codes, dtype=np.uint8)
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest E4M3 value (ties to the even code), saturating at +-448; returns bytes."""
+    vals, codes = _e4m3_table()
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.clip(np.searchsorted(vals, a), 1, len(vals) - 1)
+    lo = hi - 1
+    d_lo, d_hi = a - vals[lo], vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (codes[hi] % 2 == 0))
+    out = np.where(pick_hi, codes[hi], codes[lo]).astype(np.uint8)
+    return np.where((x < 0) & (out != 0), out | np.uint8(0x80), out).astype(np.uint8)
+
+
+def quantize_e4m3(x: np.ndarray):
+    """Per-tensor scaled E4M3: returns (bytes, scale) with x ~ scale * value(bytes), max |x| at 448."""
+    amax = float(np.abs(x).max()) if x.size else 0.0
+    scale = np.float32(amax / E4M3_MAX if amax > 0 else 1.0)
+    return f32_to_e4m3_bits(np.asarray(x, dtype=np.float64) / float(scale)), float(scale)
+
+
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """float32 value of bfloat16 bit patterns (exact)."""
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
@@ -125,6 +161,9 @@ WORKLOADS = {
         DecodeWorkload("paged_decode_s4h32kv8d128_short", 4, 32, 8, 128, 256, 1024, 16, 512),
         ChunkedPrefillWorkload("chunked_prefill_s16h32kv8d128_ctx0to4096_q512", 16, 32, 8, 128, 0, 4096, 512,
                                num_pages=6000),
+        PrefillWorkload("fp8_causal_gqa_b2h32kv8n4096d128", 2, 32, 8, 4096, 128, causal=True, dtype="fp8"),
+        PrefillWorkload("fp8_causal_gqa_long_b1h32kv8n16384d128", 1, 32, 8, 16384, 128, causal=True, dtype="fp8",
+                        q_mult=4.0, k_outlier_frac=0.01, k_outlier_mult=8.0),
         PrefillWorkload("window_gqa_b1h32kv8n16384d128_w4096_g64", 1, 32, 8, 16384, 128, causal=True,
                         window=4096, n_global=64),
     ]
@@ -154,6 +193,13 @@ def prefill_inputs(w: PrefillWorkload, seed: int = 0):
                 rows = rng.choice(w.N, size=n_out, replace=False)
                 outliers[b, g] = rows
                 k[b, g, rows] *= np.float32(w.k_outlier_mult)
+    if w.dtype == "fp8":
+        # per-tensor scaled E4M3; V is handed over transposed, [B, Hkv, d, N]
+        q8, qs = quantize_e4m3(q)
+        k8, ks = quantize_e4m3(k)
+        v8, vs = quantize_e4m3(v)
+        return {"q8": q8, "k8": k8, "vt8": np.ascontiguousarray(np.swapaxes(v8, -1, -2)), "q_scale": qs,
+                "k_scale": ks, "v_scale": vs, "outliers": outliers, "scale": w.scale}
     if w.dtype == "bf16":
         q, k, v = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
     elif w.dtype != "f32":
