@@ -60,7 +60,7 @@ def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
     d_lo, d_hi = a - vals[lo], vals[hi] - a
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (codes[hi] % 2 == 0))
     out = np.where(pick_hi, codes[hi], codes[lo]).astype(np.uint8)
-    return np.where((x < 0) & (out != 0), out | np.uint8(0x80), out).astype(np.uint8)
+    return np.where(np.signbit(x), out | np.uint8(0x80), out).astype(np.uint8)
 
 
 def quantize_e4m3(x: np.ndarray):
