@@ -42,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "causal prefill attention TFLOP/s + paged decode KV GB/s, % of roofline"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0  # dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
 CSRC = os.path.join(ROOT, "paged_attention_attn_amd", "csrc")
@@ -52,6 +53,7 @@ PMC_CALLS = 3              # calls of each workload in a counter pass
 
 PREFILL_DEFAULT = "causal_b4h16n1024d64"
 SMALL_DECODE = "paged_decode_s4h32kv8d128_short"  # launch-bound: eager calls against graph replays
+FP8_MORE = ("fp8_causal_gqa_b2h32kv8n4096d128", "fp8_causal_gqa_long_b1h32kv8n16384d128")
 CHUNKED = "chunked_prefill_s16h32kv8d128_ctx0to4096_q512"  # chunked prefill over a paged cache, with append
 GRAPH_LAYERS = 32
 PREWARM_S = 0.25  # untimed calls of the step before its W warm-up steps (see prewarm)  # decode calls per step in that comparison, each with its own KV cache
@@ -221,6 +223,22 @@ class DecodeCase:
     def __call__(self):
         self.paa.paged_attn_decode(self.q, self.kc, self.vc, self.bt, self.lens, self.a["scale"],
                                    workspace=self.ws, out=self.o, lse=self.lse)
+
+
+class Fp8Case:
+    def __init__(self, torch, paa, w, seed):
+        from workloads import prefill_inputs
+        self.w = w
+        self.a = a = prefill_inputs(w, seed=seed)
+        self.q, self.k, self.vt = (torch.from_numpy(a[n]).to("cuda:0") for n in ("q8", "k8", "vt8"))
+        self.o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device="cuda:0")
+        self.lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
+        self.paa = paa
+
+    def __call__(self):
+        a = self.a
+        self.paa.attn_fwd_fp8(self.q, self.k, self.vt, self.w.causal, a["scale"], a["q_scale"], a["k_scale"],
+                              a["v_scale"], out=self.o, lse=self.lse)
 
 
 class ChunkedCase:
@@ -416,6 +434,19 @@ def run_bench(args, torch, paa) -> dict:
             del c
             _log(f"{name}: {mean:.4f} ms, {tf:.1f} TFLOP/s")
 
+    fp8 = []
+    if not args.no_more:
+        for name in FP8_MORE:
+            c = Fp8Case(torch, paa, WORKLOADS[name], args.seed)
+            phases.start(f"prefill {name}")
+            med, mean = timed(torch, c, 20, 3)
+            tf = prefill_flops(c.w) / (mean * 1e-3) / 1e12
+            fp8.append({"workload": name, "ms": round(mean, 4), "ms_median": round(med, 4), "value": round(tf, 2),
+                        "unit": "TFLOP/s", "dtype": "fp8 e4m3 in, bf16 out",
+                        "roofline": roofline("mfma", tf, PEAK_FP8_TFLOPS, "TFLOP/s", read_traffic(name))})
+            del c
+            _log(f"{name}: {mean:.4f} ms, {tf:.1f} TFLOP/s")
+
     base = None
     if not args.no_cpu_baseline:
         base = cpu_baseline(pc, dc)
@@ -452,6 +483,7 @@ def run_bench(args, torch, paa) -> dict:
                    "cold_ms": round(cold_ms, 5), "cold_value": round(db / (cold_ms * 1e-3) / 1e9, 2)},
         "prefill_more": more,
         "chunked_prefill": chunked,
+        "fp8_prefill": fp8,
         "decode_graph": small,
         "cpu_baseline": base,
         "phases": phases.names,
@@ -474,6 +506,7 @@ def run_pmc_pass(args, torch, paa) -> dict:
              PrefillCase(torch, paa, WORKLOADS[args.prefill_workload], args.seed)]
     cases += [PrefillCase(torch, paa, WORKLOADS[n], args.seed) for n in PREFILL_MORE]
     cases.append(ChunkedCase(torch, paa, WORKLOADS[CHUNKED], args.seed))
+    cases += [Fp8Case(torch, paa, WORKLOADS[n], args.seed) for n in FP8_MORE]
     for c in cases:
         phases.start(c.w.name)
         for _ in range(PMC_CALLS):

@@ -91,6 +91,28 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                  int d, int causal, float scale, hipStream_t stream);
 
 /*
+ * attn_fwd_fp8 — attn_fwd with FP8 operands: Q, K and V in OCP E4M3 (1 byte
+ * each; bias 7, no infinities, largest 448) with per-tensor scales, the FP8
+ * path of FlashAttention v3 ("Kernel Fusion and Custom Kernels", section "3.
+ * FlashAttention: The Milestone of Fusion").  The inputs are q_scale * Q,
+ * k_scale * K and v_scale * V; both products use the 8-bit matrix
+ * instructions, with fp32 accumulation and softmax.  The probabilities are
+ * rounded to E4M3 before the product with V (relative error up to 2^-4 each),
+ * so O agrees with exact attention of the scaled inputs to within
+ * 2^-4 * max|v_scale * V| per element; LSE is as precise as attn_fwd's.
+ *
+ *   q    [B, H, N, d] E4M3
+ *   k    [B, Hkv, N, d] E4M3
+ *   v_t  [B, Hkv, d, N] E4M3 — V transposed (keys contiguous)
+ *   o    [B, H, N, d] bf16 (written)
+ *   lse  [B, H, N] fp32 (written; may be NULL)
+ * N must be a multiple of 16; scale and the three tensor scales finite and
+ * positive; other rules as attn_fwd.
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* v_t, void* o, float* lse, int B, int H, int Hkv, int N,
+                 int d, int causal, float scale, float q_scale, float k_scale, float v_scale, hipStream_t stream);
+
+/*
  * paged_prefill — chunked prefill over a paged KV cache, appending the chunk.
  * A batch of sequences each brings a chunk of new tokens; sequence s already
  * holds ctx_lens[s] tokens in the paged cache ("Fast Attention Kernels and

@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     PagedDecodeGraph,
     attn_fwd,
     attn_fwd_f32,
+    attn_fwd_fp8,
     attn_fwd_window,
     attn_status_string,
     declared_functions,

@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_decode_workspace_size.restype = sz
         L.paged_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
         L.paged_attn_decode.restype = i
+        L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, f, vp]
+        L.attn_fwd_fp8.restype = i
         L.paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
         L.paged_prefill.restype = i
         L.paged_attn_decode_graph_create.argtypes = [ctypes.POINTER(DecodeCall), i, vp, ctypes.POINTER(ctypes.c_void_p)]
@@ -141,6 +143,32 @@ def attn_fwd_window(q, k, v, window: int, n_global: int = 0, scale: float | None
     """bf16 causal attention where key j is visible to query i iff j <= i and (i - j < window or j < n_global)."""
     return _prefill(lib().attn_fwd_window, torch.bfloat16, q, k, v, True, scale, out, lse,
                     mask_args=(window, n_global))
+
+
+def attn_fwd_fp8(q, k, v_t, causal: bool, scale: float | None = None, q_scale: float = 1.0, k_scale: float = 1.0,
+                 v_scale: float = 1.0, out=None, lse=None):
+    """FP8 attention (C: attn_fwd_fp8).  q [B,H,N,d], k [B,Hkv,N,d] and v_t [B,Hkv,d,N] (V transposed) hold
+    E4M3 bytes (torch.uint8 or torch.float8_e4m3fn); the inputs are their values times the scales.
+    Returns (O bf16 [B,H,N,d], LSE)."""
+    fp8 = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
+    for t, name, nd in ((q, "q", 4), (k, "k", 4), (v_t, "v_t", 4)):
+        if not isinstance(t, torch.Tensor) or t.dtype not in fp8:
+            raise TypeError(f"{name} must hold E4M3 bytes (torch.uint8 or torch.float8_e4m3fn)")
+        _require(t, name, t.dtype, nd, q.device)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v_t.shape) != (B, Hkv, d, N):
+        raise ValueError("k must be [B, Hkv, N, d] and v_t [B, Hkv, d, N]")
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    _require(out, "out", torch.bfloat16, 4, q.device)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, 3, q.device)
+    if scale is None:
+        scale = d ** -0.5
+    _check(lib().attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v_t), _ptr(out), _ptr(lse), B, H, Hkv, N, d, int(bool(causal)),
+                              float(scale), float(q_scale), float(k_scale), float(v_scale), _stream(q.device)))
+    return out, lse
 
 
 def attn_fwd_f32(q, k, v, causal: bool, scale: float | None = None, out=None, lse=None):

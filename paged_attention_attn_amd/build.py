@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "libpaged_attention_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["abi.hip", "prefill_bf16.hip", "prefill_f32.hip", "paged_decode.hip"]
+SOURCES = ["abi.hip", "prefill_bf16.hip", "prefill_fp8.hip", "prefill_f32.hip", "paged_decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

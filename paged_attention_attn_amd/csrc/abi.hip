@@ -74,6 +74,17 @@ int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float*
   return launch_status(paa::prefill_bf16(q, k, v, o, lse, B, H, Hkv, N, d, true, window, n_global, scale, stream));
 }
 
+int attn_fwd_fp8(const void* q, const void* k, const void* v_t, void* o, float* lse, int B, int H, int Hkv, int N,
+                 int d, int causal, float scale, float q_scale, float k_scale, float v_scale, hipStream_t stream) {
+  const int rc = check_prefill(q, k, v_t, o, lse, B, H, Hkv, N, d, scale);
+  if (rc != ATTN_OK) return rc;
+  if (!scale_ok(q_scale) || !scale_ok(k_scale) || !scale_ok(v_scale)) return ATTN_ERR_INVALID_SCALE;
+  if (N % 16 != 0) return ATTN_ERR_INVALID_SHAPE;  // rows of the transposed V start 16-byte aligned
+  if (B == 0 || N == 0) return ATTN_OK;
+  return launch_status(
+      paa::prefill_fp8(q, k, v_t, o, lse, B, H, Hkv, N, d, causal != 0, scale, q_scale, k_scale, v_scale, stream));
+}
+
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Hkv, int N,
                  int d, int causal, float scale, hipStream_t stream) {
   const int rc = check_prefill(q, k, v, o, lse, B, H, Hkv, N, d, scale);

@@ -13,6 +13,10 @@ hipError_t paged_prefill_bf16(const void* q, const void* k_new, const void* v_ne
                               const int* block_table, const int* ctx_lens, const int* q_start, void* o, float* lse,
                               int num_seqs, int H, int Hkv, int d, int max_pages, int num_pages, int max_q_len,
                               float scale, hipStream_t stream);
+// FP8 (e4m3) Q, K and transposed V with per-tensor scales, bf16 O (see attn_fwd_fp8 in the C header).
+hipError_t prefill_fp8(const void* q, const void* k, const void* vt, void* o, float* lse, int B, int H, int Hkv,
+                       int N, int d, bool causal, float scale, float q_scale, float k_scale, float v_scale,
+                       hipStream_t stream);
 hipError_t prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
                         int N, int d, bool causal, int window, int n_global, float scale, hipStream_t stream);
 

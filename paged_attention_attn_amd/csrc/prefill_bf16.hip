@@ -48,13 +48,11 @@
 
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "tile_pipeline.hpp"
 
 namespace paa {
 
 namespace {
-
-constexpr int kBc = 64;               // keys per tile
-constexpr float kRescaleLog2 = 8.0f;  // lazy rescale threshold (probabilities stay <= 256)
 
 template <int D>
 struct TileLayout {
@@ -64,34 +62,6 @@ struct TileLayout {
   static constexpr int kRowsPerBlock = 64 / kCpr;          // rows of one wave-wide 16 B/lane load
   static constexpr int kBlocks = kBc / kRowsPerBlock;      // such loads per tile
 };
-
-// vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
-// expcnt 6:4, lgkmcnt 11:8).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier for the tile loop.  The only LDS writes in the loop are direct global->LDS
-// loads, whose completion is tracked by vmcnt and awaited explicitly (wait_vmcnt) just before; a
-// workgroup-scope fence would make the compiler wait for every one of them (vmcnt(0)), which
-// would drain the load ring.  The wavefront-scope fences keep the compiler from moving memory
-// accesses across the barrier; lgkmcnt(0) retires this wave's own LDS reads first.
-__device__ __forceinline__ void tile_barrier() {
-  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0) only
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-template <int I, int S, typename F>
-__device__ __forceinline__ void for_stages(F& f, int j, int n) {
-  if (j + I < n) {
-    f(std::integral_constant<int, I>{}, j + I);
-    if constexpr (I + 1 < S) for_stages<I + 1, S>(f, j, n);
-  }
-}
 
 // Chunk position swizzle of tile row r (a function of r % 16 only).
 template <int D>

@@ -25,7 +25,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = paa.declared_functions()
-    assert set(names) == {"attn_fwd", "attn_fwd_f32", "attn_fwd_window", "paged_attn_decode_workspace_size", "paged_prefill",
+    assert set(names) == {"attn_fwd", "attn_fwd_f32", "attn_fwd_fp8", "attn_fwd_window", "paged_attn_decode_workspace_size", "paged_prefill",
                           "paged_attn_decode", "paged_attn_decode_graph_create", "paged_attn_decode_graph_launch",
                           "paged_attn_decode_graph_destroy", "attn_status_string"}
     for n in names:
@@ -169,3 +169,15 @@ def test_paged_prefill_validation(L):
     p[3] = ctypes.c_void_p(0x10008)  # k_cache not 16-byte aligned
     assert call(p=p) == ALIGN
     assert call(max_pages=1 << 28) == LARGE
+
+
+def test_fp8_validation(L):
+    """FP8 prefill: the bf16 rules, plus N a multiple of 16 and three finite positive tensor scales."""
+    base = (P, P, P, P, None, 1, 8, 2, 64, 128, 1, 0.1)
+    assert L.attn_fwd_fp8(P, P, P, P, None, 1, 8, 2, 40, 128, 1, 0.1, 1.0, 1.0, 1.0, None) == SHAPE  # N % 16
+    assert L.attn_fwd_fp8(P, P, P, P, None, 1, 8, 3, 64, 128, 1, 0.1, 1.0, 1.0, 1.0, None) == SHAPE
+    assert L.attn_fwd_fp8(P, P, P, P, None, 1, 8, 2, 64, 96, 1, 0.1, 1.0, 1.0, 1.0, None) == HEAD_DIM
+    for bad in ((0.0, 1.0, 1.0), (1.0, -1.0, 1.0), (1.0, 1.0, float("inf"))):
+        assert L.attn_fwd_fp8(*base, *bad, None) == SCALE
+    assert L.attn_fwd_fp8(None, P, P, P, None, 1, 8, 2, 64, 128, 1, 0.1, 1.0, 1.0, 1.0, None) == NULL
+    assert L.attn_fwd_fp8(None, None, None, None, None, 0, 8, 2, 64, 128, 1, 0.1, 1.0, 1.0, 1.0, None) == ATTN_OK
