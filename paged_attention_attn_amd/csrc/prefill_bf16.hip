@@ -522,29 +522,38 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
 // phase, and a workgroup barrier ends each period.  Stage s of the LDS ring holds K_s and
 // V_{s-1}; both groups read it in periods 2s (A) and 2s + 1 (B), and its refill with stage
 // s + STAGES goes out at the start of period 2s + 2.
-template <int D, int MASK, int HPW, int STAGES>
+//
+// Split-key mode (KSPLIT): both groups take the same query rows, group A the even key tiles and
+// group B the odd ones, so a short causal sequence's longest rows walk half as many tiles per
+// wave.  Stage s then holds K of tiles 2s and 2s + 1 and V of tiles 2s - 2 and 2s - 1 (group g's
+// in slot g of the stage); at the end group B hands its (reference max, partial sum,
+// accumulator) to group A through LDS, and group A merges them with the rescaling identity of
+// the online softmax and writes the rows.
+template <int D, int MASK, int HPW, int STAGES, bool KSPLIT = false>
 __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   constexpr int WAVES = 8;
   using T = TileLayout<D>;
   constexpr bool CAUSAL = MASK != kMaskNone;
   constexpr bool WINDOW = MASK == kMaskWindow;
-  constexpr int kRowBlocks = WAVES / HPW;              // waves per head in a workgroup
+  static_assert(!(KSPLIT && (WINDOW || MASK == kMaskPaged)), "split keys: plain and causal masks only");
+  constexpr int kRowWaves = KSPLIT ? WAVES / 2 : WAVES;  // waves holding distinct query rows
+  constexpr int kRowBlocks = kRowWaves / HPW;          // waves per head in a workgroup
   constexpr int kTileRows = kRowBlocks * 32;           // query rows per head in a workgroup
   constexpr int kKSteps = D / 16;
   constexpr int kDBlocks = D / 32;
-  constexpr int kBlocksPerWave = T::kBlocks / WAVES;   // 1 KB loads per wave per K or V tile
-  constexpr int kLoadsPerStage = 2 * kBlocksPerWave;
-  static_assert(T::kBlocks % WAVES == 0, "tile rows must split evenly over the waves");
+  constexpr int kSlots = KSPLIT ? 2 : 1;               // K (and V) tiles per stage
+  constexpr int kLoadsPerStage = 2 * kSlots * T::kBlocks / WAVES;
+  static_assert((2 * kSlots * T::kBlocks) % WAVES == 0, "tile rows must split evenly over the waves");
   static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
 
-  __shared__ __attribute__((aligned(1024))) char k_st0[T::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char k_st1[T::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char k_st2[T::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char k_st3[T::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char v_st0[T::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char v_st1[T::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char v_st2[T::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char v_st3[T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_st0[kSlots * T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_st1[kSlots * T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_st2[kSlots * T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_st3[kSlots * T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_st0[kSlots * T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_st1[kSlots * T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_st2[kSlots * T::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_st3[kSlots * T::kTileBytes];
   auto kst = [&](auto i_tag) __attribute__((always_inline)) -> PAA_LDS char* {
     constexpr int i = decltype(i_tag)::value % STAGES;
     if constexpr (i == 0) return (PAA_LDS char*)k_st0;
@@ -583,9 +592,10 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   const int g = rest % a.Hkv;
   const int b = rest / a.Hkv;
 
-  const int head = g * group + hsub * HPW + wave / kRowBlocks;
+  const int wrow = KSPLIT ? wave % kRowWaves : wave;  // this wave's row block among the workgroup's
+  const int head = g * group + hsub * HPW + wrow / kRowBlocks;
   const int q0_tile = qt * kTileRows;
-  const int q0 = q0_tile + (wave % kRowBlocks) * 32;
+  const int q0 = q0_tile + (wrow % kRowBlocks) * 32;
 
   const size_t N = a.N;
   const uint16_t* qh = a.q + ((size_t)b * a.H + head) * N * D;
@@ -603,25 +613,45 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   const int n_iter = n_glob + (n_tiles - j_win);
   auto tile_of = [&](int t) __attribute__((always_inline)) { return t < n_glob ? t : j_win + (t - n_glob); };
   const int last_tile = CAUSAL ? min(n_tiles - 1, (q0 + 31) / kBc) : n_tiles - 1;
-  const int n_act = last_tile < n_glob ? last_tile + 1 : n_glob + max(0, last_tile - j_win + 1);
+  // iteration i of this wave works on key tile key_tile(i) (tile_of(i), or 2i + grp when split);
+  // it computes iterations [0, n_act) of the n_loop the workgroup runs
+  int n_act, n_loop;
+  if constexpr (KSPLIT) {
+    n_act = last_tile >= grp ? (last_tile - grp) / 2 + 1 : 0;
+    n_loop = (n_iter + 1) / 2;
+  } else {
+    n_act = last_tile < n_glob ? last_tile + 1 : n_glob + max(0, last_tile - j_win + 1);
+    n_loop = n_iter;
+  }
+  auto key_tile = [&](int i) __attribute__((always_inline)) { return KSPLIT ? 2 * i + grp : tile_of(i); };
 
-  auto dma = [&](const uint16_t* src, int j, PAA_LDS char* dst) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < kBlocksPerWave; ++i) {
-      const int blk = wave * kBlocksPerWave + i;
-      const int r = blk * T::kRowsPerBlock + lane / T::kCpr;
-      const int c = (lane % T::kCpr) ^ swz<D>(r);
-      const int key = min(j * kBc + r, a.N - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)key * D + c * 8), (PAA_LDS void*)(dst + blk * 1024),
-                                       16, 0, 0);
-    }
+  // One 1 KB block of a stage: block u of the list [K slot 0, (K slot 1,) V slot 0, (V slot 1)];
+  // slot t of a stage holds tile j + t.
+  auto load_block = [&](int u, int jk, int jv, PAA_LDS char* kdst, PAA_LDS char* vdst) __attribute__((always_inline)) {
+    const bool is_v = u >= kSlots * T::kBlocks;
+    const int w = is_v ? u - kSlots * T::kBlocks : u;
+    const int slot = w / T::kBlocks, blk = w % T::kBlocks;
+    const int r = blk * T::kRowsPerBlock + lane / T::kCpr;
+    const int c = (lane % T::kCpr) ^ swz<D>(r);
+    const int key = min(((is_v ? jv : jk) + slot) * kBc + r, a.N - 1);  // rows past the end are masked
+    const uint16_t* src = is_v ? vh : kh;
+    PAA_LDS char* dst = (is_v ? vdst : kdst) + slot * T::kTileBytes + blk * 1024;
+    __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)key * D + c * 8), (PAA_LDS void*)dst, 16, 0, 0);
   };
   // stage s: K of iteration s and V of iteration s - 1; iterations past the end repeat the last
   // one (the buffer is free and never read), so every stage issues the same number of loads
   auto issue_stage = [&](auto s_tag, int s) __attribute__((always_inline)) {
     using Prev = std::integral_constant<int, decltype(s_tag)::value + STAGES - 1>;
-    dma(kh, tile_of(min(s, n_iter - 1)), kst(s_tag));
-    dma(vh, tile_of(min(max(s - 1, 0), n_iter - 1)), vst(Prev{}));
+    int jk, jv;
+    if constexpr (KSPLIT) {  // pairs of tiles; the last pair may reach one tile past the end (masked)
+      jk = 2 * min(s, n_loop - 1);
+      jv = 2 * min(max(s - 1, 0), n_loop - 1);
+    } else {
+      jk = tile_of(min(s, n_iter - 1));
+      jv = tile_of(min(max(s - 1, 0), n_iter - 1));
+    }
+#pragma unroll
+    for (int i = 0; i < kLoadsPerStage; ++i) load_block(wave * kLoadsPerStage + i, jk, jv, kst(s_tag), vst(Prev{}));
   };
 
   // ---- Q fragments first (their loads then retire before the ring's) ----
@@ -636,8 +666,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
         qf[t] = u32x4_t{0, 0, 0, 0};
     }
   }
-  // prologue: stage 0 (K_0 only), then stages 1 .. STAGES-1
-  dma(kh, tile_of(0), kst(std::integral_constant<int, 0>{}));
+  // prologue: stages 0 .. STAGES-1 (stage 0's V half repeats tile 0 into a free buffer)
+  issue_stage(std::integral_constant<int, 0>{}, 0);
   auto prologue = [&](auto s_tag, int s) __attribute__((always_inline)) { issue_stage(s_tag, s); };
   for_stages<1, STAGES>(prologue, 0, STAGES);
 
@@ -666,8 +696,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   auto m_phase = [&](auto u_tag, int i) __attribute__((always_inline)) {
     using U = decltype(u_tag);
     using Prev = std::integral_constant<int, U::value + STAGES - 1>;
-    const PAA_LDS char* kt = kst(U{});
-    const PAA_LDS char* vt = vst(Prev{});
+    const PAA_LDS char* kt = kst(U{}) + (KSPLIT ? grp * T::kTileBytes : 0);
+    const PAA_LDS char* vt = vst(Prev{}) + (KSPLIT ? grp * T::kTileBytes : 0);
     // each block keeps its LDS reads a few ahead of its MFMAs (not all hoisted to the top, which
     // would take more registers than the wave has)
     if (i < n_act) {
@@ -710,7 +740,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   // VALU phase of iteration i: mask, row max, lazy rescale, exponentials, row sum, bf16 P
   auto v_phase = [&](int i) __attribute__((always_inline)) {
     if (i < 0 || i >= n_act) return;
-    const int k0 = tile_of(i) * kBc;
+    const int k0 = key_tile(i) * kBc;
     const bool need_window = WINDOW && (k0 <= q0 + 31 - a.window) && (k0 + kBc - 1 >= a.n_global);
     const bool need_mask = (CAUSAL && (k0 + kBc - 1 > q0)) || (k0 + kBc > a.N) || need_window;
     if (need_mask) {
@@ -777,13 +807,49 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
       wait_vmcnt<(STAGES - 2) * kLoadsPerStage>();  // stage i + 1 has landed
       tile_barrier();
     };
-    for (int i0 = 0; i0 <= n_iter; i0 += STAGES) for_stages<0, STAGES>(period_pair, i0, n_iter + 1);
+    for (int i0 = 0; i0 <= n_loop; i0 += STAGES) for_stages<0, STAGES>(period_pair, i0, n_loop + 1);
   };
   if (grp == 0)
     run(std::integral_constant<int, 0>{});
   else
     run(std::integral_constant<int, 1>{});
   wait_vmcnt<0>();  // no load may still be writing this workgroup's LDS when it exits
+
+  if constexpr (KSPLIT) {
+    // group B's partial state to group A, lane for lane (the same rows, the same accumulator
+    // layout), through a stage buffer that is idle now: m, l, then the accumulators
+    // one stage array per row block: K stages 0 and 1, then V stages 0 and 1
+    constexpr int kPerWave = (2 + 16 * kDBlocks) * 64;  // floats
+    static_assert(kPerWave * 4 <= kSlots * T::kTileBytes, "a row block's exchange fits in one stage array");
+    static_assert(kRowWaves == 4 && STAGES >= 2, "four row blocks, four stage arrays");
+    __syncthreads();  // every wave's loads have landed and every tile read is done
+    PAA_LDS char* xbase = wrow == 0 ? (PAA_LDS char*)k_st0
+                        : wrow == 1 ? (PAA_LDS char*)k_st1
+                        : wrow == 2 ? (PAA_LDS char*)v_st0 : (PAA_LDS char*)v_st1;
+    PAA_LDS float* xch = (PAA_LDS float*)xbase;
+    if (grp == 1) {
+      xch[lane] = m_run;
+      xch[64 + lane] = l_run;
+#pragma unroll
+      for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xch[128 + (db * 16 + e) * 64 + lane] = acc[db][e];
+    }
+    __syncthreads();
+    if (grp == 1) return;  // group A writes the rows
+    const float mb = xch[lane];
+    const float lb = xch[64 + lane];
+    const float m_new = fmaxf(m_run, mb);
+    // a group that saw no visible key has m = -inf and contributes nothing
+    const float fa = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * a.scale_log2);
+    const float fb = mb == -INFINITY ? 0.f : fast_exp2((mb - m_new) * a.scale_log2);
+    m_run = m_new;
+    l_run = l_run * fa + lb * fb;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[db][e] = acc[db][e] * fa + xch[128 + (db * 16 + e) * 64 + lane] * fb;
+  }
 
   // ---- epilogue: O = acc / l, LSE = scale * m + ln(l) ----
   const int row = q0 + l32;
@@ -838,27 +904,27 @@ hipError_t launch_prefill(const PrefillArgs& base, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int MASK, int HPW, int STAGES>
+template <int D, int MASK, int HPW, int STAGES, bool KSPLIT = false>
 hipError_t launch_prefill_pp(const PrefillArgs& base, hipStream_t stream) {
   PrefillArgs a = base;
-  constexpr int kTileRows = (8 / HPW) * 32;
+  constexpr int kTileRows = ((KSPLIT ? 4 : 8) / HPW) * 32;
   a.n_qtiles = (a.N + kTileRows - 1) / kTileRows;
   a.units_per_qt = a.B * a.Hkv * ((a.H / a.Hkv) / HPW);
   const long long units = (long long)a.n_qtiles * a.units_per_qt;
   if (units > 0x7fffffffLL) return hipErrorInvalidValue;
-  const auto kernel = prefill_pp_kernel<D, MASK, HPW, STAGES>;
+  const auto kernel = prefill_pp_kernel<D, MASK, HPW, STAGES, KSPLIT>;
   a.mirror = MASK != kMaskNone && units <= resident_workgroups(kernel, 512) ? 1 : 0;
   hipLaunchKernelGGL(kernel, dim3((unsigned)units), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, int MASK>
+template <int D, int MASK, bool KSPLIT = false>
 hipError_t dispatch_pp(const PrefillArgs& a, hipStream_t stream) {
   constexpr int kStages = 2;
   const int group = a.H / a.Hkv;
-  if (group % 4 == 0) return launch_prefill_pp<D, MASK, 4, kStages>(a, stream);
-  if (group % 2 == 0) return launch_prefill_pp<D, MASK, 2, kStages>(a, stream);
-  return launch_prefill_pp<D, MASK, 1, kStages>(a, stream);
+  if (group % 4 == 0) return launch_prefill_pp<D, MASK, 4, kStages, KSPLIT>(a, stream);
+  if (group % 2 == 0) return launch_prefill_pp<D, MASK, 2, kStages, KSPLIT>(a, stream);
+  return launch_prefill_pp<D, MASK, 1, kStages, KSPLIT>(a, stream);
 }
 
 template <int D, int MASK, int WAVES>
@@ -889,6 +955,11 @@ hipError_t dispatch_hpw(const PrefillArgs& a, hipStream_t stream) {
     if constexpr (D == 128) return dispatch_pp<D, MASK>(a, stream);
     else return dispatch_group<D, MASK, 8>(a, stream);
   }
+  // Small grids (short sequences) at d = 128: the critical path is the longest causal rows, and
+  // splitting their key tiles over the two groups of a ping-pong workgroup halves the tiles each
+  // wave walks (8 heads x 2048 tokens: 47 -> 39 us).  At d = 64 the split workgroups lose to
+  // two four-wave workgroups per CU (causal 16 heads x 1024 tokens: 26.5 against 24.4 us).
+  if constexpr (D == 128 && (MASK == kMaskNone || MASK == kMaskCausal)) return dispatch_pp<D, MASK, true>(a, stream);
   return dispatch_group<D, MASK, 4>(a, stream);
 }
 

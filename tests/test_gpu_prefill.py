@@ -38,6 +38,10 @@ SMALL = [
     (1, 4, 4, 200, 128, True), (1, 6, 2, 131, 64, True),   # group 3 -> one head per workgroup
     (1, 8, 1, 190, 128, True),                               # group 8 -> two head subgroups
     (1, 2, 1, 1, 64, True), (1, 2, 2, 17, 128, False), (1, 2, 2, 64, 64, True), (3, 2, 1, 129, 128, True),
+    # d = 128 small grids take the split-key kernel: one key tile (group B idle), an even and an odd
+    # number of key tiles, a row block ending exactly on a tile edge, no mask
+    (1, 4, 4, 1, 128, True), (1, 4, 1, 63, 128, True), (2, 4, 2, 128, 128, True), (1, 4, 2, 192, 128, True),
+    (1, 8, 2, 511, 128, False), (1, 3, 3, 96, 128, True),
 ]
 
 
