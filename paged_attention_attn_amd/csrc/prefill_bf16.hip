@@ -347,15 +347,19 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
     const bool need_window = WINDOW && (k0 <= rq0 + 31 - a.window) && (k0 + kBc - 1 >= a.n_global);
     const bool need_mask = (CAUSAL && (k0 + kBc - 1 > rq0)) || (k0 + kBc > n_k) || need_window;
     if (need_mask) {
+      // element i of block mb holds key k0 + 4 half + c, c = 32 mb + 8 (i / 4) + i % 4 (a constant);
+      // compare c with per-lane bounds relative to k0 + 4 half
       const int row = rq0 + l32;
-      const int lim = CAUSAL ? min(row, n_k - 1) : n_k - 1;
+      const int base = k0 + 4 * half;
+      const int lim = (CAUSAL ? min(row, n_k - 1) : n_k - 1) - base;
+      const int win = row - a.window - base, glob = a.n_global - base;  // hidden if c <= win and c >= glob
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = k0 + 32 * mb + 8 * (i / 4) + 4 * half + (i % 4);
-          const bool out_of_window = WINDOW && row - key >= a.window && key >= a.n_global;
-          if (key > lim || out_of_window) s[mb][i] = -INFINITY;
+          const int c = 32 * mb + 8 * (i / 4) + (i % 4);
+          const bool out_of_window = WINDOW && c <= win && c >= glob;
+          if (c > lim || out_of_window) s[mb][i] = -INFINITY;
         }
     }
     float tmax = -INFINITY;
@@ -743,16 +747,18 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     const int k0 = key_tile(i) * kBc;
     const bool need_window = WINDOW && (k0 <= q0 + 31 - a.window) && (k0 + kBc - 1 >= a.n_global);
     const bool need_mask = (CAUSAL && (k0 + kBc - 1 > q0)) || (k0 + kBc > a.N) || need_window;
-    if (need_mask) {
+    if (need_mask) {  // as in the lock-step kernel: constant offsets against per-lane bounds
       const int row = q0 + l32;
-      const int lim = CAUSAL ? min(row, a.N - 1) : a.N - 1;
+      const int base = k0 + 4 * half;
+      const int lim = (CAUSAL ? min(row, a.N - 1) : a.N - 1) - base;
+      const int win = row - a.window - base, glob = a.n_global - base;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = k0 + 32 * mb + 8 * (e / 4) + 4 * half + (e % 4);
-          const bool out_of_window = WINDOW && row - key >= a.window && key >= a.n_global;
-          if (key > lim || out_of_window) s[mb][e] = -INFINITY;
+          const int c = 32 * mb + 8 * (e / 4) + (e % 4);
+          const bool out_of_window = WINDOW && c <= win && c >= glob;
+          if (c > lim || out_of_window) s[mb][e] = -INFINITY;
         }
     }
     float tmax = -INFINITY;

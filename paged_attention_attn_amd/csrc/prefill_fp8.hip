@@ -255,16 +255,13 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
     if (i < 0 || i >= n_act) return;
     const int k0 = i * kBc;
     const bool need_mask = (CAUSAL && (k0 + kBc - 1 > q0)) || (k0 + kBc > a.N);
-    if (need_mask) {
-      const int row = q0 + l32;
-      const int lim = CAUSAL ? min(row, a.N - 1) : a.N - 1;
+    if (need_mask) {  // key k0 + 4 half + c, with c a constant per element
+      const int lim = (CAUSAL ? min(q0 + l32, a.N - 1) : a.N - 1) - (k0 + 4 * half);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = k0 + 32 * mb + 8 * (e / 4) + 4 * half + (e % 4);
-          if (key > lim) s[mb][e] = -INFINITY;
-        }
+        for (int e = 0; e < 16; ++e)
+          if (32 * mb + 8 * (e / 4) + (e % 4) > lim) s[mb][e] = -INFINITY;
     }
     float tmax = -INFINITY;
 #pragma unroll
