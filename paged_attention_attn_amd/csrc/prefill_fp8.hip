@@ -19,10 +19,12 @@
 //    lane reads 32 contiguous bytes of a K row (two 16-byte LDS reads) and of its Q row.
 //  * O^T = V^T P^T: the score MFMA leaves lane l the probabilities of keys
 //    8(i/4) + 4(l/32) + i%4 (+32 for the second 32-key block), i = 0..15, of row l%32.  The
-//    contraction index (l/32, j) is taken to be key 8(j/4) + 4(l/32) + j%4, so the lane's 32
-//    probabilities, packed in order, are its B operand with no cross-lane exchange.  V is supplied
-//    transposed ([B, Hkv, d, N], keys contiguous), and a lane reads the matching 4-byte groups of
-//    its V^T row: 8 dwords at byte offsets 8g + 4(l/32).
+//    contraction index (l/32, j) is taken to be key 32(l/32) + j, so a lane's A operand is 32
+//    contiguous bytes of its V^T row (V is supplied transposed, [B, Hkv, d, N], keys
+//    contiguous), read as two 16-byte LDS reads.  For the B operand the two halves of the wave
+//    trade probabilities: after packing them to e4m3 in groups of four keys, one
+//    v_permlane32_swap per group gives the lower half the keys 0..31 and the upper half the keys
+//    32..63, already in order.
 //  * LDS: K tiles are 64 rows of d bytes, V^T tiles d rows of 64 bytes; 16-byte chunk c of row r is
 //    stored at chunk c ^ f(r), chosen so that every read above is free of bank conflicts
 //    (64 banks of 4 bytes); the swizzle is applied by choosing which chunk each lane of the direct
@@ -211,9 +213,9 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
 #pragma unroll
     for (int e = 0; e < 2; ++e)
       koff[t][e] = l32 * T::kKRowBytes + ((4 * t + 2 * half + e) ^ swz_k<D>(l32)) * 16;
-  int voff[4];  // V^T row l32 (+32 per head-dim block), chunk c, byte 4 half (+8 for the odd group)
+  int voff[2];  // V^T row l32 (+32 per head-dim block), chunks 2 half and 2 half + 1: keys 32 half .. +31
 #pragma unroll
-  for (int c = 0; c < 4; ++c) voff[c] = l32 * T::kVRowBytes + ((c ^ swz_v(l32)) * 16) + 4 * half;
+  for (int e = 0; e < 2; ++e) voff[e] = l32 * T::kVRowBytes + (((2 * half + e) ^ swz_v(l32)) * 16);
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t acc[kDBlocks];
@@ -242,10 +244,9 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
     if (i >= 1 && i - 1 < n_act) {
 #pragma unroll
       for (int db = 0; db < kDBlocks; ++db) {
-        i32x8_t vf;
-#pragma unroll
-        for (int gg = 0; gg < 8; ++gg)
-          vf[gg] = *(const PAA_LDS int*)(vt + db * 32 * T::kVRowBytes + voff[gg / 2] + 8 * (gg % 2));
+        const u32x4_t lo = *(const PAA_LDS u32x4_t*)(vt + db * 32 * T::kVRowBytes + voff[0]);
+        const u32x4_t hi = *(const PAA_LDS u32x4_t*)(vt + db * 32 * T::kVRowBytes + voff[1]);
+        const i32x8_t vf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         acc[db] = mfma_fp8(vf, pf, acc[db]);
       }
     }
@@ -281,6 +282,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
     }
     const float neg_ms = m_run == -INFINITY ? 0.f : -m_run * a.scale_log2;
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    int xy[2][4];  // e4m3 of keys 8g + 4 half + 0..3 of block mb (second block: +32)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       float p[16];
@@ -290,7 +292,15 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
         ps[e % 4] += p[e];
       }
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) pf[4 * mb + gq] = pack_fp8x4(p[4 * gq], p[4 * gq + 1], p[4 * gq + 2], p[4 * gq + 3]);
+      for (int gq = 0; gq < 4; ++gq) xy[mb][gq] = pack_fp8x4(p[4 * gq], p[4 * gq + 1], p[4 * gq + 2], p[4 * gq + 3]);
+    }
+    // swap the upper half's first block with the lower half's second: the lower half then holds
+    // keys 8g .. 8g + 7 (own, then partner) and the upper half keys 32 + 8g .. +7 (partner, then own)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const auto r = __builtin_amdgcn_permlane32_swap(xy[0][gq], xy[1][gq], false, false);
+      pf[2 * gq] = r[0];
+      pf[2 * gq + 1] = r[1];
     }
     l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
   };
