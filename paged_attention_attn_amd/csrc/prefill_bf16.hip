@@ -119,6 +119,133 @@ struct PrefillCfg {
 enum : int { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2, kMaskPaged = 3 };
 constexpr int kPageTokens = 16;  // tokens per cache page (the only page size the library accepts)
 
+// The work unit of a workgroup: query tile qt of query heads [g * group + hsub * HPW, + HPW) of
+// sequence (batch entry) b.
+struct WorkUnit {
+  int qt, hsub, g, b;
+};
+
+// Sequences ranked for the chunked-prefill order: up to this many are sorted on the device.
+constexpr int kMaxRankedSeqs = 256;
+
+// Unit of workgroup `blk`.  Heaviest work first: when the grid is larger than what the chip holds
+// at once, workgroups start as others finish and heaviest-first keeps the tail short.  When the
+// whole grid is resident at once (a.mirror), the dispatcher gives each CU workgroups a fixed
+// distance apart in launch order, so the second half of the grid is laid out in reverse: workgroup
+// u of the first half (heavy) and workgroup u + units/2 (light) then carry complementary work.
+//   Dense masks: query tiles from the last (most causal keys) to the first, each over every
+//   (b, g, hsub).
+//   Paged: the sequences' key counts (context + chunk) differ far more than a chunk's query tiles
+//   do, so the order is sequence-major, the sequence with the most keys first (ties by index; up
+//   to kMaxRankedSeqs sequences, beyond that in the given order), its query tiles last to first,
+//   then (g, hsub) innermost: consecutive workgroups go to the chip's dies (XCDs) in turn, so when
+//   Hkv * group / HPW is a multiple of their number every query tile of a (b, g) runs on one die
+//   at about the same time and reads that head's cache through one L2.
+// Paged units call this with every thread of the workgroup (it holds barriers) and `scratch`, LDS
+// room for kMaxRankedSeqs + 1 ints that nothing else uses until the call returns.
+template <int HPW, bool PAGED>
+__device__ __forceinline__ WorkUnit work_unit(const PrefillArgs& a, int blk, PAA_LDS int* scratch) {
+  const int units = a.n_qtiles * a.units_per_qt;
+  const int half_units = units / 2;
+  const int unit = (a.mirror && blk >= half_units) ? units - 1 + half_units - blk : blk;
+  const int subgroups = (a.H / a.Hkv) / HPW;
+  WorkUnit w;
+  if constexpr (!PAGED) {
+    w.qt = a.n_qtiles - 1 - unit / a.units_per_qt;
+    int rest = unit % a.units_per_qt;
+    w.hsub = rest % subgroups;
+    rest /= subgroups;
+    w.g = rest % a.Hkv;
+    w.b = rest / a.Hkv;
+  } else {
+    const int copies = a.Hkv * subgroups;  // units of one query tile of one sequence
+    const int per_seq = a.n_qtiles * copies;
+    const int rank = unit / per_seq;
+    const int r = unit % per_seq;
+    w.qt = a.n_qtiles - 1 - r / copies;
+    w.hsub = (r % copies) % subgroups;
+    w.g = (r % copies) / subgroups;
+    if (a.B > kMaxRankedSeqs) {
+      w.b = rank;
+    } else {
+      const int nthreads = blockDim.x;
+      for (int j = threadIdx.x; j < a.B; j += nthreads)
+        scratch[j] = max(a.ctx_lens[j], 0) + (a.q_start[j + 1] - a.q_start[j]);
+      __syncthreads();
+      // the sequence whose rank is `rank`: exactly one candidate has it
+      for (int c = threadIdx.x; c < a.B; c += nthreads) {
+        const int kc = scratch[c];
+        int before = 0;
+        for (int j = 0; j < a.B; ++j) {
+          const int kj = scratch[j];
+          before += (kj > kc) || (kj == kc && j < c);
+        }
+        if (before == rank) scratch[kMaxRankedSeqs] = c;
+      }
+      __syncthreads();
+      w.b = __builtin_amdgcn_readfirstlane(scratch[kMaxRankedSeqs]);
+      __syncthreads();  // every wave has read it before the room is reused
+    }
+  }
+  return w;
+}
+
+// Third word of a raw buffer resource (gfx9 family): 32-bit data format, no swizzle, no index.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// Direct loads (16 B per lane, buffer_load ... lds) of a wave's group of consecutive K or V rows
+// into LDS.  The group starts at key position row0 (wave-uniform) and has `rows` rows; a lane
+// moves 16 B of row row0 + dr, at byte `off` = (dr * stride + 8c) * 2 from the row0 row, where c
+// is the lane's piece of the row (`off` is fixed for the whole key loop).  Dense: the n_k rows
+// are `stride` elements apart from `src`.  Paged: positions before qoff are in cache page `page`
+// (the group lies in one page; a page holds 16 positions of every KV head, head g at `head_off`
+// elements into a position) and the rest are the n_k - qoff chunk rows of `src` (position - qoff);
+// cache and chunk rows are both `stride` elements apart.
+//   A load goes through a buffer resource whose size ends at the last valid row of what it reads:
+// rows at or past n_k read as zeros (they are masked) and no access leaves the valid rows.  The
+// resource and the group's byte shift are wave-uniform and worked out once per group
+// (group_source); each load then costs one vector add.  A paged group that straddles the end of
+// the context (once per sequence and stream) takes per-lane addresses instead.
+struct GroupSource {
+  const uint16_t* base;  // what the resource starts at
+  int bytes;             // its size
+  int shift;             // byte offset of the group's first row from `base`
+  bool straddles;        // paged: the group holds both cache and chunk rows
+  const uint16_t* page;  // paged: the group's first row in the cache page
+};
+
+template <bool PAGED>
+__device__ __forceinline__ GroupSource group_source(const uint16_t* src, const uint16_t* cache, int row0, int rows,
+                                                    int n_k, int qoff, int stride, int page, int head_off) {
+  const int row_bytes = stride * 2;
+  GroupSource gs{src, (n_k - qoff) * row_bytes, (row0 - qoff) * row_bytes, false, nullptr};
+  if constexpr (PAGED) {
+    if (row0 < qoff) {
+      gs.page = cache + ((size_t)page * kPageTokens + row0 % kPageTokens) * stride + head_off;
+      gs.straddles = row0 + rows > qoff;
+      gs.base = gs.page;
+      gs.bytes = rows * row_bytes;
+      gs.shift = 0;
+    }
+  }
+  return gs;
+}
+
+template <bool PAGED>
+__device__ __forceinline__ void group_load(PAA_LDS void* dst, const GroupSource& gs, const uint16_t* src, int row0,
+                                           int dr, uint32_t off, int n_k, int qoff, int stride) {
+  if (!PAGED || !gs.straddles) {
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)gs.base, (short)0, gs.bytes, kRawBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, (int)(off + (uint32_t)gs.shift), 0, 0, 0);
+  } else {
+    // chunk rows at or past n_k repeat row n_k - 1
+    const int key = min(row0 + dr, n_k - 1);
+    const char* p = key < qoff ? (const char*)gs.page + off
+                               : (const char*)(src + (size_t)(key - qoff) * stride) + (off - (uint32_t)(dr * stride * 2));
+    __builtin_amdgcn_global_load_lds((const void*)p, dst, 16, 0, 0);
+  }
+}
+
 template <int D, int MASK, int HPW, int WAVES, int RB, int STAGES>
 __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_kernel(
     PrefillArgs a) {
@@ -161,31 +288,18 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   using I0 = std::integral_constant<int, 0>;
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform: group bases stay scalar
   const int lane = tid % 64;
   const int half = lane / 32;  // which half-wave
   const int l32 = lane % 32;
   const int gi = lane % 16;
   const int colhalf = (lane / 16) % 2;
 
-  // ---- work unit: heaviest query tiles first ----
-  // When the grid is larger than what the chip holds at once, workgroups start as others finish
-  // and heaviest-first keeps the tail short.  When the whole grid is resident at once, the
-  // dispatcher gives each CU workgroups a fixed distance apart in launch order, so the second half
-  // of the grid is laid out in reverse: workgroup u of the first half (heavy) and workgroup
-  // u + units/2 (light) then carry complementary causal work.
-  const int units = a.n_qtiles * a.units_per_qt;
-  const int half_units = units / 2;
-  const int unit = (a.mirror && (int)blockIdx.x >= half_units) ? units - 1 + half_units - (int)blockIdx.x
-                                                                : (int)blockIdx.x;
-  const int qt = a.n_qtiles - 1 - unit / a.units_per_qt;
-  int rest = unit % a.units_per_qt;
+  // ---- work unit (heaviest first) ----
+  static_assert(4 * (kMaxRankedSeqs + 1) <= T::kTileBytes, "rank scratch fits a stage buffer");
+  const WorkUnit wu = work_unit<HPW, PAGED>(a, (int)blockIdx.x, (PAA_LDS int*)k_st0);
+  const int qt = wu.qt, hsub = wu.hsub, g = wu.g, b = wu.b;
   const int group = a.H / a.Hkv;
-  const int subgroups = group / HPW;
-  const int hsub = rest % subgroups;
-  rest /= subgroups;
-  const int g = rest % a.Hkv;
-  const int b = rest / a.Hkv;
 
   const int head = g * group + hsub * HPW + wave / kRowBlocks;
   const int q0_tile = qt * kTileRows;
@@ -234,25 +348,20 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   // ---- direct global -> LDS load of one tile of K or V; this wave fetches kBlocksPerWave 1 KB blocks ----
   // Paged: the rows this wave fetches lie in one cache page (kWavePage of the tile's four), whose id
   // `page` the caller looked up; positions before qoff come from the cache, the rest from the chunk.
-  const int wave_page = (wave * C::kBlocksPerWave * T::kRowsPerBlock) / kPageTokens;
-  auto dma_src = [&](const uint16_t* src, uint16_t* cache, int key, int page, int c) __attribute__((always_inline))
-      -> const uint16_t* {
-    if constexpr (PAGED) {
-      if (key < qoff) return cache + (((size_t)page * kPageTokens + key % kPageTokens) * a.Hkv + g) * D + c * 8;
-      return src + (size_t)(key - qoff) * kv_stride + c * 8;
-    } else {
-      return src + (size_t)key * D + c * 8;
-    }
-  };
+  constexpr int kGroupRows = C::kBlocksPerWave * T::kRowsPerBlock;  // consecutive tile rows one wave loads
+  const int group_r0 = wave * kGroupRows;                            // the first of them
+  static_assert(kPageTokens % kGroupRows == 0, "a wave's rows of a tile lie in one page");
+  const int wave_page = group_r0 / kPageTokens;
   auto dma = [&](const uint16_t* src, uint16_t* cache, int j, int page, PAA_LDS char* dst) __attribute__((always_inline)) {
+    const int row0 = j * kBc + group_r0;
+    const GroupSource gs = group_source<PAGED>(src, cache, row0, kGroupRows, n_k, qoff, (int)kv_stride, page, g * D);
 #pragma unroll
     for (int i = 0; i < C::kBlocksPerWave; ++i) {
       const int blk = wave * C::kBlocksPerWave + i;
-      const int r = blk * T::kRowsPerBlock + lane / T::kCpr;  // tile row written by this lane
-      const int c = (lane % T::kCpr) ^ swz<D>(r);             // data chunk stored at this lane's position
-      const int key = min(j * kBc + r, n_k - 1);  // rows past the end repeat a valid row; they are masked
-      __builtin_amdgcn_global_load_lds((const void*)dma_src(src, cache, key, page, c), (PAA_LDS void*)(dst + blk * 1024),
-                                       16, 0, 0);
+      const int dr = i * T::kRowsPerBlock + lane / T::kCpr;  // tile row written by this lane: group_r0 + dr
+      const int c = (lane % T::kCpr) ^ swz<D>(group_r0 + dr);  // data chunk stored at this lane's position
+      const uint32_t off = (uint32_t)((dr * kv_stride + c * 8) * 2);
+      group_load<PAGED>((PAA_LDS void*)(dst + blk * 1024), gs, src, row0, dr, off, n_k, qoff, (int)kv_stride);
     }
   };
   // cache page holding this wave's rows of tile j (0 when not paged); an id outside the pool is
@@ -539,7 +648,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   using T = TileLayout<D>;
   constexpr bool CAUSAL = MASK != kMaskNone;
   constexpr bool WINDOW = MASK == kMaskWindow;
-  static_assert(!(KSPLIT && (WINDOW || MASK == kMaskPaged)), "split keys: plain and causal masks only");
+  constexpr bool PAGED = MASK == kMaskPaged;
+  static_assert(!(KSPLIT && (WINDOW || PAGED)), "split keys: plain and causal masks only");
+  static_assert(!PAGED || STAGES == 2, "the paged page-id prefetch assumes two stages");
   constexpr int kRowWaves = KSPLIT ? WAVES / 2 : WAVES;  // waves holding distinct query rows
   constexpr int kRowBlocks = kRowWaves / HPW;          // waves per head in a workgroup
   constexpr int kTileRows = kRowBlocks * 32;           // query rows per head in a workgroup
@@ -582,32 +693,42 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   const int gi = lane % 16;
   const int colhalf = (lane / 16) % 2;
 
-  // ---- work unit (as in the four-wave kernel) ----
-  const int units = a.n_qtiles * a.units_per_qt;
-  const int half_units = units / 2;
-  const int unit = (a.mirror && (int)blockIdx.x >= half_units) ? units - 1 + half_units - (int)blockIdx.x
-                                                                : (int)blockIdx.x;
-  const int qt = a.n_qtiles - 1 - unit / a.units_per_qt;
-  int rest = unit % a.units_per_qt;
+  // ---- work unit (heaviest first) ----
+  static_assert(4 * (kMaxRankedSeqs + 1) <= T::kTileBytes, "rank scratch fits a stage buffer");
+  const WorkUnit wu = work_unit<HPW, PAGED>(a, (int)blockIdx.x, (PAA_LDS int*)k_st0);
+  const int qt = wu.qt, hsub = wu.hsub, g = wu.g, b = wu.b;
   const int group = a.H / a.Hkv;
-  const int subgroups = group / HPW;
-  const int hsub = rest % subgroups;
-  rest /= subgroups;
-  const int g = rest % a.Hkv;
-  const int b = rest / a.Hkv;
 
   const int wrow = KSPLIT ? wave % kRowWaves : wave;  // this wave's row block among the workgroup's
   const int head = g * group + hsub * HPW + wrow / kRowBlocks;
   const int q0_tile = qt * kTileRows;
   const int q0 = q0_tile + (wrow % kRowBlocks) * 32;
 
+  // Geometry (as in the lock-step kernel): n_q query rows, n_k keys, query row i at key position
+  // qoff + i; rows of Q / O / LSE and of K / V are q_stride / kv_stride elements apart.
   const size_t N = a.N;
-  const uint16_t* qh = a.q + ((size_t)b * a.H + head) * N * D;
-  const uint16_t* kh = a.k + ((size_t)b * a.Hkv + g) * N * D;
-  const uint16_t* vh = a.v + ((size_t)b * a.Hkv + g) * N * D;
+  int n_q = a.N, n_k = a.N, qoff = 0;
+  size_t q_base, kv_base, q_stride = D, kv_stride = D;
+  if constexpr (PAGED) {
+    const int lo = a.q_start[b];
+    n_q = a.q_start[b + 1] - lo;
+    qoff = max(a.ctx_lens[b], 0);
+    n_k = qoff + n_q;
+    if (q0_tile >= n_q) return;  // the whole workgroup: this sequence's chunk is shorter
+    q_base = (size_t)lo * a.H * D + (size_t)head * D;
+    q_stride = (size_t)a.H * D;
+    kv_base = (size_t)lo * a.Hkv * D + (size_t)g * D;
+    kv_stride = (size_t)a.Hkv * D;
+  } else {
+    q_base = ((size_t)b * a.H + head) * N * D;
+    kv_base = ((size_t)b * a.Hkv + g) * N * D;
+  }
+  const uint16_t* qh = a.q + q_base;
+  const uint16_t* kh = a.k + kv_base;
+  const uint16_t* vh = a.v + kv_base;
 
   // ---- key tiles: iteration t is tile tile_of(t); this wave computes iterations [0, n_act) ----
-  const int kv_end = CAUSAL ? min(a.N, q0_tile + kTileRows) : a.N;
+  const int kv_end = CAUSAL ? min(n_k, qoff + q0_tile + kTileRows) : n_k;
   const int n_tiles = (kv_end + kBc - 1) / kBc;
   int n_glob = 0, j_win = 0;
   if constexpr (WINDOW) {
@@ -616,7 +737,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   }
   const int n_iter = n_glob + (n_tiles - j_win);
   auto tile_of = [&](int t) __attribute__((always_inline)) { return t < n_glob ? t : j_win + (t - n_glob); };
-  const int last_tile = CAUSAL ? min(n_tiles - 1, (q0 + 31) / kBc) : n_tiles - 1;
+  const int last_tile = CAUSAL ? min(n_tiles - 1, (qoff + q0 + 31) / kBc) : n_tiles - 1;
   // iteration i of this wave works on key tile key_tile(i) (tile_of(i), or 2i + grp when split);
   // it computes iterations [0, n_act) of the n_loop the workgroup runs
   int n_act, n_loop;
@@ -631,22 +752,37 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
 
   // One 1 KB block of a stage: block u of the list [K slot 0, (K slot 1,) V slot 0, (V slot 1)];
   // slot t of a stage holds tile j + t.
-  auto load_block = [&](int u, int jk, int jv, PAA_LDS char* kdst, PAA_LDS char* vdst) __attribute__((always_inline)) {
-    const bool is_v = u >= kSlots * T::kBlocks;
-    const int w = is_v ? u - kSlots * T::kBlocks : u;
-    const int slot = w / T::kBlocks, blk = w % T::kBlocks;
-    const int r = blk * T::kRowsPerBlock + lane / T::kCpr;
-    const int c = (lane % T::kCpr) ^ swz<D>(r);
-    const int key = min(((is_v ? jv : jk) + slot) * kBc + r, a.N - 1);  // rows past the end are masked
-    const uint16_t* src = is_v ? vh : kh;
-    PAA_LDS char* dst = (is_v ? vdst : kdst) + slot * T::kTileBytes + blk * 1024;
-    __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)key * D + c * 8), (PAA_LDS void*)dst, 16, 0, 0);
+  // Paged: a wave's rows of a tile lie in one 16-token page, whose id `page` the caller looked up;
+  // positions before qoff come from the cache, the rest from the chunk.
+  // The blocks a wave loads in one stage are consecutive rows of one slot (K or V); paged, they
+  // also lie in one page.
+  constexpr int kGroupRows = kLoadsPerStage * T::kRowsPerBlock;
+  static_assert(T::kBlocks % kLoadsPerStage == 0, "a wave's blocks of a stage lie in one slot");
+  static_assert(!PAGED || kGroupRows <= kPageTokens, "a wave's rows of a stage lie in one page");
+  const bool loads_v = wave * kLoadsPerStage >= kSlots * T::kBlocks;
+  const int w0 = loads_v ? wave * kLoadsPerStage - kSlots * T::kBlocks : wave * kLoadsPerStage;
+  const int load_slot = w0 / T::kBlocks;
+  const int group_r0 = (w0 % T::kBlocks) * T::kRowsPerBlock;  // first tile row of the wave's group
+  const int wave_page = group_r0 / kPageTokens;
+  const uint16_t* load_src = loads_v ? vh : kh;
+  auto load_block = [&](int i, int row0, const GroupSource& gs, PAA_LDS char* kdst, PAA_LDS char* vdst) __attribute__((always_inline)) {
+    const int dr = i * T::kRowsPerBlock + lane / T::kCpr;   // tile row written by this lane: group_r0 + dr
+    const int c = (lane % T::kCpr) ^ swz<D>(group_r0 + dr);
+    const uint32_t off = (uint32_t)((dr * kv_stride + c * 8) * 2);
+    PAA_LDS char* dst = (loads_v ? vdst : kdst) + load_slot * T::kTileBytes + (group_r0 / T::kRowsPerBlock + i) * 1024;
+    group_load<PAGED>((PAA_LDS void*)dst, gs, load_src, row0, dr, off, n_k, qoff, (int)kv_stride);
+  };
+  auto page_of = [&](int j) __attribute__((always_inline)) -> int {  // page of this wave's rows of tile j
+    if constexpr (PAGED) {
+      const int blk = min((j * kBc) / kPageTokens + wave_page, a.max_pages - 1);
+      return min(max(a.bt[(size_t)b * a.max_pages + blk], 0), a.num_pages - 1);
+    } else {
+      return 0;
+    }
   };
   // stage s: K of iteration s and V of iteration s - 1; iterations past the end repeat the last
   // one (the buffer is free and never read), so every stage issues the same number of loads
-  auto issue_stage = [&](auto s_tag, int s) __attribute__((always_inline)) {
-    using Prev = std::integral_constant<int, decltype(s_tag)::value + STAGES - 1>;
-    int jk, jv;
+  auto stage_tiles = [&](int s, int& jk, int& jv) __attribute__((always_inline)) {
     if constexpr (KSPLIT) {  // pairs of tiles; the last pair may reach one tile past the end (masked)
       jk = 2 * min(s, n_loop - 1);
       jv = 2 * min(max(s - 1, 0), n_loop - 1);
@@ -654,8 +790,23 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
       jk = tile_of(min(s, n_iter - 1));
       jv = tile_of(min(max(s - 1, 0), n_iter - 1));
     }
+  };
+  // the page id of this wave's rows of stage s (0 when not paged)
+  auto stage_page = [&](int s) __attribute__((always_inline)) -> int {
+    int jk, jv;
+    stage_tiles(s, jk, jv);
+    return page_of(loads_v ? jv : jk);
+  };
+  int page_next = 0;  // paged: the page id of the next refill, loaded one refill ahead
+  auto issue_stage = [&](auto s_tag, int s, int page) __attribute__((always_inline)) {
+    using Prev = std::integral_constant<int, decltype(s_tag)::value + STAGES - 1>;
+    int jk, jv;
+    stage_tiles(s, jk, jv);
+    const int row0 = ((loads_v ? jv : jk) + load_slot) * kBc + group_r0;
+    const GroupSource gs = group_source<PAGED>(load_src, loads_v ? a.vc : a.kc, row0, kGroupRows, n_k, qoff,
+                                               (int)kv_stride, page, g * D);
 #pragma unroll
-    for (int i = 0; i < kLoadsPerStage; ++i) load_block(wave * kLoadsPerStage + i, jk, jv, kst(s_tag), vst(Prev{}));
+    for (int i = 0; i < kLoadsPerStage; ++i) load_block(i, row0, gs, kst(s_tag), vst(Prev{}));
   };
 
   // ---- Q fragments first (their loads then retire before the ring's) ----
@@ -664,16 +815,17 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     const int row = q0 + l32;
 #pragma unroll
     for (int t = 0; t < kKSteps; ++t) {
-      if (row < a.N)
-        qf[t] = *(const u32x4_t*)(qh + (size_t)row * D + 16 * t + 8 * half);
+      if (row < n_q)
+        qf[t] = *(const u32x4_t*)(qh + (size_t)row * q_stride + 16 * t + 8 * half);
       else
         qf[t] = u32x4_t{0, 0, 0, 0};
     }
   }
   // prologue: stages 0 .. STAGES-1 (stage 0's V half repeats tile 0 into a free buffer)
-  issue_stage(std::integral_constant<int, 0>{}, 0);
-  auto prologue = [&](auto s_tag, int s) __attribute__((always_inline)) { issue_stage(s_tag, s); };
+  issue_stage(std::integral_constant<int, 0>{}, 0, stage_page(0));
+  auto prologue = [&](auto s_tag, int s) __attribute__((always_inline)) { issue_stage(s_tag, s, stage_page(s)); };
   for_stages<1, STAGES>(prologue, 0, STAGES);
+  if constexpr (PAGED) page_next = stage_page(STAGES);
 
   int koff[kKSteps];
 #pragma unroll
@@ -746,11 +898,11 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     if (i < 0 || i >= n_act) return;
     const int k0 = key_tile(i) * kBc;
     const bool need_window = WINDOW && (k0 <= q0 + 31 - a.window) && (k0 + kBc - 1 >= a.n_global);
-    const bool need_mask = (CAUSAL && (k0 + kBc - 1 > q0)) || (k0 + kBc > a.N) || need_window;
+    const bool need_mask = (CAUSAL && (k0 + kBc - 1 > qoff + q0)) || (k0 + kBc > n_k) || need_window;
     if (need_mask) {  // as in the lock-step kernel: constant offsets against per-lane bounds
-      const int row = q0 + l32;
+      const int row = qoff + q0 + l32;  // key position of the lane's query row
       const int base = k0 + 4 * half;
-      const int lim = (CAUSAL ? min(row, a.N - 1) : a.N - 1) - base;
+      const int lim = (CAUSAL ? min(row, n_k - 1) : n_k - 1) - base;
       const int win = row - a.window - base, glob = a.n_global - base;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -806,7 +958,10 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     auto period_pair = [&](auto u_tag, int i) __attribute__((always_inline)) {
       using U = decltype(u_tag);
       using Refill = std::integral_constant<int, U::value + STAGES - 1>;  // stage i - 1 + STAGES
-      if (i >= 1) issue_stage(Refill{}, i - 1 + STAGES);
+      if (i >= 1) {
+        issue_stage(Refill{}, i - 1 + STAGES, page_next);
+        if constexpr (PAGED) page_next = stage_page(i + STAGES);  // retires with this pair's waits
+      }
       if constexpr (kLead) m_phase(U{}, i); else v_phase(i - 1);
       tile_barrier();
       if constexpr (kLead) v_phase(i); else m_phase(U{}, i);
@@ -861,8 +1016,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   const int row = q0 + l32;
   const float l_tot = l_run + swap_halves(l_run, half);
   const float inv_l = 1.f / l_tot;
-  if (row < a.N) {
-    uint16_t* orow = a.o + (((size_t)b * a.H + head) * N + row) * D;
+  if (row < n_q) {
+    uint16_t* orow = a.o + q_base + (size_t)row * q_stride;
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db) {
 #pragma unroll
@@ -873,7 +1028,31 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
         *(u32x2_t*)(orow + d0) = w;
       }
     }
-    if (a.lse != nullptr && half == 0) a.lse[((size_t)b * a.H + head) * N + row] = a.scale * m_run + __logf(l_tot);
+    if (a.lse != nullptr && half == 0) {
+      const size_t li = PAGED ? q_base / D + (size_t)row * a.H : ((size_t)b * a.H + head) * N + row;
+      a.lse[li] = a.scale * m_run + __logf(l_tot);
+    }
+  }
+
+  // ---- paged: append this workgroup's chunk rows to the caches (as in the lock-step kernel) ----
+  if constexpr (PAGED) {
+    if (hsub == 0) {
+      constexpr int kChunks = D / 8;
+      const int rows = min(kTileRows, n_q - q0_tile);
+      for (int e = tid; e < 2 * rows * kChunks; e += 64 * WAVES) {
+        const bool is_v = e >= rows * kChunks;
+        const int f = is_v ? e - rows * kChunks : e;
+        const int i = q0_tile + f / kChunks;
+        const int c = f % kChunks;
+        const int pos = qoff + i;
+        const int blk = pos / kPageTokens;
+        const int page = blk < a.max_pages ? a.bt[(size_t)b * a.max_pages + blk] : -1;
+        if (page < 0 || page >= a.num_pages) continue;
+        const u32x4_t val = *(const u32x4_t*)((is_v ? vh : kh) + (size_t)i * kv_stride + c * 8);
+        uint16_t* dst = (is_v ? a.vc : a.kc) + (((size_t)page * kPageTokens + pos % kPageTokens) * a.Hkv + g) * D + c * 8;
+        *(u32x4_t*)dst = val;
+      }
+    }
   }
 }
 
@@ -976,7 +1155,10 @@ hipError_t dispatch_paged(const PrefillArgs& a, hipStream_t stream) {
   const int hpw = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
   const long long rows8 = (8 / hpw) * 32;
   const long long units8 = (long long)a.B * a.Hkv * (group / hpw) * ((a.N + rows8 - 1) / rows8);
-  if (units8 >= 1024) return dispatch_group<D, kMaskPaged, 8>(a, stream);
+  if (units8 >= 1024) {
+    if constexpr (D == 128) return dispatch_pp<D, kMaskPaged>(a, stream);
+    else return dispatch_group<D, kMaskPaged, 8>(a, stream);
+  }
   return dispatch_group<D, kMaskPaged, 4>(a, stream);
 }
 

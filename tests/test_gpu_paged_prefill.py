@@ -77,6 +77,38 @@ def test_paged_prefill_small_full_parity(ctxs, qlens, H, Hkv, d):
     _check_all(a)
 
 
+# Grids of at least 1024 eight-wave workgroups (d = 128 takes the ping-pong kernel there): one per
+# head-sharing width (4, 2, 1 query heads per workgroup); the last two reach that size through a
+# loose max_q_len, so most of their workgroups leave at once.
+LARGE = [
+    ([0, 1, 15, 16, 17, 63, 64, 65, 500, 1000, 2047, 3, 300, 0, 777, 129],
+     [512, 1, 0, 100, 511, 64, 65, 300, 129, 17, 2, 512, 256, 16, 400, 33], 32, 8, 128, 512),
+    ([5, 0, 64, 1500, 31, 200, 16, 999], [300, 129, 0, 64, 1, 250, 77, 16], 16, 8, 128, 2048),
+    ([700, 0, 48, 1], [700, 0, 257, 1], 8, 8, 128, 8192),
+]
+
+
+@pytest.mark.parametrize("ctxs,qlens,H,Hkv,d,max_q_len", LARGE)
+def test_paged_prefill_large_grid_full_parity(ctxs, qlens, H, Hkv, d, max_q_len):
+    w = ChunkedPrefillWorkload("large", len(ctxs), H, Hkv, d, 0, 0, 1, num_pages=600)
+    _announce(f"paged prefill ctx{ctxs} q{qlens} H{H} Hkv{Hkv} d{d} max_q_len {max_q_len}")
+    a = chunked_prefill_inputs(w, seed=sum(ctxs) + H, ctx_lens=ctxs, q_lens=qlens)
+    _check_all(a, max_q_len)
+
+
+@pytest.mark.parametrize("num_seqs,H,Hkv,d", [(300, 8, 8, 128), (256, 16, 8, 128), (300, 8, 2, 64), (200, 8, 2, 64)])
+def test_paged_prefill_many_sequences(num_seqs, H, Hkv, d):
+    """Sequences are taken heaviest first when there are at most 256 of them, in the given order
+    beyond that; both orders against the oracle, with short ragged contexts and chunks."""
+    rng = np.random.default_rng(num_seqs + d)
+    ctxs = [int(x) for x in rng.integers(0, 60, size=num_seqs)]
+    qlens = [int(x) for x in rng.integers(0, 40, size=num_seqs)]
+    w = ChunkedPrefillWorkload("many", num_seqs, H, Hkv, d, 0, 0, 1, num_pages=2000)
+    _announce(f"paged prefill {num_seqs} sequences H{H} Hkv{Hkv} d{d}")
+    a = chunked_prefill_inputs(w, seed=num_seqs + d, ctx_lens=ctxs, q_lens=qlens)
+    _check_all(a, max_q_len=64)
+
+
 def test_paged_prefill_loose_max_q_len():
     """A max_q_len far above every chunk only adds workgroups that leave at once."""
     w = ChunkedPrefillWorkload("loose", 3, 8, 2, 128, 0, 0, 1, num_pages=200)
