@@ -41,7 +41,8 @@ enum {
   ATTN_ERR_UNSUPPORTED_PAGE_SIZE = 4, /* page_size != 16 */
   ATTN_ERR_WORKSPACE_TOO_SMALL = 5,   /* workspace_bytes below the required size */
   ATTN_ERR_MISALIGNED = 6,            /* a pointer breaks the alignment rule above */
-  ATTN_ERR_TOO_LARGE = 7,             /* sizes overflow the launch grid or 64-bit offsets */
+  ATTN_ERR_TOO_LARGE = 7,             /* sizes overflow the launch grid, 64-bit offsets, or the
+                                         2 GiB a kernel reads through one buffer resource */
   ATTN_ERR_UNSUPPORTED_GROUP = 8,     /* decode: more than 16 query heads per KV head */
   ATTN_ERR_LAUNCH = 9,                /* hipGetLastError reported a failed launch */
   ATTN_ERR_INVALID_SCALE = 10         /* scale is not a finite positive number */
@@ -61,8 +62,10 @@ enum {
  *   lse [B, H,   N]    fp32 (written; may be NULL to skip)
  * Query head h reads KV head h / (H / Hkv) (grouped-query attention; H must
  * be a multiple of Hkv).  d must be 64 or 128; scale must be finite and
- * positive (1/sqrt(d) in the pages' formula).  B == 0 or N == 0 is a valid
- * empty call (pointers are then not checked and may be NULL).  Arithmetic: bf16 products, fp32 accumulation and softmax; the
+ * positive (1/sqrt(d) in the pages' formula).  One batch entry's K or V head,
+ * N * d * 2 bytes, must stay below 2 GiB (ATTN_ERR_TOO_LARGE).  B == 0 or N == 0
+ * is a valid empty call (pointers are then not checked and may be NULL).
+ * Arithmetic: bf16 products, fp32 accumulation and softmax; the
  * probabilities are rounded to bf16 before the product with V.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
@@ -140,8 +143,10 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v_t, void* o, float* 
  *   lse         [T, H] fp32 (written; may be NULL)
  *   max_q_len   host upper bound on every chunk length (sizes the grid)
  * page_size must be 16, d 64 or 128, scale finite and positive,
- * max_pages_per_seq and num_pages at least 1.  num_seqs == 0 or max_q_len == 0
- * is a valid empty call (pointers may be NULL).  The caller keeps its own
+ * max_pages_per_seq and num_pages at least 1; max_q_len * Hkv * d * 2 bytes (the
+ * most chunk rows of k_new one sequence may own) must stay below 2 GiB
+ * (ATTN_ERR_TOO_LARGE).  num_seqs == 0 or max_q_len == 0 is a valid empty call
+ * (pointers may be NULL).  The caller keeps its own
  * lengths: after the call sequence s holds ctx_lens[s] + chunk length tokens.
  * Device-side rules (the length arrays and the table are never read on the
  * host): chunk lengths are at most max_q_len (rows beyond are neither computed

@@ -48,6 +48,7 @@ P = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails valid
     ((P, P, P, P, None, 1, 2, 2, 8, 96, 1, 0.1), HEAD_DIM),
     ((ctypes.c_void_p(0x10008), P, P, P, None, 1, 2, 2, 8, 64, 1, 0.1), ALIGN),
     ((P, P, P, P, None, 70000, 30000, 1, 100000, 128, 1, 0.1), LARGE),
+    ((P, P, P, P, None, 1, 1, 1, 1 << 23, 128, 1, 0.1), LARGE),  # one K head of 2 GiB
     ((P, P, P, P, None, 0, 2, 2, 8, 64, 1, 0.1), ATTN_OK),   # empty batch: nothing to launch
     ((None, None, None, None, None, 0, 2, 2, 8, 64, 1, 0.1), ATTN_OK),  # empty: pointers unused
     ((P, P, P, P, None, 1, 2, 2, 0, 64, 1, 0.1), ATTN_OK),   # empty sequence
@@ -169,6 +170,7 @@ def test_paged_prefill_validation(L):
     p[3] = ctypes.c_void_p(0x10008)  # k_cache not 16-byte aligned
     assert call(p=p) == ALIGN
     assert call(max_pages=1 << 28) == LARGE
+    assert call(Hkv=8, max_q_len=1 << 20) == LARGE  # one sequence's chunk rows of k_new: 2 GiB
 
 
 def test_fp8_validation(L):
