@@ -190,9 +190,6 @@ __device__ __forceinline__ WorkUnit work_unit(const PrefillArgs& a, int blk, PAA
   return w;
 }
 
-// Third word of a raw buffer resource (gfx9 family): 32-bit data format, no swizzle, no index.
-constexpr int kRawBufferWord3 = 0x00020000;
-
 // Direct loads (16 B per lane, buffer_load ... lds) of a wave's group of consecutive K or V rows
 // into LDS.  The group starts at key position row0 (wave-uniform) and has `rows` rows; a lane
 // moves 16 B of row row0 + dr, at byte `off` = (dr * stride + 8c) * 2 from the row0 row, where c

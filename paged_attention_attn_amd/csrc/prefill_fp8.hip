@@ -161,21 +161,28 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
   // One stage: K of iteration s and V^T of iteration s - 1.  The waves' loads are numbered
   // u = wave * kLoadsPerStage + i over the K blocks, then the V^T blocks; iterations past the end
   // repeat the last one (the buffer is free and never read), so every stage issues the same count.
+  // Loads go through buffer resources spanning this (batch, KV head)'s K and V^T, so each costs
+  // one vector add on a lane offset fixed for the loop: K rows past the end read as zeros (they
+  // are masked); V^T rows run on into the next row, so the last tile's chunks past the end are
+  // pointed back at valid keys instead.
+  const int kv_bytes = a.N * D;  // below 2^31 (checked on the host)
+  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kh, (short)0, kv_bytes, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vh, (short)0, kv_bytes, kRawBufferWord3);
   auto load_block = [&](int u, int jk, int jv, PAA_LDS char* kdst, PAA_LDS char* vdst) __attribute__((always_inline)) {
     if (u < T::kKBlocks) {
       constexpr int kRowsPerBlock = 1024 / D;
       const int r = u * kRowsPerBlock + lane / T::kKCpr;
       const int c = (lane % T::kKCpr) ^ swz_k<D>(r);
-      const int key = min(jk * kBc + r, a.N - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(kh + (size_t)key * D + c * 16), (PAA_LDS void*)(kdst + u * 1024),
-                                       16, 0, 0);
+      const uint32_t off = (uint32_t)(r * D + c * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (PAA_LDS void*)(kdst + u * 1024), 16,
+                                               (int)(off + (uint32_t)(jk * kBc * D)), 0, 0, 0);
     } else {
       const int vb = u - T::kKBlocks;
       const int d = vb * 16 + lane / 4;
       const int c = (lane % 4) ^ swz_v(d);
-      const int key0 = min(jv * kBc + 16 * c, a.N - 16);  // chunks past the end repeat valid keys
-      __builtin_amdgcn_global_load_lds((const void*)(vh + (size_t)d * N + key0), (PAA_LDS void*)(vdst + vb * 1024),
-                                       16, 0, 0);
+      const int key0 = jv * kBc + 16 * c;
+      const int key = jv * kBc + kBc <= a.N ? key0 : min(key0, a.N - 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (PAA_LDS void*)(vdst + vb * 1024), 16, d * a.N + key, 0, 0, 0);
     }
   };
   auto issue_stage = [&](auto s_tag, int s) __attribute__((always_inline)) {

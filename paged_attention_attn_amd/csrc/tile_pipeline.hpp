@@ -1,5 +1,6 @@
 // Pieces of the tiled attention loop shared by the prefill kernels: tile size, the lazy-rescale
-// threshold, exact vmcnt waits, the tile barrier and compile-time unrolling over ring stages.
+// threshold, the buffer resource format, exact vmcnt waits, the tile barrier and compile-time
+// unrolling over ring stages.
 #pragma once
 
 #include <type_traits>
@@ -10,6 +11,11 @@ namespace paa {
 
 constexpr int kBc = 64;               // keys per tile
 constexpr float kRescaleLog2 = 8.0f;  // lazy rescale threshold (probabilities stay <= 256)
+
+// Third word of a raw buffer resource (gfx9 family): 32-bit data format, no swizzle, no index.
+// The tile loads read K and V through such resources (buffer_load ... lds), sized so that
+// anything past the valid rows reads as zeros.
+constexpr int kRawBufferWord3 = 0x00020000;
 
 
 // vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
