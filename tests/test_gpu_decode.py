@@ -144,6 +144,57 @@ def test_decode_one_long_sequence_many_ranges():
     assert_close_lse(lse, rl)
 
 
+# Page lists of at least 8 pages per workgroup range (ranges = 2048 / Hkv) at three head layouts;
+# lengths around page edges, an empty and a one-token sequence, ranges that straddle sequences.
+LONG_LISTS = [
+    (128, 32, 32, [3100, 1, 0, 2500, 17, 2600]),
+    (64, 16, 16, [5000, 33, 7000, 0, 4600, 16]),
+    (128, 32, 8, [9000, 8000, 1, 7000, 6600, 2000, 511]),
+]
+
+
+@pytest.mark.parametrize("d,H,Hkv,lens", LONG_LISTS)
+def test_decode_long_lists_full_parity(d, H, Hkv, lens):
+    w = DecodeWorkload("long", len(lens), H, Hkv, d, 0, max(lens), 16, sum(-(-n // 16) for n in lens) + 8)
+    _announce(f"decode long page list d{d} H{H} Hkv{Hkv} lens {lens}")
+    a = decode_inputs(w, seed=len(lens) + d, seq_lens=lens)
+    o, lse, _ = _run(a, H)
+    ro, rl = _oracle(a)
+    empty = np.asarray(lens) == 0
+    assert np.all(o[empty] == 0) and np.all(np.isneginf(lse[empty]))
+    assert_close_bf16(o, ro)
+    assert_close_lse(lse, rl)
+
+
+def test_decode_garbage_workspace_and_repeats():
+    """Whatever the workspace held before (here random bytes), repeated calls on it and a call on a
+    fresh workspace give the same output and LSE, bit for bit."""
+    d, H, Hkv, lens = LONG_LISTS[0]
+    w = DecodeWorkload("long", len(lens), H, Hkv, d, 0, max(lens), 16, sum(-(-n // 16) for n in lens) + 8)
+    _announce("decode garbage workspace and repeats")
+    a = decode_inputs(w, seed=99, seq_lens=lens)
+    q, kc, vc = dev_bf16(a["q"]), dev_bf16(a["k_cache"]), dev_bf16(a["v_cache"])
+    bt, sl = dev_i32(a["block_table"]), dev_i32(a["seq_lens"])
+    need = paa.paged_attn_decode_workspace_size(len(lens), H, d, 16, a["block_table"].shape[1])
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, generator=gen).to("cuda:0")
+    outs = []
+    for _ in range(4):
+        lse = torch.empty((len(lens), H), dtype=torch.float32, device="cuda:0")
+        o, _ = paa.paged_attn_decode(q, kc, vc, bt, sl, a["scale"], workspace=ws, lse=lse)
+        torch.cuda.synchronize()
+        outs.append((o.view(torch.int16).cpu().numpy().copy(), lse.cpu().numpy().copy()))
+    lse = torch.empty((len(lens), H), dtype=torch.float32, device="cuda:0")
+    o, _ = paa.paged_attn_decode(q, kc, vc, bt, sl, a["scale"], lse=lse)  # fresh workspace
+    torch.cuda.synchronize()
+    outs.append((o.view(torch.int16).cpu().numpy().copy(), lse.cpu().numpy().copy()))
+    for ob, lb in outs[1:]:
+        assert np.array_equal(ob, outs[0][0]) and np.array_equal(lb.view(np.int32), outs[0][1].view(np.int32))
+    ro, rl = _oracle(a)
+    assert_close_bf16(host_f64(o), ro)
+    assert_close_lse(outs[0][1].astype(np.float64), rl)
+
+
 def test_decode_many_short_sequences():
     """600 sequences (more than one scan chunk per workgroup) of 0..40 tokens."""
     S = 600
