@@ -11,16 +11,20 @@
 // work partitioning described there.
 //
 // Mapping onto the chip:
-//  * a workgroup is 4 waves; each wave owns 32 query rows of one query head.
-//    The 4 waves cover HPW heads of one GQA group x (4 / HPW) row blocks, so
-//    all of them read the same K/V head and share its LDS tiles.
+//  * a workgroup is 4 or 8 waves; each wave owns 32 query rows of one query
+//    head.  The waves cover HPW heads of one GQA group x (waves / HPW) row
+//    blocks, so all of them read the same K/V head and share its LDS tiles.
+//    (The ping-pong kernel further below runs its 8 waves as two groups one
+//    phase apart.)
 //  * K/V tiles of 64 keys go from global memory straight into LDS
-//    (global_load_lds_dwordx4, no VGPR staging), two stages deep: the loads of
-//    tile j+1 are in flight while tile j is computed, one barrier per tile.
-//    Each 16-byte chunk c of tile row r is stored at chunk position
-//    c ^ swz(r), which keeps both the row-wise K reads and the transposed V
-//    reads below free of LDS bank conflicts; the swizzle is applied by
-//    choosing which chunk each lane fetches, so the loads stay coalesced.
+//    (buffer_load_dwordx4 ... lds, no VGPR staging), two stages deep: the
+//    loads of tile j+1 are in flight while tile j is computed, one barrier per
+//    tile.  Each load goes through a buffer resource that ends at the last
+//    valid row, so rows past the end read as zeros.  Each 16-byte chunk c of
+//    tile row r is stored at chunk position c ^ swz(r), which keeps both the
+//    row-wise K reads and the transposed V reads below free of LDS bank
+//    conflicts; the swizzle is applied by choosing which chunk each lane
+//    fetches, so the loads stay coalesced.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q kept in
 //    VGPRs for the whole kernel), so each lane ends up holding 16 scores of
 //    ONE query row (row l%32; the two half-waves split the keys).  Row max is
@@ -41,7 +45,8 @@
 //    crossing the diagonal (or the ragged end of the sequence) are masked.
 //    Work units are issued heaviest first, and consecutive units (which the
 //    dispatcher spreads over the 8 XCDs) differ in their (batch, KV head), so
-//    each XCD's L2 keeps serving the same K/V heads.
+//    each XCD's L2 keeps serving the same K/V heads (chunked prefill orders
+//    its units by sequence instead; see work_unit).
 
 #include <atomic>
 #include <type_traits>
