@@ -42,6 +42,10 @@ SMALL = [
     # number of key tiles, a row block ending exactly on a tile edge, no mask
     (1, 4, 4, 1, 128, True), (1, 4, 1, 63, 128, True), (2, 4, 2, 128, 128, True), (1, 4, 2, 192, 128, True),
     (1, 8, 2, 511, 128, False), (1, 3, 3, 96, 128, True),
+    # d = 64 short sequences: keys only in the first half of the one tile, one and a half tiles,
+    # group 4, no mask
+    (1, 2, 2, 20, 64, True), (1, 2, 2, 20, 64, False), (1, 4, 4, 96, 64, True), (2, 8, 2, 160, 64, True),
+    (1, 4, 1, 65, 64, False),
 ]
 
 
