@@ -636,7 +636,8 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
 // behind group A: in every period one group is in its MFMA phase and the other in its VALU
 // phase, and a workgroup barrier ends each period.  Stage s of the LDS ring holds K_s and
 // V_{s-1}; both groups read it in periods 2s (A) and 2s + 1 (B), and its refill with stage
-// s + STAGES goes out at the start of period 2s + 2.
+// s + STAGES goes out at the start of period 2s + 2.  Every mask of the lock-step kernel is
+// supported, the chunked prefill over the paged cache (with its append) included.
 //
 // Split-key mode (KSPLIT): both groups take the same query rows, group A the even key tiles and
 // group B the odd ones, so a short causal sequence's longest rows walk half as many tiles per
@@ -1150,7 +1151,8 @@ hipError_t dispatch_hpw(const PrefillArgs& a, hipStream_t stream) {
   return dispatch_group<D, MASK, 4>(a, stream);
 }
 
-// Chunked prefill over a paged cache: the lock-step kernel (eight waves when the grid is large).
+// Chunked prefill over a paged cache: on large grids the ping-pong kernel at d = 128 and the
+// eight-wave lock-step kernel at d = 64; on small grids the four-wave lock-step kernel.
 template <int D>
 hipError_t dispatch_paged(const PrefillArgs& a, hipStream_t stream) {
   const int group = a.H / a.Hkv;
