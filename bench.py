@@ -31,6 +31,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -98,13 +99,21 @@ def chunked_bytes(w, ctx_lens) -> float:
     return 2.0 * (2 * T * w.H * w.d + 2 * T * w.Hkv * w.d + 2 * ctx * w.Hkv * w.d + 2 * T * w.Hkv * w.d) + 4.0 * T * w.H
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments, trailing blanks and empty lines (none of which changes a kernel)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def source_digest() -> str:
-    """Digest of every kernel source: counter figures are only valid for the sources they were taken on."""
+    """Digest of the code of every kernel source: counter figures are only valid for the code they were
+    taken on (comment edits keep them)."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        with open(p, "rb") as f:
+        with open(p, encoding="utf-8") as f:
             h.update(os.path.basename(p).encode())
-            h.update(f.read())
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
