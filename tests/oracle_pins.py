@@ -177,6 +177,90 @@ def pin_rows_equal_full():
             assert abs(rl[n] - lse[b, h, i]) < 1e-14
 
 
+# ----------------------------------------------------------------- the tiled online algorithm
+
+def _online_attention(q, k, v, causal, scale, br, bc):
+    """The tile-by-tile algorithm with a running max, a running sum and a rescaled accumulator ("Kernel
+    Fusion and Custom Kernels", section 3, FlashAttention v1/v2), written independently of the oracle:
+    query blocks of br rows, key tiles of bc keys, causal tiles wholly above a block's last row skipped.
+    Query head h reads KV head h // (H // Hkv)."""
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    o = np.zeros((B, H, N, d))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            kh, vh = k[b, h // (H // Hkv)], v[b, h // (H // Hkv)]
+            for r0 in range(0, N, br):
+                rows = np.arange(r0, min(r0 + br, N))
+                m = np.full(len(rows), -np.inf)
+                l = np.zeros(len(rows))
+                acc = np.zeros((len(rows), d))
+                for c0 in range(0, N, bc):
+                    if causal and c0 > rows[-1]:
+                        break  # this tile and every later one lie above the diagonal
+                    cols = np.arange(c0, min(c0 + bc, N))
+                    s = scale * (q[b, h, rows] @ kh[cols].T)
+                    if causal:
+                        s = np.where(cols[None, :] > rows[:, None], -np.inf, s)
+                    m_new = np.maximum(m, s.max(axis=1))
+                    # a row with no visible key yet keeps m = -inf; its factors are taken as 0
+                    alpha = np.where(np.isneginf(m_new), 0.0, np.exp(np.where(np.isneginf(m), -np.inf, m - m_new)))
+                    p = np.where(np.isneginf(s), 0.0, np.exp(s - np.where(np.isneginf(m_new), 0.0, m_new)[:, None]))
+                    l = alpha * l + p.sum(axis=1)
+                    acc = alpha[:, None] * acc + p @ vh[cols]
+                    m = m_new
+                o[b, h, rows] = acc / l[:, None]
+                lse[b, h, rows] = m + np.log(l)
+    return o, lse
+
+
+def _merge_splits(parts):
+    """Merge per-split (O_c, LSE_c) of the same rows: weights exp(LSE_c - max), splits with LSE = -inf weigh 0."""
+    lses = np.stack([p[1] for p in parts])
+    top = lses.max(axis=0)
+    w = np.where(np.isneginf(lses), 0.0, np.exp(lses - top))
+    tot = w.sum(axis=0)
+    o = sum(w[c][..., None] * parts[c][0] for c in range(len(parts))) / tot[..., None]
+    return o, top + np.log(tot)
+
+
+def pin_online_tiles_equal_plain():
+    """The online algorithm reaches the plain softmax result for any tiling ("Kernel Fusion and Custom
+    Kernels", section 3: exact, not approximate), causal and not, with grouped KV heads."""
+    q, k, v = _rand((2, 4, 37, 8), 40, 2.0), _rand((2, 2, 37, 8), 41), _rand((2, 2, 37, 8), 42)
+    for causal in (False, True):
+        ro, rl = oracle.attention(q, k, v, causal, 0.3)
+        for br, bc in ((1, 1), (3, 5), (16, 8), (8, 64), (37, 37)):
+            o, lse = _online_attention(q, k, v, causal, 0.3, br, bc)
+            assert np.allclose(o, ro, rtol=0, atol=1e-12), (causal, br, bc)
+            assert np.allclose(lse, rl, rtol=0, atol=1e-12), (causal, br, bc)
+
+
+def pin_split_key_merge_equals_plain():
+    """Cutting a sequence's pages into consecutive ranges, decoding each range on its own and merging the
+    partial (O_c, LSE_c) by weights exp(LSE_c - max) (the rescaling identity of "Kernel Fusion and Custom
+    Kernels", section 3, as the decode's reduce applies it) gives the decode over all the pages."""
+    H, Hkv, d, L = 4, 2, 8, 77  # 5 pages of 16, the last one partly used
+    n_pages = -(-L // 16)
+    q = _rand((1, H, d), 46)
+    kc, vc = _rand((n_pages, 16, Hkv, d), 47), _rand((n_pages, 16, Hkv, d), 48)
+    table = np.array([[3, 0, 4, 1, 2]])
+    full_o, full_lse = oracle.paged_decode(q, kc, vc, table, np.array([L]), 0.4)
+    for cuts in ((0, 5), (0, 1, 5), (0, 2, 3, 5), (0, 1, 2, 3, 4, 5)):
+        parts = []
+        for p0, p1 in zip(cuts[:-1], cuts[1:]):
+            n = min(L, 16 * p1) - 16 * p0  # tokens of the range
+            parts.append(oracle.paged_decode(q, kc, vc, table[:, p0:p1], np.array([n]), 0.4))
+        o, lse = _merge_splits(parts)
+        assert np.allclose(o, full_o, rtol=0, atol=1e-12), cuts
+        assert np.allclose(lse, full_lse, rtol=0, atol=1e-12), cuts
+    # a range with no visible key (LSE = -inf, output 0) weighs nothing
+    empty = (np.zeros_like(full_o), np.full_like(full_lse, -np.inf))
+    o, lse = _merge_splits([empty, (full_o, full_lse)])
+    assert np.allclose(o, full_o, rtol=0, atol=1e-15) and np.allclose(lse, full_lse, rtol=0, atol=1e-15)
+
+
 # ----------------------------------------------------------------- sliding window + global tokens
 
 def _brute_window(q, k, v, window, n_global, scale):
