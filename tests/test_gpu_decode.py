@@ -98,6 +98,29 @@ def test_decode_full_size_sampled():
     assert_close_lse(lse[seqs], rl)
 
 
+def test_decode_partition_does_not_change_results():
+    """Unused block-table columns change how many equal page ranges the decode cuts the pages into
+    (57, 120, then 256 here), so each sequence is split and merged differently; the result stays within
+    the oracle's bars and within one bf16 rounding (LSE: fp32 rounding) of the other partitions."""
+    w = DecodeWorkload("split", 3, 32, 8, 128, 250, 300, 16, 80)
+    a = decode_inputs(w, seed=23)
+    assert a["block_table"].shape[1] == 19
+    ro, rl = _oracle(a)
+    outs = []
+    for cols in (19, 40, 200):
+        b = dict(a)
+        bt = np.full((3, cols), -1, dtype=np.int32)
+        bt[:, :19] = a["block_table"]
+        b["block_table"] = bt
+        o, lse, _ = _run(b, 32)
+        assert_close_bf16(o, ro)
+        assert_close_lse(lse, rl)
+        outs.append((o, lse))
+    for o, lse in outs[1:]:
+        assert np.all(np.abs(o - outs[0][0]) <= 2.0 ** -7 * np.maximum(np.abs(o), np.abs(outs[0][0])))
+        assert np.max(np.abs(lse - outs[0][1])) <= 1e-5
+
+
 def test_decode_out_of_range_page_id_is_not_read():
     """A page id past num_pages is never dereferenced; its tokens count as absent."""
     w = DecodeWorkload("oob", 1, 4, 1, 64, 48, 48, 16, 8)
