@@ -28,6 +28,7 @@ from .exact import (  # noqa: F401
     attention_window_rows,
     paged_append,
     paged_decode,
+    paged_decode_fp8,
     paged_gather,
     paged_prefill,
     softmax_probs,

@@ -247,16 +247,40 @@ def paged_decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, seqs=
     in float64 for the sequences in ``seqs`` (default: all), in that order.
     The query of sequence s sits at position L_s - 1 and sees all L_s keys.
     """
+    return _decode_rows(q, np.asarray(k_cache).shape[2], np.asarray(v_cache).shape[3],
+                        lambda s, L: paged_gather(k_cache, v_cache, np.asarray(block_table)[s], L),
+                        seq_lens, scale, seqs)
+
+
+def paged_decode_fp8(q, k8, v8, k_scale: float, v_scale: float, block_table, seq_lens, scale: float, seqs=None):
+    """Single-query decode over an FP8 (E4M3) paged KV cache with per-tensor scales.
+
+    k8, v8 [num_pages, page_size, Hkv, d] are e4m3 bytes; the cache holds their values times k_scale and
+    v_scale (the FP8 inputs of "Kernel Fusion and Custom Kernels", section "3. FlashAttention: The
+    Milestone of Fusion", v3, stored in the paged cache of "Fast Attention Kernels and Operator Fusion",
+    section "Paged Attention Kernels").  The result is :func:`paged_decode` over those values, in float64;
+    q stays bfloat16.  Only the tokens a sequence holds are decoded.
+    """
+    def gather(s, L):
+        t = np.arange(int(L))
+        blk, slot = _page_slot(t, np.asarray(k8).shape[1])
+        pages = np.asarray(block_table)[s][blk]
+        return (e4m3_bits_to_f64(np.asarray(k8)[pages, slot]) * float(k_scale),
+                e4m3_bits_to_f64(np.asarray(v8)[pages, slot]) * float(v_scale))
+    return _decode_rows(q, np.asarray(k8).shape[2], np.asarray(v8).shape[3], gather, seq_lens, scale, seqs)
+
+
+def _decode_rows(q, Hkv: int, d_v: int, gather, seq_lens, scale: float, seqs):
+    """One query row per sequence attending over the L_s keys/values gather(s, L_s) returns."""
     q64 = _as_f64(q)
     S, H, d = q64.shape
-    Hkv = np.asarray(k_cache).shape[2]
     _check_heads(H, Hkv)
     seqs = range(S) if seqs is None else list(seqs)
-    o = np.zeros((len(seqs), H, np.asarray(v_cache).shape[3]))
+    o = np.zeros((len(seqs), H, d_v))
     lse = np.zeros((len(seqs), H))
     for n, s in enumerate(seqs):
         L = int(seq_lens[s])
-        kk, vv = paged_gather(k_cache, v_cache, np.asarray(block_table)[s], L)
+        kk, vv = gather(s, L)
         for h in range(H):
             g = _kv_head(h, H, Hkv)
             o_h, l_h = _attend(q64[s, h][None, :], kk[:, g], vv[:, g], scale, None)

@@ -631,4 +631,46 @@ def pin_fp8_scales_enter_linearly():
     assert np.allclose(o4, 2 * o, rtol=0, atol=1e-13) and np.array_equal(lse4, lse)
 
 
+def _fp8_decode_case(seed):
+    """A small FP8 paged cache: 3 sequences (one empty-tailed page each), 2 KV heads, 5 of 9 pages used."""
+    rng = np.random.default_rng(seed)
+    lens = np.array([21, 1, 30])
+    table = np.array([[4, 7], [0, -1], [8, 2]], dtype=np.int32)
+    k8 = rng.integers(0, 256, size=(9, 16, 2, 8), dtype=np.uint8)
+    v8 = rng.integers(0, 256, size=(9, 16, 2, 8), dtype=np.uint8)
+    for x in (k8, v8):  # NaN codes only where no token sits
+        x[(x & 0x7F) == 0x7F] = 0x3C
+        for s, L in enumerate(lens):
+            for t in range(L, 32):
+                if t // 16 < 2 and table[s, t // 16] >= 0:
+                    x[table[s, t // 16], t % 16] = 0x7F
+    q = _rand((3, 4, 8), seed + 1)
+    return q, k8, v8, table, lens
+
+
+def pin_fp8_decode_is_decode_of_the_values():
+    """With unit scales, FP8 decode is the bfloat16 decode of the same numbers, decoded here by torch's
+    float8_e4m3fn (every finite E4M3 value is a bfloat16); NaN codes in unused slots are never read."""
+    import torch
+    q, k8, v8, table, lens = _fp8_decode_case(50)
+    o8, l8 = oracle.paged_decode_fp8(q, k8, v8, 1.0, 1.0, table, lens, 0.7)
+    as_bf16 = lambda x: torch.from_numpy(x.copy()).view(torch.float8_e4m3fn).to(torch.bfloat16).view(torch.int16) \
+        .numpy().view(np.uint16)
+    o, l = oracle.paged_decode(q, as_bf16(k8), as_bf16(v8), table, lens, 0.7)
+    assert np.all(np.isfinite(o8)) and np.all(np.isfinite(l8))
+    assert np.allclose(o8, o, rtol=0, atol=1e-13) and np.allclose(l8, l, rtol=0, atol=1e-13)
+
+
+def pin_fp8_decode_scales_enter_linearly():
+    """k_scale multiplies every score (the same as multiplying the softmax scale); v_scale multiplies the
+    output and leaves the LSE alone."""
+    q, k8, v8, table, lens = _fp8_decode_case(51)
+    base_o, base_l = oracle.paged_decode_fp8(q, k8, v8, 1.0, 1.0, table, lens, 0.6)
+    o, l = oracle.paged_decode_fp8(q, k8, v8, 1.0, 4.0, table, lens, 0.6)
+    assert np.allclose(o, 4.0 * base_o, rtol=0, atol=1e-12) and np.allclose(l, base_l, rtol=0, atol=0)
+    o, l = oracle.paged_decode_fp8(q, k8, v8, 0.25, 1.0, table, lens, 0.6)
+    o2, l2 = oracle.paged_decode_fp8(q, k8, v8, 1.0, 1.0, table, lens, 0.15)
+    assert np.allclose(o, o2, rtol=0, atol=1e-13) and np.allclose(l, l2, rtol=0, atol=1e-13)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -82,3 +82,20 @@ def test_fp8_workload_layout():
     a = prefill_inputs(w, seed=1)
     assert a["q8"].shape == (1, 4, 48, 64) and a["k8"].shape == (1, 2, 48, 64) and a["vt8"].shape == (1, 2, 64, 48)
     assert a["q8"].dtype == np.uint8 and a["vt8"].flags["C_CONTIGUOUS"]
+
+
+def test_fp8_decode_inputs_quantize_the_bf16_draws():
+    """FP8 decode inputs hold the bf16 draws quantized per tensor (max |x| -> 448), with the E4M3 NaN code
+    in exactly the slots no token occupies."""
+    from workloads import DecodeWorkload, decode_inputs, decode_inputs_fp8, quantize_e4m3
+    w = DecodeWorkload("fp8dec", 4, 8, 2, 64, 1, 90, 16, 40)
+    a = decode_inputs(w, seed=7)
+    b = decode_inputs_fp8(w, seed=7)
+    assert np.array_equal(a["q"], b["q"]) and np.array_equal(a["block_table"], b["block_table"])
+    for name, sname in (("k_cache", "k_scale"), ("v_cache", "v_scale")):
+        x = bf16_bits_to_f32(a[name])
+        used = ~np.isnan(x)
+        assert np.array_equal(b[name][~used], np.full((~used).sum(), 0x7F, np.uint8))
+        codes, scale = quantize_e4m3(x[used])
+        assert b[sname] == scale and abs(scale * 448.0 - np.abs(x[used]).max()) <= 1e-6 * scale * 448.0
+        assert np.array_equal(b[name][used], codes)

@@ -17,5 +17,6 @@ from .generators import (  # noqa: F401
     bf16_bits_to_f32,
     prefill_inputs,
     decode_inputs,
+    decode_inputs_fp8,
     BF16_NAN,
 )

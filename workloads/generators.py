@@ -258,6 +258,25 @@ def decode_inputs(w: DecodeWorkload, seed: int = 0, poison: bool = True, seq_len
             "seq_lens": lens, "scale": w.scale, "max_pages_per_seq": max_pages}
 
 
+E4M3_NAN = np.uint8(0x7F)  # S.1111.111: the E4M3 ("fn") NaN pattern
+
+
+def decode_inputs_fp8(w: DecodeWorkload, seed: int = 0, poison: bool = True, seq_lens=None, block_table=None):
+    """FP8 (E4M3) paged-decode inputs: the draws of :func:`decode_inputs` (same order, same values),
+    with the K and V pools quantized per tensor (scale = max |x| over the stored tokens / 448, each
+    value rounded to the nearest E4M3 code, ties to even).  With ``poison`` every slot no token
+    occupies holds the E4M3 NaN code.  Q stays bfloat16; adds ``k_scale`` and ``v_scale``."""
+    a = decode_inputs(w, seed, poison=True, seq_lens=seq_lens, block_table=block_table)
+    out = dict(a)
+    for name, sname in (("k_cache", "k_scale"), ("v_cache", "v_scale")):
+        x = bf16_bits_to_f32(a[name])
+        used = ~np.isnan(x)  # drawn tokens are finite; every other slot was poisoned
+        codes, scale = quantize_e4m3(np.where(used, x, np.float32(0)))
+        codes[~used] = E4M3_NAN if poison else np.uint8(0)
+        out[name], out[sname] = codes, scale
+    return out
+
+
 def chunked_prefill_inputs(w: ChunkedPrefillWorkload, seed: int = 0, poison: bool = True, ctx_lens=None,
                            q_lens=None):
     """Chunked-prefill inputs.
