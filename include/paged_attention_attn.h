@@ -207,6 +207,27 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, c
                       hipStream_t stream);
 
 /*
+ * paged_attn_decode_fp8 — paged_attn_decode over an FP8 KV cache: k_cache and
+ * v_cache hold OCP E4M3 bytes (sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, no infinities, S.1111.111 = NaN), [num_pages, page_size, Hkv, d], and
+ * the cached keys and values are those values times k_scale and v_scale (per
+ * tensor).  This is the FP8 variant of "Kernel Fusion and Custom Kernels",
+ * section "3. FlashAttention: The Milestone of Fusion" (v3, FP8 inputs) applied
+ * to the paged cache of "Fast Attention Kernels and Operator Fusion", section
+ * "Paged Attention Kernels"; it halves the bytes the decode streams.
+ *   q, block_table, seq_lens, o, lse, workspace and every rule on them are those
+ *   of paged_attn_decode (q bf16, o bf16, the same workspace size).
+ *   k_scale, v_scale  finite and positive, else ATTN_ERR_INVALID_SCALE.
+ * Each byte is turned into bf16 exactly (every finite E4M3 value is a bf16);
+ * the scores use scale * k_scale, each partial output is multiplied by
+ * v_scale.  Slots at or past L_s may hold anything, NaN codes included.
+ */
+int paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale, float v_scale,
+                          const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse, int num_seqs,
+                          int H, int Hkv, int d, int page_size, int max_pages_per_seq, int num_pages, float scale,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The decode step as a replayable graph ("Fast Attention Kernels and
  * Operator Fusion", section "Fusion and CUDA Graphs with torch.compile": a
  * graph records a fixed sequence of GPU operations and replays it with one

@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     declared_functions,
     lib,
     paged_attn_decode,
+    paged_attn_decode_fp8,
     paged_attn_decode_workspace_size,
     paged_prefill,
 )

@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_decode_workspace_size.restype = sz
         L.paged_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
         L.paged_attn_decode.restype = i
+        L.paged_attn_decode_fp8.argtypes = [vp, vp, vp, f, f, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
+        L.paged_attn_decode_fp8.restype = i
         L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, f, vp]
         L.attn_fwd_fp8.restype = i
         L.paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
@@ -224,12 +226,13 @@ def paged_attn_decode_workspace_size(num_seqs: int, H: int, d: int, page_size: i
     return int(lib().paged_attn_decode_workspace_size(num_seqs, H, d, page_size, max_pages_per_seq))
 
 
-def _decode_args(q, k_cache, v_cache, block_table, seq_lens, scale, num_pages, workspace, out, lse):
+def _decode_args(q, k_cache, v_cache, block_table, seq_lens, scale, num_pages, workspace, out, lse,
+                 cache_dtype=torch.bfloat16):
     """Checks the decode tensors and fills in the defaults; returns the C argument list (without a stream)."""
     _require(q, "q", torch.bfloat16, 3)
     dev = q.device
-    _require(k_cache, "k_cache", torch.bfloat16, 4, dev)
-    _require(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _require(k_cache, "k_cache", cache_dtype, 4, dev)
+    _require(v_cache, "v_cache", cache_dtype, 4, dev)
     _require(block_table, "block_table", torch.int32, 2, dev)
     _require(seq_lens, "seq_lens", torch.int32, 1, dev)
     S, H, d = q.shape
@@ -268,6 +271,17 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, scale: float |
     args, _, out, lse = _decode_args(q, k_cache, v_cache, block_table, seq_lens, scale, num_pages, workspace, out,
                                      lse)
     _check(lib().paged_attn_decode(*args, _stream(q.device)))
+    return out, lse
+
+
+def paged_attn_decode_fp8(q, k_cache, v_cache, block_table, seq_lens, k_scale: float, v_scale: float,
+                          scale: float | None = None, num_pages=None, workspace=None, out=None, lse=None):
+    """Paged decode over an FP8 cache: caches [P,16,Hkv,d] uint8 holding E4M3 codes of the keys / values divided
+    by k_scale / v_scale; q, block_table, seq_lens, workspace, out and lse as in :func:`paged_attn_decode`."""
+    args, _, out, lse = _decode_args(q, k_cache, v_cache, block_table, seq_lens, scale, num_pages, workspace, out,
+                                     lse, cache_dtype=torch.uint8)
+    args = args[:3] + [float(k_scale), float(v_scale)] + args[3:]
+    _check(lib().paged_attn_decode_fp8(*args, _stream(q.device)))
     return out, lse
 
 

@@ -132,16 +132,19 @@ size_t paged_attn_decode_workspace_size(int num_seqs, int H, int d, int page_siz
   return w.total();
 }
 
-int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
-                      const int32_t* seq_lens, void* o, float* lse, int num_seqs, int H, int Hkv, int d, int page_size,
-                      int max_pages_per_seq, int num_pages, float scale, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream) {
+namespace {
+
+// Both decode entry points: the bf16 cache, or (fp8) an E4M3 cache with per-tensor scales.
+int decode_call(const void* q, const void* k_cache, const void* v_cache, bool fp8, float k_scale, float v_scale,
+                const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse, int num_seqs, int H, int Hkv,
+                int d, int page_size, int max_pages_per_seq, int num_pages, float scale, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
   if (num_seqs < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || max_pages_per_seq < 0 || num_pages < 0)
     return ATTN_ERR_INVALID_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
   if (page_size != 16) return ATTN_ERR_UNSUPPORTED_PAGE_SIZE;
   if (H / Hkv > 16) return ATTN_ERR_UNSUPPORTED_GROUP;
-  if (!scale_ok(scale)) return ATTN_ERR_INVALID_SCALE;
+  if (!scale_ok(scale) || (fp8 && (!scale_ok(k_scale) || !scale_ok(v_scale)))) return ATTN_ERR_INVALID_SCALE;
   if (num_seqs == 0) return ATTN_OK;  // empty call: nothing is read or written
   // block_table may be NULL only when it has no columns (then it is never read)
   if (!q || !k_cache || !v_cache || (!block_table && max_pages_per_seq > 0) || !seq_lens || !o || !workspace)
@@ -164,9 +167,27 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, c
   float* ws_o = reinterpret_cast<float*>(base);
   float* ws_lse = reinterpret_cast<float*>(base + w.o_bytes);
   int* ws_range = reinterpret_cast<int*>(base + w.o_bytes + w.lse_bytes);
-  return launch_status(paa::paged_decode_bf16(q, k_cache, v_cache, block_table, seq_lens, o, lse, num_seqs, H, Hkv, d,
-                                              max_pages_per_seq, num_pages, scale, ws_o, ws_lse, ws_range, parts,
-                                              (int)w.slots, stream));
+  return launch_status(paa::paged_decode(q, k_cache, v_cache, fp8, k_scale, v_scale, block_table, seq_lens, o, lse,
+                                         num_seqs, H, Hkv, d, max_pages_per_seq, num_pages, scale, ws_o, ws_lse,
+                                         ws_range, parts, (int)w.slots, stream));
+}
+
+}  // namespace
+
+int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                      const int32_t* seq_lens, void* o, float* lse, int num_seqs, int H, int Hkv, int d, int page_size,
+                      int max_pages_per_seq, int num_pages, float scale, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  return decode_call(q, k_cache, v_cache, false, 1.f, 1.f, block_table, seq_lens, o, lse, num_seqs, H, Hkv, d,
+                     page_size, max_pages_per_seq, num_pages, scale, workspace, workspace_bytes, stream);
+}
+
+int paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale, float v_scale,
+                          const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse, int num_seqs,
+                          int H, int Hkv, int d, int page_size, int max_pages_per_seq, int num_pages, float scale,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_call(q, k_cache, v_cache, true, k_scale, v_scale, block_table, seq_lens, o, lse, num_seqs, H, Hkv, d,
+                     page_size, max_pages_per_seq, num_pages, scale, workspace, workspace_bytes, stream);
 }
 
 // ---- the decode step as a replayable hipGraph ----

@@ -32,9 +32,10 @@ int decode_max_parts(int H);
 hipError_t decode_setup(int d);
 int decode_parts(int num_seqs, int H, int Hkv, int max_pages_per_seq);
 
-hipError_t paged_decode_bf16(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
-                             const int* seq_lens, void* o, float* lse, int num_seqs, int H, int Hkv, int d,
-                             int max_pages_per_seq, int num_pages, float scale, float* ws_o, float* ws_lse,
-                             int* ws_range, int parts, int slots, hipStream_t stream);
+// Decode over a bf16 cache, or (fp8) over an E4M3 cache holding its values divided by k_scale, v_scale.
+hipError_t paged_decode(const void* q, const void* k_cache, const void* v_cache, bool fp8, float k_scale,
+                        float v_scale, const int* block_table, const int* seq_lens, void* o, float* lse, int num_seqs,
+                        int H, int Hkv, int d, int max_pages_per_seq, int num_pages, float scale, float* ws_o,
+                        float* ws_lse, int* ws_range, int parts, int slots, hipStream_t stream);
 
 }  // namespace paa

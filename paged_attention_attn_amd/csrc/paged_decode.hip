@@ -38,6 +38,8 @@
 // the tests) never reaches the result.  A page id outside [0, num_pages) is
 // never dereferenced: its tokens count as masked.
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -59,8 +61,8 @@ struct DecodeLds {
 
 struct DecodeArgs {
   const uint16_t* q;
-  const uint16_t* kc;
-  const uint16_t* vc;
+  const void* kc;  // bf16, or E4M3 bytes for the FP8 cache
+  const void* vc;
   const int* bt;
   const int* lens;
   float* ws_o;     // [slots, H, D] partial outputs (normalised)
@@ -69,7 +71,8 @@ struct DecodeArgs {
   uint16_t* o;
   float* lse;
   int S, H, Hkv, group, max_pages, num_pages, parts, slots, waves;
-  float scale, scale_log2;
+  float scale, scale_log2;  // the softmax scale (times k_scale for the FP8 cache)
+  float vscale;             // factor on the output: v_scale for the FP8 cache, 1 otherwise
 };
 
 __device__ __forceinline__ int seq_len_clamped(const DecodeArgs& a, int s) {
@@ -153,12 +156,33 @@ struct Walker {
   }
 };
 
-template <int D>
+// Two E4M3 bytes (the low or high half of w, lower byte first) -> two bf16, exactly (every finite
+// E4M3 value is a bf16).
+template <bool HIGH>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH));
+}
+
+// Eight E4M3 bytes -> eight bf16 (an MFMA operand), in byte order.
+__device__ __forceinline__ u32x4_t e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  return u32x4_t{e4m3x2_to_bf16x2<false>(lo), e4m3x2_to_bf16x2<true>(lo), e4m3x2_to_bf16x2<false>(hi),
+                 e4m3x2_to_bf16x2<true>(hi)};
+}
+
+template <int D, bool FP8>
 __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeArgs a) {
   constexpr int kKSteps = D / 32;          // 16x16x32 k-steps over d for the scores
   constexpr int kDBlocks = D / 16;         // 16-wide d blocks of the output
-  constexpr int kChunksPerRow = D / 8;     // 16-byte chunks per V row
-  constexpr int kVChunks = kPage * kChunksPerRow / 64;  // per lane per page
+  constexpr int kChunksPerRow = D / 8;     // 16-byte bf16 chunks per V row in LDS
+  // the cache as loaded: bf16, or E4M3 bytes (8 bytes of a K row per k-step, V rows in 16-byte
+  // chunks of 16 values), turned into bf16 only when the step is computed
+  using CacheT = std::conditional_t<FP8, uint8_t, uint16_t>;
+  using KRaw = std::conditional_t<FP8, u32x2_t, u32x4_t>;
+  constexpr int kRawPerRow = FP8 ? D / 16 : kChunksPerRow;  // 16-byte loads per V row
+  constexpr int kVRaw = kPage * kRawPerRow / 64;            // per lane per page
+  static_assert(kPage * kRawPerRow % 64 == 0, "V loads split evenly over the lanes");
+  const CacheT* kc = (const CacheT*)a.kc;
+  const CacheT* vc = (const CacheT*)a.vc;
   using Lds = DecodeLds<D>;
 
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_raw[];
@@ -252,11 +276,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeAr
     return __builtin_amdgcn_readlane(bt_vec, lp - bt_base);
   };
 
-  u32x4_t kf[2][kKSteps], vr[2][kVChunks], qf[kKSteps];
-  u32x4_t kn[2][kKSteps], vn[2][kVChunks], qn[kKSteps];
+  KRaw kf[2][kKSteps], kn[2][kKSteps];
+  u32x4_t vr[2][kVRaw], vn[2][kVRaw], qf[kKSteps], qn[kKSteps];
 
   // loads of one step into (k, v, q): K in the MFMA A layout, V rows as 16-byte chunks
-  auto issue = [&](Step& st, u32x4_t (&k)[2][kKSteps], u32x4_t (&v)[2][kVChunks], u32x4_t (&qq)[kKSteps]) {
+  auto issue = [&](Step& st, KRaw (&k)[2][kKSteps], u32x4_t (&v)[2][kVRaw], u32x4_t (&qq)[kKSteps]) {
     if (st.first) {
 #pragma unroll
       for (int t = 0; t < kKSteps; ++t)
@@ -269,16 +293,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeAr
       const int pid = pp < st.np ? page_id(st, pp) : -1;
       st.pid[pp] = pid;
       const bool ok = pid >= 0 && pid < a.num_pages;
-      const uint16_t* kpage = a.kc + (size_t)(ok ? pid : 0) * kPage * tok_stride + (size_t)g * D;
-      const uint16_t* vpage = a.vc + (size_t)(ok ? pid : 0) * kPage * tok_stride + (size_t)g * D;
+      const CacheT* kpage = kc + (size_t)(ok ? pid : 0) * kPage * tok_stride + (size_t)g * D;
+      const CacheT* vpage = vc + (size_t)(ok ? pid : 0) * kPage * tok_stride + (size_t)g * D;
 #pragma unroll
       for (int t = 0; t < kKSteps; ++t)
-        k[pp][t] = ok ? *(const u32x4_t*)(kpage + r16 * tok_stride + 32 * t + 8 * c16) : u32x4_t{0, 0, 0, 0};
+        k[pp][t] = ok ? *(const KRaw*)(kpage + r16 * tok_stride + 32 * t + 8 * c16) : KRaw{};
 #pragma unroll
-      for (int i = 0; i < kVChunks; ++i) {
+      for (int i = 0; i < kVRaw; ++i) {
         const int c = lane + 64 * i;
-        const int row = c / kChunksPerRow;
-        const int col = (c % kChunksPerRow) * 8;
+        const int row = c / kRawPerRow;
+        const int col = (c % kRawPerRow) * (FP8 ? 16 : 8);
         v[pp][i] = (ok && tp + row < st.L) ? *(const u32x4_t*)(vpage + row * tok_stride + col)
                                            : u32x4_t{0, 0, 0, 0};
       }
@@ -309,11 +333,18 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeAr
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-      for (int i = 0; i < kVChunks; ++i) {
+      for (int i = 0; i < kVRaw; ++i) {
         const int c = lane + 64 * i;
-        const int row = c / kChunksPerRow;
-        const int col = (c % kChunksPerRow) * 8;
-        *(PAA_LDS u32x4_t*)(vl + (kPage * pp + row) * Lds::kStrideV + col) = vr[pp][i];
+        const int row = c / kRawPerRow;
+        PAA_LDS uint16_t* dst = vl + (kPage * pp + row) * Lds::kStrideV;
+        if constexpr (FP8) {  // 16 values -> two 16-byte bf16 chunks
+          const u32x4_t w = vr[pp][i];
+          const int col = (c % kRawPerRow) * 16;
+          *(PAA_LDS u32x4_t*)(dst + col) = e4m3x8_to_bf16x8(w[0], w[1]);
+          *(PAA_LDS u32x4_t*)(dst + col + 8) = e4m3x8_to_bf16x8(w[2], w[3]);
+        } else {
+          *(PAA_LDS u32x4_t*)(dst + (c % kRawPerRow) * 8) = vr[pp][i];
+        }
       }
 
     // scores S[token][head]: lane holds tokens 4*c16 + i of each page, head r16
@@ -322,7 +353,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeAr
     for (int pp = 0; pp < 2; ++pp) {
       sc[pp] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < kKSteps; ++t) sc[pp] = mfma16x16x32(kf[pp][t], qf[t], sc[pp]);
+      for (int t = 0; t < kKSteps; ++t) {
+        u32x4_t kb;
+        if constexpr (FP8)
+          kb = e4m3x8_to_bf16x8(kf[pp][t][0], kf[pp][t][1]);
+        else
+          kb = kf[pp][t];
+        sc[pp] = mfma16x16x32(kb, qf[t], sc[pp]);
+      }
     }
     // mask slots at or past the end, pages outside the step and pages that were not read
     float tmax = -INFINITY;
@@ -383,7 +421,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeAr
       const int slot = cur.s + blockIdx.x;
       if (head_ok) {
         // a segment whose pages were all rejected has no visible key: zero output, LSE = -inf
-        const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const float inv_l = l_tot > 0.f ? a.vscale / l_tot : 0.f;
         const size_t base = (size_t)slot * a.H + head;
         float* wo = a.ws_o + base * D;
 #pragma unroll
@@ -405,7 +443,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeAr
 #pragma unroll
       for (int t = 0; t < kKSteps; ++t) kf[pp][t] = kn[pp][t];
 #pragma unroll
-      for (int i = 0; i < kVChunks; ++i) vr[pp][i] = vn[pp][i];
+      for (int i = 0; i < kVRaw; ++i) vr[pp][i] = vn[pp][i];
     }
     if (cur.first) {
 #pragma unroll
@@ -543,22 +581,22 @@ int waves_for(int Hkv) {
 
 // Raise the partial kernel's dynamic LDS limit to the largest slice, once per process
 // (thread-safe static initialisation).
-template <int D>
+template <int D, bool FP8>
 hipError_t setup_decode() {
-  static const hipError_t attr = hipFuncSetAttribute((const void*)decode_partial_kernel<D>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)decode_partial_kernel<D, FP8>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      kMaxWaves * DecodeLds<D>::kPerWave * 2);
   return attr;
 }
 
-template <int D>
+template <int D, bool FP8>
 hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {
   a.waves = waves_for(a.Hkv);
   const int lds_bytes = a.waves * DecodeLds<D>::kPerWave * 2;
-  const hipError_t attr = setup_decode<D>();
+  const hipError_t attr = setup_decode<D, FP8>();
   if (attr != hipSuccess) return attr;
   dim3 grid1((unsigned)a.parts, (unsigned)(a.Hkv / a.waves));
-  hipLaunchKernelGGL(decode_partial_kernel<D>, grid1, dim3(64 * a.waves), lds_bytes, stream, a);
+  hipLaunchKernelGGL((decode_partial_kernel<D, FP8>), grid1, dim3(64 * a.waves), lds_bytes, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long rows = (long long)a.S * a.H;
@@ -572,7 +610,7 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t decode_setup(int d) { return d == 64 ? setup_decode<64>() : setup_decode<128>(); }
+hipError_t decode_setup(int d) { return d == 64 ? setup_decode<64, false>() : setup_decode<128, false>(); }
 
 int decode_max_parts(int H) {
   // Hkv >= H / 16 (at most 16 query heads per KV head), so kTargetWaves / Hkv <= 16 * kTargetWaves / H
@@ -588,14 +626,14 @@ int decode_parts(int num_seqs, int H, int Hkv, int max_pages_per_seq) {
   return p < 1 ? 1 : (int)p;
 }
 
-hipError_t paged_decode_bf16(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
-                             const int* seq_lens, void* o, float* lse, int num_seqs, int H, int Hkv, int d,
-                             int max_pages_per_seq, int num_pages, float scale, float* ws_o, float* ws_lse,
-                             int* ws_range, int parts, int slots, hipStream_t stream) {
+hipError_t paged_decode(const void* q, const void* k_cache, const void* v_cache, bool fp8, float k_scale,
+                        float v_scale, const int* block_table, const int* seq_lens, void* o, float* lse, int num_seqs,
+                        int H, int Hkv, int d, int max_pages_per_seq, int num_pages, float scale, float* ws_o,
+                        float* ws_lse, int* ws_range, int parts, int slots, hipStream_t stream) {
   DecodeArgs a{};
   a.q = (const uint16_t*)q;
-  a.kc = (const uint16_t*)k_cache;
-  a.vc = (const uint16_t*)v_cache;
+  a.kc = k_cache;
+  a.vc = v_cache;
   a.bt = block_table;
   a.lens = seq_lens;
   a.ws_o = ws_o;
@@ -611,10 +649,13 @@ hipError_t paged_decode_bf16(const void* q, const void* k_cache, const void* v_c
   a.num_pages = num_pages;
   a.parts = parts;
   a.slots = slots;
-  a.scale = scale;
-  a.scale_log2 = scale * kLog2e;
-  if (d == 64) return launch_decode<64>(a, stream);
-  return launch_decode<128>(a, stream);
+  // the FP8 cache holds its values divided by k_scale and v_scale: k_scale joins the softmax scale,
+  // v_scale multiplies each partial output (the LSE does not depend on it)
+  a.scale = fp8 ? scale * k_scale : scale;
+  a.scale_log2 = a.scale * kLog2e;
+  a.vscale = fp8 ? v_scale : 1.f;
+  if (fp8) return d == 64 ? launch_decode<64, true>(a, stream) : launch_decode<128, true>(a, stream);
+  return d == 64 ? launch_decode<64, false>(a, stream) : launch_decode<128, false>(a, stream);
 }
 
 }  // namespace paa

@@ -26,7 +26,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = paa.declared_functions()
     assert set(names) == {"attn_fwd", "attn_fwd_f32", "attn_fwd_fp8", "attn_fwd_window", "paged_attn_decode_workspace_size", "paged_prefill",
-                          "paged_attn_decode", "paged_attn_decode_graph_create", "paged_attn_decode_graph_launch",
+                          "paged_attn_decode", "paged_attn_decode_fp8", "paged_attn_decode_graph_create",
+                          "paged_attn_decode_graph_launch",
                           "paged_attn_decode_graph_destroy", "attn_status_string"}
     for n in names:
         assert hasattr(L, n), n
@@ -93,6 +94,29 @@ def test_decode_validation(L):
     assert call(scale=float("nan")) == SCALE
     assert call(S=0) == ATTN_OK
     assert call(S=0, q=None, ws=None) == ATTN_OK  # empty: pointers unused
+
+
+def test_decode_fp8_validation(L):
+    """The FP8 decode checks what the bf16 decode checks, plus both cache scales (no GPU needed)."""
+    ws = paa.paged_attn_decode_workspace_size(4, 8, 128, 16, 10)
+    base = dict(q=P, kc=P, vc=P, ks=0.5, vs=0.25, bt=P, lens=P, o=P, lse=None, S=4, H=8, Hkv=2, d=128, ps=16,
+                mp=10, np_=100, scale=0.1, ws=P, wsb=ws)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.paged_attn_decode_fp8(a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["bt"], a["lens"], a["o"],
+                                       a["lse"], a["S"], a["H"], a["Hkv"], a["d"], a["ps"], a["mp"], a["np_"],
+                                       a["scale"], a["ws"], a["wsb"], None)
+
+    assert call(kc=None) == NULL
+    assert call(Hkv=3) == SHAPE
+    assert call(d=96) == HEAD_DIM
+    assert call(ps=8) == PAGE
+    assert call(wsb=ws - 1) == WS
+    assert call(vc=ctypes.c_void_p(0x10008)) == ALIGN
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert call(ks=bad) == SCALE and call(vs=bad) == SCALE
+    assert call(S=0) == ATTN_OK
 
 
 def test_decode_graph_validation(L):

@@ -1,0 +1,99 @@
+"""GPU parity of paged_attn_decode_fp8 (through the C ABI) against the float64 oracle."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_attention_attn_amd as paa
+from gpu_util import assert_close_bf16, assert_close_lse, dev_bf16, dev_i32, host_f64
+from workloads import WORKLOADS, DecodeWorkload, decode_inputs_fp8
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"[gpu] {msg}", file=sys.stderr, flush=True)
+
+
+def _dev_u8(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda:0")
+
+
+def _run(a, H):
+    lse = torch.empty((a["q"].shape[0], H), dtype=torch.float32, device="cuda:0")
+    o, _ = paa.paged_attn_decode_fp8(dev_bf16(a["q"]), _dev_u8(a["k_cache"]), _dev_u8(a["v_cache"]),
+                                     dev_i32(a["block_table"]), dev_i32(a["seq_lens"]), a["k_scale"], a["v_scale"],
+                                     a["scale"], lse=lse)
+    torch.cuda.synchronize()
+    return host_f64(o), lse.cpu().numpy().astype(np.float64), o
+
+
+def _oracle(a, seqs=None):
+    return oracle.paged_decode_fp8(a["q"], a["k_cache"], a["v_cache"], a["k_scale"], a["v_scale"],
+                                   a["block_table"], a["seq_lens"], a["scale"], seqs=seqs)
+
+
+@pytest.mark.parametrize("d,H,Hkv", [(128, 32, 8), (64, 8, 8), (128, 16, 1), (64, 6, 2)])
+def test_fp8_decode_small_ragged_lengths(d, H, Hkv):
+    """Lengths 0, 1, page edges and ragged tails; every unused slot holds the E4M3 NaN code."""
+    lens = [0, 1, 15, 16, 17, 100, 255, 300]
+    w = DecodeWorkload("fp8small", len(lens), H, Hkv, d, 1, 300, 16, 200)
+    _announce(f"fp8 decode d{d} H{H} Hkv{Hkv}")
+    a = decode_inputs_fp8(w, seed=d + H + Hkv, seq_lens=lens)
+    o, lse, _ = _run(a, H)
+    ro, rl = _oracle(a)
+    empty = np.asarray(lens) == 0
+    assert np.all(o[empty] == 0) and np.all(np.isneginf(lse[empty]))
+    assert_close_bf16(o[~empty], ro[~empty])
+    assert_close_lse(lse[~empty], rl[~empty])
+
+
+def test_fp8_decode_full_size_sampled():
+    """64 sequences, H=32, Hkv=8, d=128, lengths in [512, 8192], 40000-page pool, E4M3 cache: 16 sequences
+    against the oracle."""
+    w = WORKLOADS["paged_decode_s64h32kv8d128"]
+    _announce("fp8 " + w.name)
+    a = decode_inputs_fp8(w, seed=0)
+    o, lse, _ = _run(a, w.H)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    lens = a["seq_lens"]
+    seqs = sorted(set([int(np.argmin(lens)), int(np.argmax(lens))] +
+                      list(np.random.default_rng(5).choice(64, 14, replace=False))))
+    ro, rl = _oracle(a, seqs)
+    assert_close_bf16(o[seqs], ro)
+    assert_close_lse(lse[seqs], rl)
+
+
+def test_fp8_decode_matches_bf16_decode_of_the_same_values():
+    """With unit scales the FP8 decode turns each code into the bf16 value the bf16 decode reads from a bf16
+    cache holding the same numbers, and then computes the same way: outputs and LSE are bitwise equal."""
+    w = DecodeWorkload("fp8eq", 5, 32, 8, 128, 1, 700, 16, 300)
+    a = decode_inputs_fp8(w, seed=31)
+    a["k_scale"] = a["v_scale"] = 1.0
+    _, _, o8 = _run(a, 32)
+    lse8 = torch.empty((5, 32), dtype=torch.float32, device="cuda:0")
+    paa.paged_attn_decode_fp8(dev_bf16(a["q"]), _dev_u8(a["k_cache"]), _dev_u8(a["v_cache"]),
+                              dev_i32(a["block_table"]), dev_i32(a["seq_lens"]), 1.0, 1.0, a["scale"], lse=lse8)
+    as_bf16 = lambda x: torch.from_numpy(x.copy()).view(torch.float8_e4m3fn).to(torch.bfloat16).to("cuda:0")
+    lse16 = torch.empty((5, 32), dtype=torch.float32, device="cuda:0")
+    o16, _ = paa.paged_attn_decode(dev_bf16(a["q"]), as_bf16(a["k_cache"]), as_bf16(a["v_cache"]),
+                                   dev_i32(a["block_table"]), dev_i32(a["seq_lens"]), a["scale"], lse=lse16)
+    torch.cuda.synchronize()
+    assert torch.equal(o8.view(torch.int16), o16.view(torch.int16))
+    assert torch.equal(lse8.view(torch.int32), lse16.view(torch.int32))
+
+
+def test_fp8_decode_argument_errors():
+    q = torch.zeros((2, 4, 128), dtype=torch.bfloat16, device="cuda:0")
+    kc = torch.zeros((4, 16, 1, 128), dtype=torch.uint8, device="cuda:0")
+    bt = torch.zeros((2, 2), dtype=torch.int32, device="cuda:0")
+    lens = torch.ones((2,), dtype=torch.int32, device="cuda:0")
+    with pytest.raises(RuntimeError, match="scale"):
+        paa.paged_attn_decode_fp8(q, kc, kc, bt, lens, 0.0, 1.0)
+    with pytest.raises(TypeError):
+        paa.paged_attn_decode_fp8(q, kc.to(torch.bfloat16), kc.to(torch.bfloat16), bt, lens, 1.0, 1.0)
