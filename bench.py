@@ -55,6 +55,7 @@ PMC_CALLS = 3              # calls of each workload in a counter pass
 PREFILL_DEFAULT = "causal_b4h16n1024d64"
 SMALL_DECODE = "paged_decode_s4h32kv8d128_short"  # launch-bound: eager calls against graph replays
 FP8_MORE = ("fp8_causal_gqa_b2h32kv8n4096d128", "fp8_causal_gqa_long_b1h32kv8n16384d128")
+FP8_DECODE_SUFFIX = "_fp8kv"  # the decode workload over an E4M3 cache
 CHUNKED = "chunked_prefill_s16h32kv8d128_ctx0to4096_q512"  # chunked prefill over a paged cache, with append
 GRAPH_LAYERS = 32
 PREWARM_S = 0.25  # untimed calls of the step before its W warm-up steps (see prewarm)  # decode calls per step in that comparison, each with its own KV cache
@@ -76,10 +77,11 @@ def prefill_bytes(w) -> float:
     return el * (w.B * w.H * w.N * w.d * 2 + w.B * w.Hkv * w.N * w.d * 2) + 4 * w.B * w.H * w.N
 
 
-def decode_bytes(w, lens) -> float:
-    """K and V of the valid tokens, Q, O, LSE, the block-table entries used and the lengths."""
+def decode_bytes(w, lens, kv_bytes: int = 2) -> float:
+    """K and V of the valid tokens (kv_bytes per element: 2 for bf16, 1 for E4M3), Q, O, LSE, the block-table
+    entries used and the lengths."""
     lens = np.asarray(lens, dtype=np.int64)
-    kv = float(lens.sum()) * w.Hkv * w.d * 2 * 2
+    kv = float(lens.sum()) * w.Hkv * w.d * kv_bytes * 2
     qo = 2.0 * len(lens) * w.H * w.d * 2
     return kv + qo + 4.0 * len(lens) * w.H + 4.0 * float((-(-lens // w.page_size)).sum()) + 4.0 * len(lens)
 
@@ -232,6 +234,30 @@ class DecodeCase:
     def __call__(self):
         self.paa.paged_attn_decode(self.q, self.kc, self.vc, self.bt, self.lens, self.a["scale"],
                                    workspace=self.ws, out=self.o, lse=self.lse)
+
+
+class Fp8DecodeCase:
+    """The decode workload with its K/V cache held as E4M3 bytes and per-tensor scales."""
+
+    def __init__(self, torch, paa, w, seed):
+        from workloads import decode_inputs_fp8
+        self.w = w
+        self.name = w.name + FP8_DECODE_SUFFIX
+        self.a = a = decode_inputs_fp8(w, seed=seed)
+        self.q = to_dev_bf16(torch, a["q"])
+        self.kc, self.vc = torch.from_numpy(a["k_cache"]).to("cuda:0"), torch.from_numpy(a["v_cache"]).to("cuda:0")
+        self.bt, self.lens = to_dev_i32(torch, a["block_table"]), to_dev_i32(torch, a["seq_lens"])
+        self.ws = torch.zeros(paa.paged_attn_decode_workspace_size(w.num_seqs, w.H, w.d, w.page_size,
+                                                                   w.max_pages_per_seq),
+                              dtype=torch.uint8, device="cuda:0")
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((w.num_seqs, w.H), dtype=torch.float32, device="cuda:0")
+        self.paa = paa
+
+    def __call__(self):
+        a = self.a
+        self.paa.paged_attn_decode_fp8(self.q, self.kc, self.vc, self.bt, self.lens, a["k_scale"], a["v_scale"],
+                                       a["scale"], workspace=self.ws, out=self.o, lse=self.lse)
 
 
 class Fp8Case:
@@ -456,6 +482,21 @@ def run_bench(args, torch, paa) -> dict:
             del c
             _log(f"{name}: {mean:.4f} ms, {tf:.1f} TFLOP/s")
 
+    fp8_decode = None
+    if not args.no_more:
+        c = Fp8DecodeCase(torch, paa, dw, args.seed)
+        phases.start(f"decode {c.name}")
+        med, mean = timed(torch, c, 50, 5)
+        fb = decode_bytes(dw, c.a["seq_lens"], kv_bytes=1)
+        gbs = fb / (mean * 1e-3) / 1e9
+        fp8_decode = {"workload": c.name, "ms": round(mean, 5), "ms_median": round(med, 5), "value": round(gbs, 2),
+                      "unit": "GB/s", "dtype": "e4m3 K/V cache, bf16 q and out", "algorithmic_gb": round(fb / 1e9, 5),
+                      "tokens_per_s": round(float(c.a["seq_lens"].sum()) / (mean * 1e-3)),
+                      "speedup_vs_bf16_cache": round(dec_ms / mean, 3),
+                      "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", read_traffic(c.name))}
+        del c
+        _log(f"{fp8_decode['workload']}: {mean:.4f} ms, {gbs:.1f} GB/s")
+
     base = None
     if not args.no_cpu_baseline:
         base = cpu_baseline(pc, dc)
@@ -493,6 +534,7 @@ def run_bench(args, torch, paa) -> dict:
         "prefill_more": more,
         "chunked_prefill": chunked,
         "fp8_prefill": fp8,
+        "fp8_decode": fp8_decode,
         "decode_graph": small,
         "cpu_baseline": base,
         "phases": phases.names,
@@ -516,8 +558,9 @@ def run_pmc_pass(args, torch, paa) -> dict:
     cases += [PrefillCase(torch, paa, WORKLOADS[n], args.seed) for n in PREFILL_MORE]
     cases.append(ChunkedCase(torch, paa, WORKLOADS[CHUNKED], args.seed))
     cases += [Fp8Case(torch, paa, WORKLOADS[n], args.seed) for n in FP8_MORE]
+    cases.append(Fp8DecodeCase(torch, paa, WORKLOADS[args.decode_workload], args.seed))
     for c in cases:
-        phases.start(c.w.name)
+        phases.start(getattr(c, "name", c.w.name))
         for _ in range(PMC_CALLS):
             c()
     torch.cuda.synchronize()
