@@ -177,7 +177,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeAr
   // the cache as loaded: bf16, or E4M3 bytes (8 bytes of a K row per k-step, V rows in 16-byte
   // chunks of 16 values), turned into bf16 only when the step is computed
   using CacheT = std::conditional_t<FP8, uint8_t, uint16_t>;
-  using KRaw = std::conditional_t<FP8, u32x2_t, u32x4_t>;
+  // K loads: bf16, 16 bytes (8 values) per lane per k-step; E4M3, 16 bytes (16 values) per lane per
+  // two k-steps.  For the E4M3 cache the contraction over d is taken in a permuted order, the same
+  // for K and q: k-step 2u + v, lane group c16 covers d = 16*c16 + 64*u + 8*v .. +7, so one load
+  // fills two k-steps and each instruction reads 64 contiguous bytes of each of 16 rows.
+  using KRaw = u32x4_t;
+  constexpr int kKLoads = FP8 ? kKSteps / 2 : kKSteps;
   constexpr int kRawPerRow = FP8 ? D / 16 : kChunksPerRow;  // 16-byte loads per V row
   constexpr int kVRaw = kPage * kRawPerRow / 64;            // per lane per page
   static_assert(kPage * kRawPerRow % 64 == 0, "V loads split evenly over the lanes");
@@ -276,15 +281,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeAr
     return __builtin_amdgcn_readlane(bt_vec, lp - bt_base);
   };
 
-  KRaw kf[2][kKSteps], kn[2][kKSteps];
+  KRaw kf[2][kKLoads], kn[2][kKLoads];
   u32x4_t vr[2][kVRaw], vn[2][kVRaw], qf[kKSteps], qn[kKSteps];
 
   // loads of one step into (k, v, q): K in the MFMA A layout, V rows as 16-byte chunks
-  auto issue = [&](Step& st, KRaw (&k)[2][kKSteps], u32x4_t (&v)[2][kVRaw], u32x4_t (&qq)[kKSteps]) {
+  auto issue = [&](Step& st, KRaw (&k)[2][kKLoads], u32x4_t (&v)[2][kVRaw], u32x4_t (&qq)[kKSteps]) {
     if (st.first) {
 #pragma unroll
       for (int t = 0; t < kKSteps; ++t)
-        qq[t] = head_ok ? *(const u32x4_t*)(a.q + ((size_t)st.s * a.H + head) * D + 32 * t + 8 * c16)
+        qq[t] = head_ok ? *(const u32x4_t*)(a.q + ((size_t)st.s * a.H + head) * D +
+                                            (FP8 ? 16 * c16 + 64 * (t / 2) + 8 * (t % 2) : 32 * t + 8 * c16))
                         : u32x4_t{0, 0, 0, 0};
     }
 #pragma unroll
@@ -296,8 +302,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeAr
       const CacheT* kpage = kc + (size_t)(ok ? pid : 0) * kPage * tok_stride + (size_t)g * D;
       const CacheT* vpage = vc + (size_t)(ok ? pid : 0) * kPage * tok_stride + (size_t)g * D;
 #pragma unroll
-      for (int t = 0; t < kKSteps; ++t)
-        k[pp][t] = ok ? *(const KRaw*)(kpage + r16 * tok_stride + 32 * t + 8 * c16) : KRaw{};
+      for (int t = 0; t < kKLoads; ++t)
+        k[pp][t] = ok ? *(const KRaw*)(kpage + r16 * tok_stride + (FP8 ? 16 * c16 + 64 * t : 32 * t + 8 * c16))
+                      : KRaw{};
 #pragma unroll
       for (int i = 0; i < kVRaw; ++i) {
         const int c = lane + 64 * i;
@@ -356,7 +363,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeAr
       for (int t = 0; t < kKSteps; ++t) {
         u32x4_t kb;
         if constexpr (FP8)
-          kb = e4m3x8_to_bf16x8(kf[pp][t][0], kf[pp][t][1]);
+          kb = e4m3x8_to_bf16x8(kf[pp][t / 2][2 * (t % 2)], kf[pp][t / 2][2 * (t % 2) + 1]);
         else
           kb = kf[pp][t];
         sc[pp] = mfma16x16x32(kb, qf[t], sc[pp]);
@@ -441,7 +448,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeAr
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
 #pragma unroll
-      for (int t = 0; t < kKSteps; ++t) kf[pp][t] = kn[pp][t];
+      for (int t = 0; t < kKLoads; ++t) kf[pp][t] = kn[pp][t];
 #pragma unroll
       for (int i = 0; i < kVRaw; ++i) vr[pp][i] = vn[pp][i];
     }

@@ -71,21 +71,24 @@ def test_fp8_decode_full_size_sampled():
 
 def test_fp8_decode_matches_bf16_decode_of_the_same_values():
     """With unit scales the FP8 decode turns each code into the bf16 value the bf16 decode reads from a bf16
-    cache holding the same numbers, and then computes the same way: outputs and LSE are bitwise equal."""
+    cache holding the same numbers; only the order of the sum over d in the scores differs, so outputs agree
+    within one bf16 rounding and LSEs within fp32 rounding."""
     w = DecodeWorkload("fp8eq", 5, 32, 8, 128, 1, 700, 16, 300)
     a = decode_inputs_fp8(w, seed=31)
-    a["k_scale"] = a["v_scale"] = 1.0
-    _, _, o8 = _run(a, 32)
     lse8 = torch.empty((5, 32), dtype=torch.float32, device="cuda:0")
-    paa.paged_attn_decode_fp8(dev_bf16(a["q"]), _dev_u8(a["k_cache"]), _dev_u8(a["v_cache"]),
-                              dev_i32(a["block_table"]), dev_i32(a["seq_lens"]), 1.0, 1.0, a["scale"], lse=lse8)
+    o8, _ = paa.paged_attn_decode_fp8(dev_bf16(a["q"]), _dev_u8(a["k_cache"]), _dev_u8(a["v_cache"]),
+                                      dev_i32(a["block_table"]), dev_i32(a["seq_lens"]), 1.0, 1.0, a["scale"],
+                                      lse=lse8)
     as_bf16 = lambda x: torch.from_numpy(x.copy()).view(torch.float8_e4m3fn).to(torch.bfloat16).to("cuda:0")
     lse16 = torch.empty((5, 32), dtype=torch.float32, device="cuda:0")
     o16, _ = paa.paged_attn_decode(dev_bf16(a["q"]), as_bf16(a["k_cache"]), as_bf16(a["v_cache"]),
                                    dev_i32(a["block_table"]), dev_i32(a["seq_lens"]), a["scale"], lse=lse16)
     torch.cuda.synchronize()
-    assert torch.equal(o8.view(torch.int16), o16.view(torch.int16))
-    assert torch.equal(lse8.view(torch.int32), lse16.view(torch.int32))
+    x, y = host_f64(o8), host_f64(o16)
+    assert np.all(np.abs(x - y) <= 2.0 ** -7 * np.maximum(np.abs(x), np.abs(y)))
+    # scores here reach the hundreds (E4M3 values up to 448 with unit scales): a few fp32 ulps of the LSE
+    ulp = np.finfo(np.float32).eps * np.abs(lse16.cpu().numpy())
+    assert np.all(np.abs(lse8.cpu().numpy() - lse16.cpu().numpy()) <= 4 * ulp)
 
 
 def test_fp8_decode_argument_errors():
