@@ -236,7 +236,10 @@ int paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_cach
  *
  * attn_decode_call holds the arguments of one paged_attn_decode call (same
  * meaning, layout and rules; the stream is the graph's).  A model's decode
- * step makes one such call per layer.
+ * step makes one such call per layer.  kv_fp8 = 1 makes it a
+ * paged_attn_decode_fp8 call instead (E4M3 caches, k_scale and v_scale under
+ * that function's rules); with kv_fp8 = 0 the scales are ignored; any other
+ * value is ATTN_ERR_INVALID_SHAPE.
  *
  * paged_attn_decode_graph_create — checks every call exactly as
  * paged_attn_decode does, then captures the num_calls calls in order (each a
@@ -263,6 +266,8 @@ typedef struct attn_decode_call {
   float scale;
   void* workspace;
   size_t workspace_bytes;
+  int kv_fp8;
+  float k_scale, v_scale;
 } attn_decode_call;
 
 int paged_attn_decode_graph_create(const attn_decode_call* calls, int num_calls, hipStream_t capture_stream,

@@ -30,7 +30,8 @@ class DecodeCall(ctypes.Structure):
                 ("lse", ctypes.c_void_p), ("num_seqs", ctypes.c_int), ("H", ctypes.c_int), ("Hkv", ctypes.c_int),
                 ("d", ctypes.c_int), ("page_size", ctypes.c_int), ("max_pages_per_seq", ctypes.c_int),
                 ("num_pages", ctypes.c_int), ("scale", ctypes.c_float), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("kv_fp8", ctypes.c_int), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float)]
 
 
 def lib() -> ctypes.CDLL:
@@ -290,7 +291,8 @@ class PagedDecodeGraph:
 
     ``calls`` is a list of dicts, one per paged_attn_decode call in order (say one per layer of a
     model's decode step), with the keyword names of :func:`paged_attn_decode` (q, k_cache, v_cache,
-    block_table, seq_lens, and optionally scale, num_pages, workspace, out, lse).  Their tensors are
+    block_table, seq_lens, and optionally scale, num_pages, workspace, out, lse).  Caches of dtype uint8 make
+    the call a :func:`paged_attn_decode_fp8` call, whose k_scale and v_scale the dict then gives.  Tensors are
     the graph's fixed buffers: update the inputs in place between replays; every replay rewrites the
     outputs (``self.outputs[i]`` is call i's (out, lse)).  Missing workspaces and outputs are
     allocated here, at creation; a replay allocates nothing.
@@ -299,10 +301,12 @@ class PagedDecodeGraph:
     def __init__(self, calls, capture_stream=None):
         structs, self.outputs, self._keep = [], [], []
         for c in calls:
+            fp8 = c["k_cache"].dtype == torch.uint8
             args, ws, out, lse = _decode_args(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"],
                                               c.get("scale"), c.get("num_pages"), c.get("workspace"), c.get("out"),
-                                              c.get("lse"))
-            structs.append(DecodeCall(*[a.value if isinstance(a, ctypes.c_void_p) else a for a in args]))
+                                              c.get("lse"), cache_dtype=torch.uint8 if fp8 else torch.bfloat16)
+            extra = [1, float(c["k_scale"]), float(c["v_scale"])] if fp8 else [0, 1.0, 1.0]
+            structs.append(DecodeCall(*[a.value if isinstance(a, ctypes.c_void_p) else a for a in args], *extra))
             self.outputs.append((out, lse))
             self._keep.append((c, ws, out, lse))  # the graph holds their addresses
         if not structs:

@@ -233,7 +233,8 @@ int check_decode_call(const attn_decode_call& c) {
   if (c.d != 64 && c.d != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
   if (c.page_size != 16) return ATTN_ERR_UNSUPPORTED_PAGE_SIZE;
   if (c.H / c.Hkv > 16) return ATTN_ERR_UNSUPPORTED_GROUP;
-  if (!scale_ok(c.scale)) return ATTN_ERR_INVALID_SCALE;
+  if (c.kv_fp8 != 0 && c.kv_fp8 != 1) return ATTN_ERR_INVALID_SHAPE;
+  if (!scale_ok(c.scale) || (c.kv_fp8 && (!scale_ok(c.k_scale) || !scale_ok(c.v_scale)))) return ATTN_ERR_INVALID_SCALE;
   if (c.num_seqs == 0) return ATTN_OK;
   if (!c.q || !c.k_cache || !c.v_cache || (!c.block_table && c.max_pages_per_seq > 0) || !c.seq_lens || !c.o ||
       !c.workspace)
@@ -257,14 +258,14 @@ int paged_attn_decode_graph_create(const attn_decode_call* calls, int num_calls,
   }
   // one-time kernel attributes are set outside the capture
   for (int i = 0; i < num_calls; ++i)
-    if (paa::decode_setup(calls[i].d) != hipSuccess) return ATTN_ERR_LAUNCH;
+    if (paa::decode_setup(calls[i].d, calls[i].kv_fp8 != 0) != hipSuccess) return ATTN_ERR_LAUNCH;
   if (hipStreamBeginCapture(capture_stream, hipStreamCaptureModeThreadLocal) != hipSuccess) return ATTN_ERR_LAUNCH;
   int rc = ATTN_OK;
   for (int i = 0; i < num_calls && rc == ATTN_OK; ++i) {
     const attn_decode_call& c = calls[i];
-    rc = paged_attn_decode(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, c.o, c.lse, c.num_seqs, c.H, c.Hkv,
-                           c.d, c.page_size, c.max_pages_per_seq, c.num_pages, c.scale, c.workspace,
-                           c.workspace_bytes, capture_stream);
+    rc = decode_call(c.q, c.k_cache, c.v_cache, c.kv_fp8 != 0, c.k_scale, c.v_scale, c.block_table, c.seq_lens, c.o,
+                     c.lse, c.num_seqs, c.H, c.Hkv, c.d, c.page_size, c.max_pages_per_seq, c.num_pages, c.scale,
+                     c.workspace, c.workspace_bytes, capture_stream);
   }
   hipGraph_t graph = nullptr;
   const hipError_t end = hipStreamEndCapture(capture_stream, &graph);  // always end the capture

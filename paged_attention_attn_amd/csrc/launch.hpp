@@ -29,7 +29,7 @@ hipError_t prefill_f32(const float* q, const float* k, const float* v, float* o,
 // Hkv that divides H with at most 16 query heads per KV head.
 int decode_max_parts(int H);
 // One-time per-process setup of the decode kernels (no launch); done before any graph capture.
-hipError_t decode_setup(int d);
+hipError_t decode_setup(int d, bool fp8);
 int decode_parts(int num_seqs, int H, int Hkv, int max_pages_per_seq);
 
 // Decode over a bf16 cache, or (fp8) over an E4M3 cache holding its values divided by k_scale, v_scale.

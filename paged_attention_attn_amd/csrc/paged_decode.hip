@@ -617,7 +617,10 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t decode_setup(int d) { return d == 64 ? setup_decode<64, false>() : setup_decode<128, false>(); }
+hipError_t decode_setup(int d, bool fp8) {
+  if (fp8) return d == 64 ? setup_decode<64, true>() : setup_decode<128, true>();
+  return d == 64 ? setup_decode<64, false>() : setup_decode<128, false>();
+}
 
 int decode_max_parts(int H) {
   // Hkv >= H / 16 (at most 16 query heads per KV head), so kTargetWaves / Hkv <= 16 * kTargetWaves / H

@@ -143,6 +143,10 @@ def test_decode_graph_validation(L):
     assert create([call(workspace_bytes=ws - 1)]) == WS
     assert create([call(scale=-1.0)]) == SCALE
     assert create([call(block_table=None)]) == NULL
+    assert create([call(kv_fp8=2)]) == SHAPE
+    assert create([call(kv_fp8=1, k_scale=0.0, v_scale=1.0)]) == SCALE  # an FP8 call's scales are checked
+    assert create([call(kv_fp8=1, k_scale=1.0, v_scale=float("nan"))]) == SCALE
+    assert create([call(kv_fp8=0, k_scale=0.0, v_scale=0.0), call(d=96)]) == HEAD_DIM  # ... a bf16 call's are not
     arr = (_binding.DecodeCall * 1)(call())
     assert L.paged_attn_decode_graph_create(arr, 0, S, ctypes.byref(handle)) == SHAPE
     assert L.paged_attn_decode_graph_create(None, 1, S, ctypes.byref(handle)) == NULL

@@ -316,6 +316,46 @@ def test_decode_graph_full_workload_matches_eager():
         g.close()
 
 
+def test_decode_graph_mixes_fp8_and_bf16_caches():
+    """Layers with E4M3 caches and layers with bf16 caches in one graph: every replay equals the eager calls
+    bit for bit."""
+    from workloads import decode_inputs_fp8
+    lens = [5, 300, 1, 777]
+    w = DecodeWorkload("mixed", len(lens), 32, 8, 128, 1, 800, 16, 300)
+    layers, eager = [], []
+    for i in range(4):
+        fp8 = i % 2 == 1
+        a = (decode_inputs_fp8 if fp8 else decode_inputs)(w, seed=70 + i, seq_lens=lens)
+        kc, vc = ((torch.from_numpy(a["k_cache"]).to("cuda:0"), torch.from_numpy(a["v_cache"]).to("cuda:0")) if fp8
+                  else (dev_bf16(a["k_cache"]), dev_bf16(a["v_cache"])))
+        c = dict(q=dev_bf16(a["q"]), k_cache=kc, v_cache=vc, block_table=dev_i32(a["block_table"]),
+                 seq_lens=dev_i32(a["seq_lens"]), scale=a["scale"],
+                 lse=torch.empty((len(lens), 32), dtype=torch.float32, device="cuda:0"))
+        if fp8:
+            c.update(k_scale=a["k_scale"], v_scale=a["v_scale"])
+            o, _ = paa.paged_attn_decode_fp8(c["q"], kc, vc, c["block_table"], c["seq_lens"], a["k_scale"],
+                                             a["v_scale"], a["scale"], lse=c["lse"])
+        else:
+            o, _ = paa.paged_attn_decode(c["q"], kc, vc, c["block_table"], c["seq_lens"], a["scale"], lse=c["lse"])
+        torch.cuda.synchronize()
+        eager.append((o.clone(), c["lse"].clone()))
+        layers.append(c)
+    _announce("decode graph mixing FP8 and bf16 caches")
+    g = paa.PagedDecodeGraph(layers)
+    try:
+        for rep in range(2):
+            for (o, lse) in g.outputs:
+                o.zero_()
+                lse.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            for (o, lse), (eo, el) in zip(g.outputs, eager):
+                assert torch.equal(o.view(torch.int16), eo.view(torch.int16))
+                assert torch.equal(lse.view(torch.int32), el.view(torch.int32))
+    finally:
+        g.close()
+
+
 def test_decode_graph_layers_in_one_submission():
     """Several decode calls (the layers of one decode step, with their own caches, head dims and group sizes,
     sharing one workspace as consecutive calls on one stream may) captured into one graph: every call's
