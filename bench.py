@@ -19,6 +19,8 @@ Other modes (used to produce the summaries kept under profiles/):
   --pmc-pass                 a few launches of every kernel plus a plain copy
                              of known size, for a rocprofv3 --pmc run
   --summarize-trace DIR      markdown summary of a rocprofv3 --kernel-trace run
+  --summarize-mfma D P       MFMA utilisation per workload from a counter run (D)
+                             MFMA_COUNTERS
   --summarize-counters F W   HBM bytes per launch from a FETCH_SIZE run (F)
                              and a WRITE_SIZE run (W), calibrated by the copy
 """
@@ -668,6 +670,50 @@ def summarize_counters(fetch_dir, write_dir, pass_json, command) -> str:
     return "\n".join(lines) + "\n"
 
 
+MFMA_COUNTERS = ("MfmaUtil", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES",
+                 "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8")
+
+
+def summarize_mfma(mfma_dir, pass_json, command) -> str:
+    """JSON lines: per workload and kernel, the matrix-core use one rocprofv3 --pmc run of MFMA_COUNTERS
+    measured: MfmaUtil (MFMA-busy cycles over GPU-active cycles times SIMDs, %), the MFMA flops executed per
+    call (MOPS x 512) against the workload's algorithmic flops, and the share of MFMA-busy cycles in which a
+    VALU instruction also issued."""
+    from workloads import WORKLOADS, PrefillWorkload
+    with open(pass_json) as f:
+        meta = json.loads([l for l in f if l.startswith("{")][-1])
+    names = meta["phases"]
+    per = {}
+    for counter in MFMA_COUNTERS:
+        groups = _split_phases(_load_counters(mfma_dir, counter), len(names))
+        if len(groups) != len(names) or any(COPY_KERNEL_TAG not in r["name"] for r in groups[0]):
+            raise SystemExit(f"{counter}: dispatches do not split into the pass's phases {names}")
+        for name, g in zip(names[1:], groups[1:]):
+            for r in g:
+                k = per.setdefault((name, _short(r["name"])), {})
+                k.setdefault(counter, []).append(r["value"])
+    lines = ["# Matrix-core use per workload and kernel from one rocprofv3 --pmc run (per-dispatch means).",
+             f"# Command (repository root): {command}",
+             "# mfma_util_pct: MfmaUtil = sum of SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs) x 100.",
+             "# mfma_tflop_per_call: (SQ_INSTS_VALU_MFMA_MOPS_BF16 + _F8) x 512 / 1e12; algorithmic_tflop: the",
+             "# workload's 4*d*visible-pairs count (prefill only); coexec_share: SQ_VALU_MFMA_COEXEC_CYCLES /",
+             "# SQ_VALU_MFMA_BUSY_CYCLES, the MFMA-busy cycles in which a VALU instruction issued too."]
+    for (name, kernel), c in per.items():
+        mean = {k: statistics.fmean(v) for k, v in c.items()}
+        flops = (mean.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + mean.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0)) * 512
+        e = {"workload": name, "kernel": kernel, "mfma_util_pct": round(mean["MfmaUtil"], 2),
+             "mfma_tflop_per_call": round(flops / 1e12, 5)}
+        w = WORKLOADS.get(name)
+        if isinstance(w, PrefillWorkload):
+            e["algorithmic_tflop"] = round(prefill_flops(w) / 1e12, 5)
+        busy = mean.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        if busy > 0:
+            e["coexec_share"] = round(mean["SQ_VALU_MFMA_COEXEC_CYCLES"] / busy, 4)
+        e["sources"] = meta["sources"]
+        lines.append(json.dumps(e))
+    return "\n".join(lines) + "\n"
+
+
 # ----------------------------------------------------------------- main
 
 def main() -> int:
@@ -683,6 +729,7 @@ def main() -> int:
     ap.add_argument("--pmc-pass", action="store_true", help="short run for a rocprofv3 --pmc pass")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"))
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PASS_JSON"))
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("MFMA_DIR", "PASS_JSON"))
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     args = ap.parse_args()
 
@@ -691,6 +738,9 @@ def main() -> int:
         return 0
     if args.summarize_counters:
         sys.stdout.write(summarize_counters(*args.summarize_counters, args.command))
+        return 0
+    if args.summarize_mfma:
+        sys.stdout.write(summarize_mfma(*args.summarize_mfma, args.command))
         return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
