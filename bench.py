@@ -48,6 +48,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0  # dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_counters.txt")
 CSRC = os.path.join(ROOT, "paged_attention_attn_amd", "csrc")
 PHASE_GAP_S = 0.05         # idle time left between phases so a trace can be split by them
 COPY_BYTES = 1 << 30       # calibration copy: 1 GiB read + 1 GiB written
@@ -136,9 +137,27 @@ def read_traffic(workload: str):
     return None
 
 
-def roofline(kind, achieved, peak, unit, traffic):
-    return {"bound": kind, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": traffic}
+def read_mfma_busy(workload: str):
+    """MfmaUtil (%) of the workload's attention kernel from the committed counter summary, if taken on these
+    sources."""
+    if not os.path.exists(MFMA_FILE):
+        return None
+    with open(MFMA_FILE) as f:
+        for line in f:
+            if line.startswith("{"):
+                e = json.loads(line)
+                if e.get("workload") == workload and e.get("sources") == source_digest() and \
+                        e.get("mfma_tflop_per_call", 0) > 0:
+                    return e["mfma_util_pct"]
+    return None
+
+
+def roofline(kind, achieved, peak, unit, traffic, mfma_busy_pct=None):
+    r = {"bound": kind, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": traffic}
+    if kind == "mfma":
+        r["mfma_busy_pct"] = mfma_busy_pct  # matrix-core busy share of active cycles (counters), or None
+    return r
 
 
 # ----------------------------------------------------------------- device helpers
@@ -390,7 +409,7 @@ def run_bench(args, torch, paa) -> dict:
     db = decode_bytes(dw, dc.a["seq_lens"])
     pre_tf = pf / (pre_ms * 1e-3) / 1e12
     dec_gbs = db / (dec_ms * 1e-3) / 1e9
-    pre_roof = roofline("mfma", pre_tf, PEAK_BF16_TFLOPS, "TFLOP/s", read_traffic(pw.name))
+    pre_roof = roofline("mfma", pre_tf, PEAK_BF16_TFLOPS, "TFLOP/s", read_traffic(pw.name), read_mfma_busy(pw.name))
     dec_roof = roofline("hbm", dec_gbs, PEAK_HBM_GBS, "GB/s", read_traffic(dw.name))
 
     # ---- decode with the 256 MB last-level cache evicted before every call ----
@@ -454,7 +473,8 @@ def run_bench(args, torch, paa) -> dict:
     chunked = {"workload": CHUNKED, "ms": round(mean, 4), "ms_median": round(med, 4), "value": round(c_tf, 2),
                "unit": "TFLOP/s", "algorithmic_gflop": round(chunked_flops(cc.w, cc.a["ctx_lens"]) / 1e9, 3),
                "algorithmic_mb": round(chunked_bytes(cc.w, cc.a["ctx_lens"]) / 1e6, 3),
-               "roofline": roofline("mfma", c_tf, PEAK_BF16_TFLOPS, "TFLOP/s", read_traffic(CHUNKED))}
+               "roofline": roofline("mfma", c_tf, PEAK_BF16_TFLOPS, "TFLOP/s", read_traffic(CHUNKED),
+                                    read_mfma_busy(CHUNKED))}
     _log(f"{CHUNKED}: {mean:.4f} ms, {c_tf:.1f} TFLOP/s")
     del cc
 
@@ -467,7 +487,8 @@ def run_bench(args, torch, paa) -> dict:
             tf = prefill_flops(c.w) / (mean * 1e-3) / 1e12
             more.append({"workload": name, "ms": round(mean, 4), "ms_median": round(med, 4),
                          "value": round(tf, 2), "unit": "TFLOP/s",
-                         "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", read_traffic(name))})
+                         "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", read_traffic(name),
+                                              read_mfma_busy(name))})
             del c
             _log(f"{name}: {mean:.4f} ms, {tf:.1f} TFLOP/s")
 
@@ -480,7 +501,8 @@ def run_bench(args, torch, paa) -> dict:
             tf = prefill_flops(c.w) / (mean * 1e-3) / 1e12
             fp8.append({"workload": name, "ms": round(mean, 4), "ms_median": round(med, 4), "value": round(tf, 2),
                         "unit": "TFLOP/s", "dtype": "fp8 e4m3 in, bf16 out",
-                        "roofline": roofline("mfma", tf, PEAK_FP8_TFLOPS, "TFLOP/s", read_traffic(name))})
+                        "roofline": roofline("mfma", tf, PEAK_FP8_TFLOPS, "TFLOP/s", read_traffic(name),
+                                             read_mfma_busy(name))})
             del c
             _log(f"{name}: {mean:.4f} ms, {tf:.1f} TFLOP/s")
 
