@@ -100,3 +100,33 @@ def test_fp8_decode_argument_errors():
         paa.paged_attn_decode_fp8(q, kc, kc, bt, lens, 0.0, 1.0)
     with pytest.raises(TypeError):
         paa.paged_attn_decode_fp8(q, kc.to(torch.bfloat16), kc.to(torch.bfloat16), bt, lens, 1.0, 1.0)
+
+
+def test_fp8_decode_zero_page_table():
+    """max_pages_per_seq == 0: every length clamps to 0, so O = 0 and LSE = -inf."""
+    q = torch.randn((3, 4, 128), device="cuda:0").to(torch.bfloat16)
+    kc = torch.zeros((2, 16, 1, 128), dtype=torch.uint8, device="cuda:0")
+    bt = torch.zeros((3, 0), dtype=torch.int32, device="cuda:0")
+    lens = torch.full((3,), 5, dtype=torch.int32, device="cuda:0")
+    lse = torch.empty((3, 4), dtype=torch.float32, device="cuda:0")
+    o, _ = paa.paged_attn_decode_fp8(q, kc, kc, bt, lens, 0.5, 0.5, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(o.float() == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_fp8_decode_out_of_range_page_id_is_not_read():
+    """A page id past num_pages is never dereferenced; its tokens count as absent (here the middle page of
+    three), so the result is the decode over the other two pages."""
+    w = DecodeWorkload("fp8oob", 1, 4, 1, 64, 48, 48, 16, 8)
+    bt = np.array([[2, 5, 7]], dtype=np.int32)
+    a = decode_inputs_fp8(w, seed=6, seq_lens=[48], block_table=bt)
+    bad = dict(a)
+    bad["block_table"] = np.array([[2, 1 << 30, 7]], dtype=np.int32)
+    o, lse, _ = _run(bad, 4)
+    # the same tokens with the middle page dropped: a two-page sequence over pages 2 and 7
+    two = dict(a)
+    two["block_table"] = np.array([[2, 7, -1]], dtype=np.int32)
+    two["seq_lens"] = np.array([32], dtype=np.int32)
+    ro, rl = _oracle(two)
+    assert_close_bf16(o, ro)
+    assert_close_lse(lse, rl)
