@@ -775,10 +775,21 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     PAA_LDS char* dst = (loads_v ? vdst : kdst) + load_slot * T::kTileBytes + (group_r0 / T::kRowsPerBlock + i) * 1024;
     group_load<PAGED>((PAA_LDS void*)dst, gs, load_src, row0, dr, off, n_k, qoff, (int)kv_stride);
   };
+  // Paged: lane k of pw holds the page of this wave's rows of tile pw_t0 + k, so a tile's page is a
+  // lane read.  A scalar load per tile would be retired by the next tile barrier's lgkmcnt(0) and
+  // stall every period on its latency (400 against 316 us for chunked prefill with no lookup).  A
+  // refill (once per 64 tiles) is one vector load whose value is used at once; paged runs use two
+  // stages, whose every pair ends with vmcnt(0), so it leaves the ring's exact waits intact.
+  int pw = 0, pw_t0 = -(1 << 30);
   auto page_of = [&](int j) __attribute__((always_inline)) -> int {  // page of this wave's rows of tile j
     if constexpr (PAGED) {
-      const int blk = min((j * kBc) / kPageTokens + wave_page, a.max_pages - 1);
-      return min(max(a.bt[(size_t)b * a.max_pages + blk], 0), a.num_pages - 1);
+      if (j < pw_t0 || j >= pw_t0 + 64) {
+        pw_t0 = j;
+        const int blk = min((j + lane) * (kBc / kPageTokens) + wave_page, a.max_pages - 1);
+        pw = min(max(a.bt[(size_t)b * a.max_pages + blk], 0), a.num_pages - 1);
+        return __builtin_amdgcn_readfirstlane(pw);
+      }
+      return __builtin_amdgcn_readlane(pw, j - pw_t0);
     } else {
       return 0;
     }
