@@ -367,11 +367,20 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
     }
   };
   // cache page holding this wave's rows of tile j (0 when not paged); an id outside the pool is
-  // clamped into it, so no access leaves the pool (such a table gives unspecified results)
+  // clamped into it, so no access leaves the pool (such a table gives unspecified results).
+  // Lane k of pw holds the page of tile pw_t0 + k, so most lookups are a lane read; a refill (once
+  // per 64 tiles, or at the jump to a window) is one vector load used at once.  Paged runs use two
+  // stages, whose every tile ends with vmcnt(0), so the refill leaves the ring's waits exact.
+  int pw = 0, pw_t0 = -(1 << 30);
   auto page_of = [&](int j) __attribute__((always_inline)) -> int {
     if constexpr (PAGED) {
-      const int blk = min((j * kBc) / kPageTokens + wave_page, a.max_pages - 1);
-      return min(max(a.bt[(size_t)b * a.max_pages + blk], 0), a.num_pages - 1);
+      if (j < pw_t0 || j >= pw_t0 + 64) {
+        pw_t0 = j;
+        const int blk = min((j + lane) * (kBc / kPageTokens) + wave_page, a.max_pages - 1);
+        pw = min(max(a.bt[(size_t)b * a.max_pages + blk], 0), a.num_pages - 1);
+        return __builtin_amdgcn_readfirstlane(pw);
+      }
+      return __builtin_amdgcn_readlane(pw, j - pw_t0);
     } else {
       return 0;
     }
