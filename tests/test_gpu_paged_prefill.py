@@ -66,6 +66,9 @@ SMALL = [
     ([511, 17], [1, 300], 16, 4, 128),
     ([1000], [65], 6, 2, 64),
     ([0, 0, 0, 0], [128, 127, 129, 1], 2, 1, 128),
+    # more than 64 key tiles: the per-wave window of page ids is refilled mid-sequence
+    ([4100, 1], [60, 2], 2, 1, 128),
+    ([4200, 70], [40, 3], 4, 2, 64),
 ]
 
 
@@ -78,13 +81,15 @@ def test_paged_prefill_small_full_parity(ctxs, qlens, H, Hkv, d):
 
 
 # Grids of at least 1024 eight-wave workgroups (d = 128 takes the ping-pong kernel there): one per
-# head-sharing width (4, 2, 1 query heads per workgroup); the last two reach that size through a
+# head-sharing width (4, 2, 1 query heads per workgroup); the last three reach that size through a
 # loose max_q_len, so most of their workgroups leave at once.
 LARGE = [
     ([0, 1, 15, 16, 17, 63, 64, 65, 500, 1000, 2047, 3, 300, 0, 777, 129],
      [512, 1, 0, 100, 511, 64, 65, 300, 129, 17, 2, 512, 256, 16, 400, 33], 32, 8, 128, 512),
     ([5, 0, 64, 1500, 31, 200, 16, 999], [300, 129, 0, 64, 1, 250, 77, 16], 16, 8, 128, 2048),
     ([700, 0, 48, 1], [700, 0, 257, 1], 8, 8, 128, 8192),
+    # d = 64 (eight-wave lock-step kernel) with contexts past 64 key tiles
+    ([4200, 0, 70, 3000], [10, 100, 300, 1], 8, 8, 64, 8192),
 ]
 
 
