@@ -29,6 +29,10 @@
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
+/* Only the functions below are exported from the shared library (it is built with hidden
+ * visibility by default). */
+#define ATTN_API __attribute__((visibility("default")))
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -68,7 +72,7 @@ enum {
  * Arithmetic: bf16 products, fp32 accumulation and softmax; the
  * probabilities are rounded to bf16 before the product with V.
  */
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
+ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
              int causal, float scale, hipStream_t stream);
 
 /*
@@ -82,15 +86,20 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
  * arithmetic are those of attn_fwd; window must be >= 1 and n_global >= 0
  * (ATTN_ERR_INVALID_SHAPE otherwise).  window >= N is the plain causal mask.
  */
-int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+ATTN_API int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
                     int d, int window, int n_global, float scale, hipStream_t stream);
 
 /*
  * attn_fwd_f32 — the same operation with fp32 inputs, outputs and arithmetic
- * throughout (no reduced-precision matrix instructions).  Shapes, masking,
- * head grouping and LSE as for attn_fwd; d must be 64 or 128.
+ * throughout (no reduced-precision matrix instructions): the attention of
+ * "Fast Attention Kernels and Operator Fusion", section "FlashAttention-Style
+ * Kernels", tiled with the online softmax of "Kernel Fusion and Custom
+ * Kernels", section "3. FlashAttention: The Milestone of Fusion" (v1), so the
+ * score matrix is never written to memory.  Shapes, masking, head grouping and
+ * LSE as for attn_fwd; d must be 64 or 128.  One work item per query row: this
+ * is the exactness reference of the family, not a throughput path.
  */
-int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Hkv, int N,
+ATTN_API int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Hkv, int N,
                  int d, int causal, float scale, hipStream_t stream);
 
 /*
@@ -112,7 +121,7 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
  * N must be a multiple of 16; scale and the three tensor scales finite and
  * positive; other rules as attn_fwd.
  */
-int attn_fwd_fp8(const void* q, const void* k, const void* v_t, void* o, float* lse, int B, int H, int Hkv, int N,
+ATTN_API int attn_fwd_fp8(const void* q, const void* k, const void* v_t, void* o, float* lse, int B, int H, int Hkv, int N,
                  int d, int causal, float scale, float q_scale, float k_scale, float v_scale, hipStream_t stream);
 
 /*
@@ -156,19 +165,26 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v_t, void* o, float* 
  * appends to must not be read by another in the same call.  No workspace, no
  * atomics: the result is deterministic.  Arithmetic as attn_fwd.
  */
-int paged_prefill(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+ATTN_API int paged_prefill(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                   const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_start, void* o, float* lse,
                   int num_seqs, int H, int Hkv, int d, int page_size, int max_pages_per_seq, int num_pages,
                   int max_q_len, float scale, hipStream_t stream);
 
 /*
  * paged_attn_decode_workspace_size — bytes of device workspace that
- * paged_attn_decode needs for these shapes (0 on invalid shapes).  It is
- * about (P + num_seqs) * H * (d + 1) * 4 bytes, where P <= 32768 / H is the
- * number of equal page ranges the decode cuts the cache into: linear in
- * num_seqs, H and d, and never larger for longer sequences.
+ * paged_attn_decode needs for these shapes (0 on invalid shapes).  The
+ * workspace holds one partial (normalised O, LSE) per (page range, sequence)
+ * pair, which the reduce kernel merges with the rescaling identity of the
+ * online softmax ("Kernel Fusion and Custom Kernels", section "3.
+ * FlashAttention: The Milestone of Fusion", v1: partial results combine by
+ * rescaling with the running maxima and sums).  It is about
+ * (P + num_seqs) * H * (d + 1) * 4 bytes, where P <= 32768 / H is the number
+ * of equal page ranges the decode cuts the cache into: linear in num_seqs, H
+ * and d, and never larger for longer sequences, so the N^2 score matrix whose
+ * memory "Finding the Next One: Fusion Beyond Attention" describes as the
+ * materialised path's cost is never allocated.
  */
-size_t paged_attn_decode_workspace_size(int num_seqs, int H, int d, int page_size, int max_pages_per_seq);
+ATTN_API size_t paged_attn_decode_workspace_size(int num_seqs, int H, int d, int page_size, int max_pages_per_seq);
 
 /*
  * paged_attn_decode — single-query attention per sequence over a paged KV
@@ -201,7 +217,7 @@ size_t paged_attn_decode_workspace_size(int num_seqs, int H, int d, int page_siz
  * a separate reduce kernel merges them on the same stream.  Its cost per
  * workgroup includes one pass over seq_lens (num_seqs reads).
  */
-int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+ATTN_API int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
                       const int32_t* seq_lens, void* o, float* lse, int num_seqs, int H, int Hkv, int d, int page_size,
                       int max_pages_per_seq, int num_pages, float scale, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
@@ -222,7 +238,7 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, c
  * the scores use scale * k_scale, each partial output is multiplied by
  * v_scale.  Slots at or past L_s may hold anything, NaN codes included.
  */
-int paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale, float v_scale,
+ATTN_API int paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale, float v_scale,
                           const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse, int num_seqs,
                           int H, int Hkv, int d, int page_size, int max_pages_per_seq, int num_pages, float scale,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -270,21 +286,26 @@ typedef struct attn_decode_call {
   float k_scale, v_scale;
 } attn_decode_call;
 
-int paged_attn_decode_graph_create(const attn_decode_call* calls, int num_calls, hipStream_t capture_stream,
+ATTN_API int paged_attn_decode_graph_create(const attn_decode_call* calls, int num_calls, hipStream_t capture_stream,
                                    void** graph_out);
 
 /* paged_attn_decode_graph_launch — one replay of the captured decode calls on
  * `stream` (asynchronous, stream-ordered).  ATTN_ERR_NULL_POINTER for a NULL
  * handle, ATTN_ERR_LAUNCH if the runtime rejects the launch. */
-int paged_attn_decode_graph_launch(void* graph, hipStream_t stream);
+ATTN_API int paged_attn_decode_graph_launch(void* graph, hipStream_t stream);
 
 /* paged_attn_decode_graph_destroy — releases a handle from
  * paged_attn_decode_graph_create (NULL is accepted).  Replays already
  * enqueued are not waited for: synchronise the stream first. */
-int paged_attn_decode_graph_destroy(void* graph);
+ATTN_API int paged_attn_decode_graph_destroy(void* graph);
 
-/* attn_status_string — a static, human-readable description of a status code. */
-const char* attn_status_string(int status);
+/* attn_status_string — a static, human-readable description of a status code.
+ * Unsupported inputs are reported as errors rather than served by a slower
+ * path: "Finding the Next One: Fusion Beyond Attention" warns that a fused
+ * kernel which silently falls back to the materialised computation loses its
+ * benefit without any sign; here every such case is a nonzero status that
+ * this string explains. */
+ATTN_API const char* attn_status_string(int status);
 
 #ifdef __cplusplus
 }

@@ -44,7 +44,7 @@ Readings taken where the pages are silent (each repeated in the design doc):
   adds nothing once the causal mask applies.
 
 The helpers ``_kv_head``, ``_scores``, ``_apply_causal``, ``_window_mask``, ``_softmax``,
-``_page_slot`` and ``_chunk_positions`` are looked up at call time, so tests can plant a mistake in
+``_page_slot``, ``_chunk_positions`` and ``_selected`` are looked up at call time, so tests can plant a mistake in
 one of them (on the CPU) and check that a pin catches it.
 """
 
@@ -270,12 +270,17 @@ def paged_decode_fp8(q, k8, v8, k_scale: float, v_scale: float, block_table, seq
     return _decode_rows(q, np.asarray(k8).shape[2], np.asarray(v8).shape[3], gather, seq_lens, scale, seqs)
 
 
+def _selected(n_seqs: int, seqs):
+    """The sequences a call covers, in the order asked for: all of them when seqs is None."""
+    return range(n_seqs) if seqs is None else list(seqs)
+
+
 def _decode_rows(q, Hkv: int, d_v: int, gather, seq_lens, scale: float, seqs):
     """One query row per sequence attending over the L_s keys/values gather(s, L_s) returns."""
     q64 = _as_f64(q)
     S, H, d = q64.shape
     _check_heads(H, Hkv)
-    seqs = range(S) if seqs is None else list(seqs)
+    seqs = _selected(S, seqs)
     o = np.zeros((len(seqs), H, d_v))
     lse = np.zeros((len(seqs), H))
     for n, s in enumerate(seqs):
@@ -333,7 +338,7 @@ def paged_prefill(q, k_new, v_new, k_cache, v_cache, block_table, ctx_lens, q_st
     Hkv = np.asarray(k_cache).shape[2]
     _check_heads(H, Hkv)
     kc, vc = paged_append(k_cache, v_cache, k_new, v_new, block_table, ctx_lens, q_start)
-    seqs = range(len(ctx_lens)) if seqs is None else list(seqs)
+    seqs = _selected(len(ctx_lens), seqs)
     o, lse = [], []
     for s in seqs:
         lo, hi = int(q_start[s]), int(q_start[s + 1])

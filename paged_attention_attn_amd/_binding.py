@@ -76,7 +76,7 @@ def declared_functions() -> list[str]:
     with open(HEADER) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return re.findall(r"^\s*(?:ATTN_API\s+)?(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
 
 
 def attn_status_string(status: int) -> str:
@@ -96,6 +96,23 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _shape(t, name, shape):
+    """Raises ValueError unless t is a tensor of exactly this shape.  Shapes are checked before dtype and
+    device, and the library sizes every write from q's shape, so an output of any other shape is refused
+    rather than written past its end."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _dims(t, name, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+
+
 def _require(t, name, dtype, ndim, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -112,23 +129,24 @@ def _require(t, name, dtype, ndim, device=None):
 
 
 def _prefill(entry, dtype, q, k, v, causal, scale, out, lse, mask_args=None):
+    _dims(q, "q", 4)
+    _dims(k, "k", 4)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    _shape(k, "k", (B, Hkv, N, d))
+    _shape(v, "v", (B, Hkv, N, d))
+    if out is not None:
+        _shape(out, "out", (B, H, N, d))
+    if lse is not None:
+        _shape(lse, "lse", (B, H, N))
     _require(q, "q", dtype, 4)
     _require(k, "k", dtype, 4, q.device)
     _require(v, "v", dtype, 4, q.device)
-    B, H, N, d = q.shape
-    Hkv = k.shape[1]
-    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
-        raise ValueError(f"k, v must be [B, Hkv, N, d] matching q {tuple(q.shape)}; got {tuple(k.shape)}, "
-                         f"{tuple(v.shape)}")
     if out is None:
         out = torch.empty_like(q)
     _require(out, "out", dtype, 4, q.device)
-    if tuple(out.shape) != tuple(q.shape):
-        raise ValueError("out must have q's shape")
     if lse is not None:
         _require(lse, "lse", torch.float32, 3, q.device)
-        if tuple(lse.shape) != (B, H, N):
-            raise ValueError("lse must be [B, H, N]")
     if scale is None:
         scale = d ** -0.5
     mask = [int(bool(causal))] if mask_args is None else [int(x) for x in mask_args]
@@ -154,14 +172,20 @@ def attn_fwd_fp8(q, k, v_t, causal: bool, scale: float | None = None, q_scale: f
     E4M3 bytes (torch.uint8 or torch.float8_e4m3fn); the inputs are their values times the scales.
     Returns (O bf16 [B,H,N,d], LSE)."""
     fp8 = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
-    for t, name, nd in ((q, "q", 4), (k, "k", 4), (v_t, "v_t", 4)):
-        if not isinstance(t, torch.Tensor) or t.dtype not in fp8:
-            raise TypeError(f"{name} must hold E4M3 bytes (torch.uint8 or torch.float8_e4m3fn)")
-        _require(t, name, t.dtype, nd, q.device)
+    _dims(q, "q", 4)
+    _dims(k, "k", 4)
     B, H, N, d = q.shape
     Hkv = k.shape[1]
-    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v_t.shape) != (B, Hkv, d, N):
-        raise ValueError("k must be [B, Hkv, N, d] and v_t [B, Hkv, d, N]")
+    _shape(k, "k", (B, Hkv, N, d))
+    _shape(v_t, "v_t", (B, Hkv, d, N))
+    if out is not None:
+        _shape(out, "out", (B, H, N, d))
+    if lse is not None:
+        _shape(lse, "lse", (B, H, N))
+    for t, name, nd in ((q, "q", 4), (k, "k", 4), (v_t, "v_t", 4)):
+        if t.dtype not in fp8:
+            raise TypeError(f"{name} must hold E4M3 bytes (torch.uint8 or torch.float8_e4m3fn)")
+        _require(t, name, t.dtype, nd, q.device)
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
     _require(out, "out", torch.bfloat16, 4, q.device)
@@ -188,6 +212,23 @@ def paged_prefill(q, k_new, v_new, k_cache, v_cache, block_table, ctx_lens, q_st
     block_table [S, max_pages], ctx_lens [S], q_start [S + 1] int32 on the same device.  max_q_len
     bounds every chunk length (default T, known without reading the device).  Returns (O, LSE).
     """
+    for t, name, nd in ((q, "q", 3), (k_cache, "k_cache", 4), (ctx_lens, "ctx_lens", 1),
+                        (block_table, "block_table", 2)):
+        _dims(t, name, nd)
+    T, H, d = q.shape
+    P, page_size, Hkv, dk = k_cache.shape
+    if dk != d:
+        raise ValueError(f"k_cache's head dim {dk} differs from q's {d}")
+    S = ctx_lens.shape[0]
+    _shape(v_cache, "v_cache", tuple(k_cache.shape))
+    _shape(k_new, "k_new", (T, Hkv, d))
+    _shape(v_new, "v_new", (T, Hkv, d))
+    _shape(block_table, "block_table", (S, block_table.shape[1]))
+    _shape(q_start, "q_start", (S + 1,))
+    if out is not None:
+        _shape(out, "out", (T, H, d))
+    if lse is not None:
+        _shape(lse, "lse", (T, H))
     _require(q, "q", torch.bfloat16, 3)
     dev = q.device
     _require(k_new, "k_new", torch.bfloat16, 3, dev)
@@ -197,15 +238,6 @@ def paged_prefill(q, k_new, v_new, k_cache, v_cache, block_table, ctx_lens, q_st
     _require(block_table, "block_table", torch.int32, 2, dev)
     _require(ctx_lens, "ctx_lens", torch.int32, 1, dev)
     _require(q_start, "q_start", torch.int32, 1, dev)
-    T, H, d = q.shape
-    P, page_size, Hkv, dk = k_cache.shape
-    if tuple(v_cache.shape) != tuple(k_cache.shape) or dk != d:
-        raise ValueError("k_cache and v_cache must both be [num_pages, page_size, Hkv, d]")
-    if tuple(k_new.shape) != (T, Hkv, d) or tuple(v_new.shape) != (T, Hkv, d):
-        raise ValueError("k_new and v_new must be [T, Hkv, d] with T and d of q and Hkv of the caches")
-    S = ctx_lens.shape[0]
-    if block_table.shape[0] != S or q_start.shape[0] != S + 1:
-        raise ValueError("block_table needs one row and q_start S + 1 entries for the S sequences of ctx_lens")
     if max_q_len is None:
         max_q_len = T
     if num_pages is None:
@@ -230,19 +262,26 @@ def paged_attn_decode_workspace_size(num_seqs: int, H: int, d: int, page_size: i
 def _decode_args(q, k_cache, v_cache, block_table, seq_lens, scale, num_pages, workspace, out, lse,
                  cache_dtype=torch.bfloat16):
     """Checks the decode tensors and fills in the defaults; returns the C argument list (without a stream)."""
+    for t, name, nd in ((q, "q", 3), (k_cache, "k_cache", 4), (block_table, "block_table", 2)):
+        _dims(t, name, nd)
+    S, H, d = q.shape
+    P, page_size, Hkv, dk = k_cache.shape
+    if dk != d:
+        raise ValueError(f"k_cache's head dim {dk} differs from q's {d}")
+    max_pages = block_table.shape[1]
+    _shape(v_cache, "v_cache", tuple(k_cache.shape))
+    _shape(block_table, "block_table", (S, max_pages))
+    _shape(seq_lens, "seq_lens", (S,))
+    if out is not None:
+        _shape(out, "out", (S, H, d))
+    if lse is not None:
+        _shape(lse, "lse", (S, H))
     _require(q, "q", torch.bfloat16, 3)
     dev = q.device
     _require(k_cache, "k_cache", cache_dtype, 4, dev)
     _require(v_cache, "v_cache", cache_dtype, 4, dev)
     _require(block_table, "block_table", torch.int32, 2, dev)
     _require(seq_lens, "seq_lens", torch.int32, 1, dev)
-    S, H, d = q.shape
-    P, page_size, Hkv, dk = k_cache.shape
-    if tuple(v_cache.shape) != tuple(k_cache.shape) or dk != d:
-        raise ValueError("k_cache and v_cache must both be [num_pages, page_size, Hkv, d]")
-    if block_table.shape[0] != S or seq_lens.shape[0] != S:
-        raise ValueError("block_table and seq_lens need one row per sequence")
-    max_pages = block_table.shape[1]
     if num_pages is None:
         num_pages = P
     need = paged_attn_decode_workspace_size(S, H, d, page_size, max_pages)

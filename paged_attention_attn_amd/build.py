@@ -27,6 +27,10 @@ FLAGS = [
     "-fPIC",
     "-Wall",
     "-Wno-unused-function",
+    # host symbols are hidden unless the public header marks them (ATTN_API): the library exports
+    # exactly the declared C entry points
+    "-Xarch_host", "-fvisibility=hidden",
+    "-Xarch_host", "-fvisibility-inlines-hidden",
     # packed fp32 VALU ops stay off: ordinary float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
@@ -52,8 +56,14 @@ def build(verbose: bool = False) -> str:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)
+    # the dynamic symbol table holds exactly the entry points the public header declares
+    from ._binding import declared_functions
+    version_script = os.path.join(BUILD, "exports.map")
+    with open(version_script, "w") as f:
+        f.write("{\n  global:\n" + "".join(f"    {n};\n" for n in declared_functions()) + "  local: *;\n};\n")
     tmp = LIB_PATH + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, f"-Wl,--version-script={version_script}",
+          "-o", tmp])
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -56,6 +56,102 @@ constexpr size_t kWsAlign = 256;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Workspace layout: partial outputs [slots, H, d] fp32, partial LSE [slots, H]
+// fp32, then the [num_seqs, 2] int32 slot range of each sequence and one int32
+// holding the total page count; each region
+// starts on a kWsAlign boundary.  slots = partitions + num_seqs.
+struct DecodeWs {
+  long long slots;
+  size_t o_bytes, lse_bytes, range_bytes;
+  size_t total() const { return o_bytes + lse_bytes + range_bytes; }
+};
+
+bool decode_ws(int num_seqs, int H, int d, int max_pages_per_seq, DecodeWs* w) {
+  long long parts = paa::decode_max_parts(H);
+  const long long pages = (long long)num_seqs * max_pages_per_seq;
+  if (parts > pages) parts = pages;
+  if (parts < 1) parts = 1;
+  w->slots = parts + num_seqs;
+  const long long rows = elems(w->slots, H, 1, 1);
+  if (rows < 0 || elems(rows, d + 1, 4, 1) < 0) return false;
+  w->o_bytes = round_up((size_t)rows * d * sizeof(float), kWsAlign);
+  w->lse_bytes = round_up((size_t)rows * sizeof(float), kWsAlign);
+  w->range_bytes = round_up(((size_t)num_seqs * 2 + 1) * sizeof(int32_t), kWsAlign);
+  return true;
+}
+
+// Argument checks shared by both decode entry points and the graph builder: the bf16 cache, or (fp8)
+// an E4M3 cache with per-tensor scales.  Host-visible sizes and pointer values only.
+int check_decode(const void* q, const void* k_cache, const void* v_cache, bool fp8, float k_scale, float v_scale,
+                 const int32_t* block_table, const int32_t* seq_lens, const void* o, const float* lse, int num_seqs,
+                 int H, int Hkv, int d, int page_size, int max_pages_per_seq, int num_pages, float scale,
+                 const void* workspace, size_t workspace_bytes) {
+  if (num_seqs < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || max_pages_per_seq < 0 || num_pages < 0)
+    return ATTN_ERR_INVALID_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  if (page_size != 16) return ATTN_ERR_UNSUPPORTED_PAGE_SIZE;
+  if (H / Hkv > 16) return ATTN_ERR_UNSUPPORTED_GROUP;
+  if (!scale_ok(scale) || (fp8 && (!scale_ok(k_scale) || !scale_ok(v_scale)))) return ATTN_ERR_INVALID_SCALE;
+  if (num_seqs == 0) return ATTN_OK;  // empty call: nothing is read or written
+  // block_table may be NULL only when it has no columns (then it is never read)
+  if (!q || !k_cache || !v_cache || (!block_table && max_pages_per_seq > 0) || !seq_lens || !o || !workspace)
+    return ATTN_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 4) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(lse, 4) || !aligned(workspace, 16))
+    return ATTN_ERR_MISALIGNED;
+  if (elems(num_pages, page_size, Hkv, d) < 0) return ATTN_ERR_TOO_LARGE;
+  // page positions and (sequence, head) rows are 32-bit inside the kernels
+  if ((long long)num_seqs * max_pages_per_seq > 0x7fffffffLL / page_size ||
+      (long long)num_seqs * H > 0x7fffffffLL)
+    return ATTN_ERR_TOO_LARGE;
+  DecodeWs w;
+  if (!decode_ws(num_seqs, H, d, max_pages_per_seq, &w)) return ATTN_ERR_TOO_LARGE;
+  if (workspace_bytes < w.total()) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  return ATTN_OK;
+}
+
+// Enqueues one decode (partial and reduce kernels) after check_decode has passed.
+int launch_decode(const void* q, const void* k_cache, const void* v_cache, bool fp8, float k_scale, float v_scale,
+                  const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse, int num_seqs, int H,
+                  int Hkv, int d, int max_pages_per_seq, int num_pages, float scale, void* workspace,
+                  hipStream_t stream) {
+  if (num_seqs == 0) return ATTN_OK;
+  DecodeWs w;
+  decode_ws(num_seqs, H, d, max_pages_per_seq, &w);
+  const int parts = paa::decode_parts(num_seqs, H, Hkv, max_pages_per_seq);
+  char* base = static_cast<char*>(workspace);
+  float* ws_o = reinterpret_cast<float*>(base);
+  float* ws_lse = reinterpret_cast<float*>(base + w.o_bytes);
+  int* ws_range = reinterpret_cast<int*>(base + w.o_bytes + w.lse_bytes);
+  return launch_status(paa::paged_decode(q, k_cache, v_cache, fp8, k_scale, v_scale, block_table, seq_lens, o, lse,
+                                         num_seqs, H, Hkv, d, max_pages_per_seq, num_pages, scale, ws_o, ws_lse,
+                                         ws_range, parts, (int)w.slots, stream));
+}
+
+int decode_call(const void* q, const void* k_cache, const void* v_cache, bool fp8, float k_scale, float v_scale,
+                const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse, int num_seqs, int H, int Hkv,
+                int d, int page_size, int max_pages_per_seq, int num_pages, float scale, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  const int rc = check_decode(q, k_cache, v_cache, fp8, k_scale, v_scale, block_table, seq_lens, o, lse, num_seqs, H,
+                              Hkv, d, page_size, max_pages_per_seq, num_pages, scale, workspace, workspace_bytes);
+  if (rc != ATTN_OK) return rc;
+  return launch_decode(q, k_cache, v_cache, fp8, k_scale, v_scale, block_table, seq_lens, o, lse, num_seqs, H, Hkv, d,
+                       max_pages_per_seq, num_pages, scale, workspace, stream);
+}
+
+struct DecodeGraph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+// The same checks as paged_attn_decode, for one call of a graph (nothing is launched).
+int check_decode_call(const attn_decode_call& c) {
+  if (c.kv_fp8 != 0 && c.kv_fp8 != 1) return ATTN_ERR_INVALID_SHAPE;
+  return check_decode(c.q, c.k_cache, c.v_cache, c.kv_fp8 != 0, c.k_scale, c.v_scale, c.block_table, c.seq_lens, c.o,
+                      c.lse, c.num_seqs, c.H, c.Hkv, c.d, c.page_size, c.max_pages_per_seq, c.num_pages, c.scale,
+                      c.workspace, c.workspace_bytes);
+}
+
 }  // namespace
 
 extern "C" {
@@ -96,34 +192,6 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
   return launch_status(paa::prefill_f32(q, k, v, o, lse, B, H, Hkv, N, d, causal != 0, scale, stream));
 }
 
-namespace {
-
-// Workspace layout: partial outputs [slots, H, d] fp32, partial LSE [slots, H]
-// fp32, then the [num_seqs, 2] int32 slot range of each sequence and one int32
-// holding the total page count; each region
-// starts on a kWsAlign boundary.  slots = partitions + num_seqs.
-struct DecodeWs {
-  long long slots;
-  size_t o_bytes, lse_bytes, range_bytes;
-  size_t total() const { return o_bytes + lse_bytes + range_bytes; }
-};
-
-bool decode_ws(int num_seqs, int H, int d, int max_pages_per_seq, DecodeWs* w) {
-  long long parts = paa::decode_max_parts(H);
-  const long long pages = (long long)num_seqs * max_pages_per_seq;
-  if (parts > pages) parts = pages;
-  if (parts < 1) parts = 1;
-  w->slots = parts + num_seqs;
-  const long long rows = elems(w->slots, H, 1, 1);
-  if (rows < 0 || elems(rows, d + 1, 4, 1) < 0) return false;
-  w->o_bytes = round_up((size_t)rows * d * sizeof(float), kWsAlign);
-  w->lse_bytes = round_up((size_t)rows * sizeof(float), kWsAlign);
-  w->range_bytes = round_up(((size_t)num_seqs * 2 + 1) * sizeof(int32_t), kWsAlign);
-  return true;
-}
-
-}  // namespace
-
 size_t paged_attn_decode_workspace_size(int num_seqs, int H, int d, int page_size, int max_pages_per_seq) {
   if (num_seqs < 0 || H < 1 || (d != 64 && d != 128) || page_size != 16 || max_pages_per_seq < 0) return 0;
   if (num_seqs == 0) return kWsAlign;
@@ -131,48 +199,6 @@ size_t paged_attn_decode_workspace_size(int num_seqs, int H, int d, int page_siz
   if (!decode_ws(num_seqs, H, d, max_pages_per_seq, &w)) return 0;
   return w.total();
 }
-
-namespace {
-
-// Both decode entry points: the bf16 cache, or (fp8) an E4M3 cache with per-tensor scales.
-int decode_call(const void* q, const void* k_cache, const void* v_cache, bool fp8, float k_scale, float v_scale,
-                const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse, int num_seqs, int H, int Hkv,
-                int d, int page_size, int max_pages_per_seq, int num_pages, float scale, void* workspace,
-                size_t workspace_bytes, hipStream_t stream) {
-  if (num_seqs < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || max_pages_per_seq < 0 || num_pages < 0)
-    return ATTN_ERR_INVALID_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
-  if (page_size != 16) return ATTN_ERR_UNSUPPORTED_PAGE_SIZE;
-  if (H / Hkv > 16) return ATTN_ERR_UNSUPPORTED_GROUP;
-  if (!scale_ok(scale) || (fp8 && (!scale_ok(k_scale) || !scale_ok(v_scale)))) return ATTN_ERR_INVALID_SCALE;
-  if (num_seqs == 0) return ATTN_OK;  // empty call: nothing is read or written
-  // block_table may be NULL only when it has no columns (then it is never read)
-  if (!q || !k_cache || !v_cache || (!block_table && max_pages_per_seq > 0) || !seq_lens || !o || !workspace)
-    return ATTN_ERR_NULL_POINTER;
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 4) ||
-      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(lse, 4) || !aligned(workspace, 16))
-    return ATTN_ERR_MISALIGNED;
-  if (elems(num_pages, page_size, Hkv, d) < 0) return ATTN_ERR_TOO_LARGE;
-  // page positions and (sequence, head) rows are 32-bit inside the kernels
-  if ((long long)num_seqs * max_pages_per_seq > 0x7fffffffLL / page_size ||
-      (long long)num_seqs * H > 0x7fffffffLL)
-    return ATTN_ERR_TOO_LARGE;
-  const size_t need = paged_attn_decode_workspace_size(num_seqs, H, d, page_size, max_pages_per_seq);
-  if (need == 0) return ATTN_ERR_TOO_LARGE;
-  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
-  const int parts = paa::decode_parts(num_seqs, H, Hkv, max_pages_per_seq);
-  DecodeWs w;
-  if (!decode_ws(num_seqs, H, d, max_pages_per_seq, &w)) return ATTN_ERR_TOO_LARGE;
-  char* base = static_cast<char*>(workspace);
-  float* ws_o = reinterpret_cast<float*>(base);
-  float* ws_lse = reinterpret_cast<float*>(base + w.o_bytes);
-  int* ws_range = reinterpret_cast<int*>(base + w.o_bytes + w.lse_bytes);
-  return launch_status(paa::paged_decode(q, k_cache, v_cache, fp8, k_scale, v_scale, block_table, seq_lens, o, lse,
-                                         num_seqs, H, Hkv, d, max_pages_per_seq, num_pages, scale, ws_o, ws_lse,
-                                         ws_range, parts, (int)w.slots, stream));
-}
-
-}  // namespace
 
 int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
                       const int32_t* seq_lens, void* o, float* lse, int num_seqs, int H, int Hkv, int d, int page_size,
@@ -189,8 +215,6 @@ int paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_cach
   return decode_call(q, k_cache, v_cache, true, k_scale, v_scale, block_table, seq_lens, o, lse, num_seqs, H, Hkv, d,
                      page_size, max_pages_per_seq, num_pages, scale, workspace, workspace_bytes, stream);
 }
-
-// ---- the decode step as a replayable hipGraph ----
 
 int paged_prefill(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                   const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_start, void* o, float* lse,
@@ -220,30 +244,7 @@ int paged_prefill(const void* q, const void* k_new, const void* v_new, void* k_c
                                                scale, stream));
 }
 
-namespace {
-struct DecodeGraph {
-  hipGraph_t graph;
-  hipGraphExec_t exec;
-};
-
-// The same checks as paged_attn_decode, for one call of a graph (nothing is launched).
-int check_decode_call(const attn_decode_call& c) {
-  if (c.num_seqs < 0 || c.H < 1 || c.Hkv < 1 || c.H % c.Hkv != 0 || c.max_pages_per_seq < 0 || c.num_pages < 0)
-    return ATTN_ERR_INVALID_SHAPE;
-  if (c.d != 64 && c.d != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
-  if (c.page_size != 16) return ATTN_ERR_UNSUPPORTED_PAGE_SIZE;
-  if (c.H / c.Hkv > 16) return ATTN_ERR_UNSUPPORTED_GROUP;
-  if (c.kv_fp8 != 0 && c.kv_fp8 != 1) return ATTN_ERR_INVALID_SHAPE;
-  if (!scale_ok(c.scale) || (c.kv_fp8 && (!scale_ok(c.k_scale) || !scale_ok(c.v_scale)))) return ATTN_ERR_INVALID_SCALE;
-  if (c.num_seqs == 0) return ATTN_OK;
-  if (!c.q || !c.k_cache || !c.v_cache || (!c.block_table && c.max_pages_per_seq > 0) || !c.seq_lens || !c.o ||
-      !c.workspace)
-    return ATTN_ERR_NULL_POINTER;
-  if (c.workspace_bytes < paged_attn_decode_workspace_size(c.num_seqs, c.H, c.d, c.page_size, c.max_pages_per_seq))
-    return ATTN_ERR_WORKSPACE_TOO_SMALL;
-  return ATTN_OK;
-}
-}  // namespace
+// ---- the decode step as a replayable hipGraph ----
 
 int paged_attn_decode_graph_create(const attn_decode_call* calls, int num_calls, hipStream_t capture_stream,
                                    void** graph_out) {
@@ -263,19 +264,22 @@ int paged_attn_decode_graph_create(const attn_decode_call* calls, int num_calls,
   int rc = ATTN_OK;
   for (int i = 0; i < num_calls && rc == ATTN_OK; ++i) {
     const attn_decode_call& c = calls[i];
-    rc = decode_call(c.q, c.k_cache, c.v_cache, c.kv_fp8 != 0, c.k_scale, c.v_scale, c.block_table, c.seq_lens, c.o,
-                     c.lse, c.num_seqs, c.H, c.Hkv, c.d, c.page_size, c.max_pages_per_seq, c.num_pages, c.scale,
-                     c.workspace, c.workspace_bytes, capture_stream);
+    rc = launch_decode(c.q, c.k_cache, c.v_cache, c.kv_fp8 != 0, c.k_scale, c.v_scale, c.block_table, c.seq_lens,
+                       c.o, c.lse, c.num_seqs, c.H, c.Hkv, c.d, c.max_pages_per_seq, c.num_pages, c.scale, c.workspace,
+                       capture_stream);
   }
   hipGraph_t graph = nullptr;
   const hipError_t end = hipStreamEndCapture(capture_stream, &graph);  // always end the capture
+  // Every argument was checked before the capture began, so any failure from here on is the runtime's
+  // (ATTN_ERR_LAUNCH); a graph that cannot be released is reported the same way.
   if (rc != ATTN_OK || end != hipSuccess || graph == nullptr) {
-    if (graph != nullptr) hipGraphDestroy(graph);
-    return rc != ATTN_OK ? rc : ATTN_ERR_LAUNCH;
+    const bool released = graph == nullptr || hipGraphDestroy(graph) == hipSuccess;
+    return released && rc != ATTN_OK ? rc : ATTN_ERR_LAUNCH;
   }
   hipGraphExec_t exec = nullptr;
   if (hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess) {
-    hipGraphDestroy(graph);
+    const hipError_t released = hipGraphDestroy(graph);
+    (void)released;  // the call has failed (ATTN_ERR_LAUNCH) whether or not the graph could be released
     return ATTN_ERR_LAUNCH;
   }
   *graph_out = new DecodeGraph{graph, exec};

@@ -673,4 +673,54 @@ def pin_fp8_decode_scales_enter_linearly():
     assert np.allclose(o, o2, rtol=0, atol=1e-13) and np.allclose(l, l2, rtol=0, atol=1e-13)
 
 
+
+def pin_fp8_rows_equal_full():
+    """attention_fp8_rows returns exactly the selected rows of attention_fp8 (the same dequantisation,
+    V taken back from its transpose the same way), causal and not, with grouped KV heads."""
+    q8, k8, vt8, qs, ks, vs = _fp8_case(2, 6, 2, 48, 16, 64)
+    rows = [(0, 0, 0), (1, 5, 47), (0, 3, 16), (1, 2, 31), (0, 4, 1), (1, 0, 46)]
+    for causal in (False, True):
+        o, lse = oracle.attention_fp8(q8, k8, vt8, causal, 0.3, qs, ks, vs)
+        ro, rl = oracle.attention_fp8_rows(q8, k8, vt8, causal, 0.3, qs, ks, vs, rows)
+        for n, (b, h, i) in enumerate(rows):
+            assert np.allclose(ro[n], o[b, h, i], rtol=0, atol=1e-14)
+            assert abs(rl[n] - lse[b, h, i]) < 1e-14
+
+
+def pin_decode_seqs_subset_equals_full():
+    """paged_decode and paged_decode_fp8 with seqs= return the full call's rows of those sequences, in the
+    order asked for (repeats included)."""
+    H, Hkv, d = 4, 2, 8
+    tables = [[5, 0, 3], [1, 7, -1], [6, 2, 4]]
+    lens = [45, 20, 33]
+    rng = np.random.default_rng(31)
+    kc, vc = rng.standard_normal((8, 16, Hkv, d)), rng.standard_normal((8, 16, Hkv, d))
+    q = _rand((3, H, d), 32)
+    bt = np.array(tables, dtype=np.int32)
+    o, lse = oracle.paged_decode(q, kc, vc, bt, lens, 0.4)
+    for seqs in ([2, 0], [1], [2, 2, 1, 0]):
+        so, sl = oracle.paged_decode(q, kc, vc, bt, lens, 0.4, seqs=seqs)
+        assert so.shape == (len(seqs), H, d)
+        assert np.array_equal(so, o[seqs]) and np.array_equal(sl, lse[seqs])
+    q, k8, v8, table, lens8 = _fp8_decode_case(52)
+    o, lse = oracle.paged_decode_fp8(q, k8, v8, 0.5, 2.0, table, lens8, 0.7)
+    for seqs in ([2, 0], [1, 1]):
+        so, sl = oracle.paged_decode_fp8(q, k8, v8, 0.5, 2.0, table, lens8, 0.7, seqs=seqs)
+        assert np.array_equal(so, o[seqs]) and np.array_equal(sl, lse[seqs])
+
+
+def pin_chunked_seqs_subset_equals_full():
+    """paged_prefill with seqs= returns the full call's chunk rows of those sequences, concatenated in the
+    order asked for, and the same appended caches."""
+    c = _chunked_case([40, 0, 17], [9, 21, 16], 4, 2, 8, 12, 33)
+    o, lse, kc, vc = _run_chunked(c, 0.45)
+    qs = c["q_start"]
+    for seqs in ([2, 0], [1], [0, 2, 1]):
+        so, sl, skc, svc = oracle.paged_prefill(c["q"], c["k_new"], c["v_new"], c["kc"], c["vc"], c["bt"], c["ctx"],
+                                                qs, 0.45, seqs=seqs)
+        want = np.concatenate([np.arange(qs[s], qs[s + 1]) for s in seqs])
+        assert np.array_equal(so, o[want]) and np.array_equal(sl, lse[want])
+        assert np.array_equal(skc, kc, equal_nan=True) and np.array_equal(svc, vc, equal_nan=True)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

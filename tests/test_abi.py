@@ -6,8 +6,11 @@ from __future__ import annotations
 
 import ctypes
 import os
+import shutil
+import subprocess
 
 import pytest
+import torch
 
 import paged_attention_attn_amd as paa
 from paged_attention_attn_amd import _binding
@@ -31,6 +34,18 @@ def test_exports_every_declared_symbol(L):
                           "paged_attn_decode_graph_destroy", "attn_status_string"}
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_exports_exactly_the_declared_symbols(L):
+    """The library's dynamic symbol table defines the declared entry points and nothing else: no helper,
+    no C++ internal, no compiler-generated global."""
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not installed")
+    out = subprocess.run([nm, "-D", "--defined-only", paa.LIB_PATH], check=True, capture_output=True,
+                         text=True).stdout
+    defined = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert defined == set(paa.declared_functions())
 
 
 def test_status_strings(L):
@@ -144,6 +159,8 @@ def test_decode_graph_validation(L):
     assert create([call(scale=-1.0)]) == SCALE
     assert create([call(block_table=None)]) == NULL
     assert create([call(kv_fp8=2)]) == SHAPE
+    assert create([call(q=0x10004)]) == ALIGN  # the graph checks exactly what an eager call checks
+    assert create([call(max_pages_per_seq=1 << 28)]) == LARGE  # token positions past 2^31
     assert create([call(kv_fp8=1, k_scale=0.0, v_scale=1.0)]) == SCALE  # an FP8 call's scales are checked
     assert create([call(kv_fp8=1, k_scale=1.0, v_scale=float("nan"))]) == SCALE
     assert create([call(kv_fp8=0, k_scale=0.0, v_scale=0.0), call(d=96)]) == HEAD_DIM  # ... a bf16 call's are not
@@ -211,3 +228,75 @@ def test_fp8_validation(L):
         assert L.attn_fwd_fp8(*base, *bad, None) == SCALE
     assert L.attn_fwd_fp8(None, P, P, P, None, 1, 8, 2, 64, 128, 1, 0.1, 1.0, 1.0, 1.0, None) == NULL
     assert L.attn_fwd_fp8(None, None, None, None, None, 0, 8, 2, 64, 128, 1, 0.1, 1.0, 1.0, 1.0, None) == ATTN_OK
+
+
+# ---- the Python binding refuses output buffers of the wrong shape (before any device check) ----
+
+def _bf(*shape):
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def _expect_shape_error(fn, name):
+    with pytest.raises(ValueError, match=f"{name} must have shape"):
+        fn()
+
+
+def _expect_device_error(fn):
+    with pytest.raises(ValueError, match="must be on a GPU"):
+        fn()
+
+
+def test_binding_prefill_output_shapes():
+    q, k, v = _bf(1, 4, 8, 64), _bf(1, 2, 8, 64), _bf(1, 2, 8, 64)
+    for entry in (paa.attn_fwd, lambda *a, **kw: paa.attn_fwd_window(*a[:3], 4, 0, **kw)):
+        call = lambda **kw: entry(q, k, v, True, **kw) if entry is paa.attn_fwd else entry(q, k, v, **kw)  # noqa
+        _expect_shape_error(lambda: call(out=_bf(1, 4, 7, 64)), "out")
+        _expect_shape_error(lambda: call(lse=torch.zeros(1, 4, 7)), "lse")
+        _expect_shape_error(lambda: call(lse=torch.zeros(4, 8)), "lse")
+        _expect_device_error(lambda: call(out=_bf(1, 4, 8, 64), lse=torch.zeros(1, 4, 8)))
+    _expect_shape_error(lambda: paa.attn_fwd(q, _bf(1, 2, 9, 64), v, True), "k")
+    _expect_shape_error(lambda: paa.attn_fwd(q, k, _bf(1, 2, 8, 32), True), "v")
+    f = lambda t: torch.zeros(t, dtype=torch.float32)  # noqa: E731
+    _expect_shape_error(lambda: paa.attn_fwd_f32(f((1, 4, 8, 64)), f((1, 2, 8, 64)), f((1, 2, 8, 64)), True,
+                                                 out=f((1, 4, 8, 32))), "out")
+
+
+def test_binding_fp8_output_shapes():
+    u = lambda *s: torch.zeros(s, dtype=torch.uint8)  # noqa: E731
+    q, k, vt = u(1, 4, 16, 64), u(1, 2, 16, 64), u(1, 2, 64, 16)
+    _expect_shape_error(lambda: paa.attn_fwd_fp8(q, k, vt, True, out=_bf(1, 4, 15, 64)), "out")
+    _expect_shape_error(lambda: paa.attn_fwd_fp8(q, k, vt, True, lse=torch.zeros(1, 4, 15)), "lse")
+    _expect_shape_error(lambda: paa.attn_fwd_fp8(q, k, u(1, 2, 16, 64), True), "v_t")
+    _expect_device_error(lambda: paa.attn_fwd_fp8(q, k, vt, True, out=_bf(1, 4, 16, 64),
+                                                  lse=torch.zeros(1, 4, 16)))
+
+
+def test_binding_decode_output_shapes():
+    i32 = lambda *s: torch.zeros(s, dtype=torch.int32)  # noqa: E731
+    q, kc, vc, bt, lens = _bf(3, 8, 128), _bf(10, 16, 2, 128), _bf(10, 16, 2, 128), i32(3, 4), i32(3)
+    for entry, extra in ((paa.paged_attn_decode, ()), ):
+        _expect_shape_error(lambda: entry(q, kc, vc, bt, lens, *extra, out=_bf(2, 8, 128)), "out")
+        _expect_shape_error(lambda: entry(q, kc, vc, bt, lens, *extra, lse=torch.zeros(3, 4)), "lse")
+        _expect_shape_error(lambda: entry(q, kc, vc, bt, i32(2), *extra), "seq_lens")
+        _expect_shape_error(lambda: entry(q, kc, vc, i32(2, 4), lens, *extra), "block_table")
+        _expect_shape_error(lambda: entry(q, kc, _bf(10, 16, 2, 64), bt, lens, *extra), "v_cache")
+        _expect_device_error(lambda: entry(q, kc, vc, bt, lens, *extra, out=_bf(3, 8, 128),
+                                           lse=torch.zeros(3, 8)))
+    u8 = torch.zeros((10, 16, 2, 128), dtype=torch.uint8)
+    _expect_shape_error(lambda: paa.paged_attn_decode_fp8(q, u8, u8, bt, lens, 1.0, 1.0, out=_bf(3, 8, 64)), "out")
+    _expect_shape_error(lambda: paa.paged_attn_decode_fp8(q, u8, u8, bt, lens, 1.0, 1.0,
+                                                          lse=torch.zeros(8, 3)), "lse")
+    with pytest.raises(ValueError, match="out must have shape"):  # a graph call is checked the same way
+        paa.PagedDecodeGraph([dict(q=q, k_cache=kc, v_cache=vc, block_table=bt, seq_lens=lens, out=_bf(3, 8, 64))])
+
+
+def test_binding_paged_prefill_output_shapes():
+    i32 = lambda *s: torch.zeros(s, dtype=torch.int32)  # noqa: E731
+    q, kn, vn = _bf(20, 8, 64), _bf(20, 2, 64), _bf(20, 2, 64)
+    kc, vc, bt, ctx, qs = _bf(10, 16, 2, 64), _bf(10, 16, 2, 64), i32(2, 5), i32(2), i32(3)
+    call = lambda **kw: paa.paged_prefill(q, kn, vn, kc, vc, bt, ctx, qs, **kw)  # noqa: E731
+    _expect_shape_error(lambda: call(out=_bf(20, 8, 32)), "out")
+    _expect_shape_error(lambda: call(lse=torch.zeros(20, 4)), "lse")
+    _expect_shape_error(lambda: paa.paged_prefill(q, kn, vn, kc, vc, bt, ctx, i32(2)), "q_start")
+    _expect_shape_error(lambda: paa.paged_prefill(q, _bf(19, 2, 64), vn, kc, vc, bt, ctx, qs), "k_new")
+    _expect_device_error(lambda: call(out=_bf(20, 8, 64), lse=torch.zeros(20, 8)))

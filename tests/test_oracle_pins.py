@@ -95,6 +95,8 @@ MUTANTS = {
     "chunk_positions_reversed": ("_chunk_positions", lambda ctx, n: ctx + np.arange(n)[::-1]),
     "fp8_exponent_bias_8": ("e4m3_bits_to_f64", _mut_e4m3_bias8),
     "fp8_v_not_transposed": ("_dequant_fp8", _mut_dequant_no_transpose),
+    "seqs_subset_ignored": ("_selected", lambda n, seqs: range(n)),
+    "seqs_subset_reordered": ("_selected", lambda n, seqs: range(n) if seqs is None else sorted(set(seqs))),
 }
 
 
