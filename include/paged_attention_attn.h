@@ -49,7 +49,9 @@ enum {
                                          2 GiB a kernel reads through one buffer resource */
   ATTN_ERR_UNSUPPORTED_GROUP = 8,     /* decode: more than 16 query heads per KV head */
   ATTN_ERR_LAUNCH = 9,                /* hipGetLastError reported a failed launch */
-  ATTN_ERR_INVALID_SCALE = 10         /* scale is not a finite positive number */
+  ATTN_ERR_INVALID_SCALE = 10,        /* scale is not a finite positive number */
+  ATTN_ERR_SCRATCH_TOO_SMALL = 11     /* paged_attn_decode_no_alloc: the call needs more workspace
+                                         than ATTN_DECODE_SCRATCH_BYTES */
 };
 
 /*
@@ -221,6 +223,29 @@ ATTN_API int paged_attn_decode(const void* q, const void* k_cache, const void* v
                       const int32_t* seq_lens, void* o, float* lse, int num_seqs, int H, int Hkv, int d, int page_size,
                       int max_pages_per_seq, int num_pages, float scale, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
+
+/*
+ * paged_attn_decode_no_alloc — paged_attn_decode for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments, layouts, rules and
+ * results, without the workspace arguments.  Its split-KV partials go to a
+ * fixed device array of ATTN_DECODE_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends; the call allocates nothing.
+ * A call whose workspace (paged_attn_decode_workspace_size) would exceed that
+ * size returns ATTN_ERR_SCRATCH_TOO_SMALL before anything is launched (at
+ * d = 128, num_seqs * H up to about 31000 fits).  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (on different
+ * streams, or from different threads) race and must be ordered by the
+ * caller.  Nothing in the array needs clearing between calls.  The device
+ * address of the array is looked up on the first call on each device, with
+ * that device made current for the lookup (the caller's current device is
+ * restored).
+ */
+#define ATTN_DECODE_SCRATCH_BYTES (32u << 20)
+ATTN_API int paged_attn_decode_no_alloc(const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                                        int num_seqs, int H, int Hkv, int d, int page_size, int max_pages_per_seq,
+                                        int num_pages, float scale, hipStream_t stream);
 
 /*
  * paged_attn_decode_fp8 — paged_attn_decode over an FP8 KV cache: k_cache and

@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     lib,
     paged_attn_decode,
     paged_attn_decode_fp8,
+    paged_attn_decode_no_alloc,
     paged_attn_decode_workspace_size,
     paged_prefill,
 )

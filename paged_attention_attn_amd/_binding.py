@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_decode_workspace_size.restype = sz
         L.paged_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
         L.paged_attn_decode.restype = i
+        L.paged_attn_decode_no_alloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+        L.paged_attn_decode_no_alloc.restype = i
         L.paged_attn_decode_fp8.argtypes = [vp, vp, vp, f, f, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
         L.paged_attn_decode_fp8.restype = i
         L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, f, vp]
@@ -260,7 +262,7 @@ def paged_attn_decode_workspace_size(num_seqs: int, H: int, d: int, page_size: i
 
 
 def _decode_args(q, k_cache, v_cache, block_table, seq_lens, scale, num_pages, workspace, out, lse,
-                 cache_dtype=torch.bfloat16):
+                 cache_dtype=torch.bfloat16, need_workspace=True):
     """Checks the decode tensors and fills in the defaults; returns the C argument list (without a stream)."""
     for t, name, nd in ((q, "q", 3), (k_cache, "k_cache", 4), (block_table, "block_table", 2)):
         _dims(t, name, nd)
@@ -284,10 +286,11 @@ def _decode_args(q, k_cache, v_cache, block_table, seq_lens, scale, num_pages, w
     _require(seq_lens, "seq_lens", torch.int32, 1, dev)
     if num_pages is None:
         num_pages = P
-    need = paged_attn_decode_workspace_size(S, H, d, page_size, max_pages)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    _require(workspace, "workspace", torch.uint8, 1, dev)
+    if need_workspace:
+        need = paged_attn_decode_workspace_size(S, H, d, page_size, max_pages)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        _require(workspace, "workspace", torch.uint8, 1, dev)
     if out is None:
         out = torch.empty_like(q)
     _require(out, "out", torch.bfloat16, 3, dev)
@@ -296,7 +299,8 @@ def _decode_args(q, k_cache, v_cache, block_table, seq_lens, scale, num_pages, w
     if scale is None:
         scale = d ** -0.5
     args = [_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse), S, H,
-            Hkv, d, page_size, max_pages, int(num_pages), float(scale), _ptr(workspace), workspace.numel()]
+            Hkv, d, page_size, max_pages, int(num_pages), float(scale), _ptr(workspace),
+            workspace.numel() if workspace is not None else 0]
     return args, workspace, out, lse
 
 
@@ -311,6 +315,17 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, scale: float |
     args, _, out, lse = _decode_args(q, k_cache, v_cache, block_table, seq_lens, scale, num_pages, workspace, out,
                                      lse)
     _check(lib().paged_attn_decode(*args, _stream(q.device)))
+    return out, lse
+
+
+def paged_attn_decode_no_alloc(q, k_cache, v_cache, block_table, seq_lens, scale: float | None = None,
+                               num_pages=None, out=None, lse=None):
+    """:func:`paged_attn_decode` with the library's fixed per-GPU scratch as its workspace (C:
+    paged_attn_decode_no_alloc): the C call allocates nothing.  Pass ``out`` (and ``lse``) to keep this
+    wrapper from allocating them.  Calls that overlap on one GPU race on that scratch."""
+    args, _, out, lse = _decode_args(q, k_cache, v_cache, block_table, seq_lens, scale, num_pages, None, out, lse,
+                                     need_workspace=False)
+    _check(lib().paged_attn_decode_no_alloc(*args[:15], _stream(q.device)))
     return out, lse
 
 

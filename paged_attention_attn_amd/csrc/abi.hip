@@ -4,10 +4,42 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/paged_attention_attn.h"
 #include "launch.hpp"
 
 namespace {
+
+// Decode workspace for callers that cannot allocate (paged_attn_decode_no_alloc).  Each GPU the library
+// runs on holds its own copy until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: only the address hipGetSymbolAddress returns for a device is ever passed to a kernel.
+constexpr size_t kScratchBytes = ATTN_DECODE_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// The device address of `scratch` on the device that runs `stream`, looked up once per device with that
+// device current (the caller's current device is restored).
+int scratch_for(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return ATTN_ERR_LAUNCH;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return ATTN_ERR_LAUNCH;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return ATTN_ERR_LAUNCH;
+    if (e != hipSuccess || ptr == nullptr) return ATTN_ERR_LAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -244,6 +276,23 @@ int paged_prefill(const void* q, const void* k_new, const void* v_new, void* k_c
                                                scale, stream));
 }
 
+int paged_attn_decode_no_alloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                               const int32_t* seq_lens, void* o, float* lse, int num_seqs, int H, int Hkv, int d,
+                               int page_size, int max_pages_per_seq, int num_pages, float scale, hipStream_t stream) {
+  // the workspace checks run against a stand-in pointer; the real address is looked up only after every
+  // host-side check has passed
+  const void* stand_in = reinterpret_cast<const void*>(uintptr_t{256});
+  int rc = check_decode(q, k_cache, v_cache, false, 1.f, 1.f, block_table, seq_lens, o, lse, num_seqs, H, Hkv, d,
+                        page_size, max_pages_per_seq, num_pages, scale, stand_in, kScratchBytes);
+  if (rc == ATTN_ERR_WORKSPACE_TOO_SMALL) return ATTN_ERR_SCRATCH_TOO_SMALL;
+  if (rc != ATTN_OK || num_seqs == 0) return rc;
+  void* ws = nullptr;
+  rc = scratch_for(stream, &ws);
+  if (rc != ATTN_OK) return rc;
+  return launch_decode(q, k_cache, v_cache, false, 1.f, 1.f, block_table, seq_lens, o, lse, num_seqs, H, Hkv, d,
+                       max_pages_per_seq, num_pages, scale, ws, stream);
+}
+
 // ---- the decode step as a replayable hipGraph ----
 
 int paged_attn_decode_graph_create(const attn_decode_call* calls, int num_calls, hipStream_t capture_stream,
@@ -313,6 +362,9 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_UNSUPPORTED_GROUP: return "unsupported grouping: at most 16 query heads per KV head in decode";
     case ATTN_ERR_LAUNCH: return "kernel launch or graph operation failed (HIP runtime error)";
     case ATTN_ERR_INVALID_SCALE: return "invalid scale: it must be a finite positive number";
+    case ATTN_ERR_SCRATCH_TOO_SMALL:
+      return "the call needs more than the library's fixed decode scratch (ATTN_DECODE_SCRATCH_BYTES); "
+             "use paged_attn_decode with a caller-supplied workspace";
     default: return "unknown status code";
   }
 }

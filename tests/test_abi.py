@@ -15,7 +15,7 @@ import torch
 import paged_attention_attn_amd as paa
 from paged_attention_attn_amd import _binding
 
-ATTN_OK, NULL, SHAPE, HEAD_DIM, PAGE, WS, ALIGN, LARGE, GROUP, LAUNCH, SCALE = range(11)
+ATTN_OK, NULL, SHAPE, HEAD_DIM, PAGE, WS, ALIGN, LARGE, GROUP, LAUNCH, SCALE, SCRATCH = range(12)
 
 
 @pytest.fixture(scope="module")
@@ -29,7 +29,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = paa.declared_functions()
     assert set(names) == {"attn_fwd", "attn_fwd_f32", "attn_fwd_fp8", "attn_fwd_window", "paged_attn_decode_workspace_size", "paged_prefill",
-                          "paged_attn_decode", "paged_attn_decode_fp8", "paged_attn_decode_graph_create",
+                          "paged_attn_decode", "paged_attn_decode_fp8", "paged_attn_decode_no_alloc",
+                          "paged_attn_decode_graph_create",
                           "paged_attn_decode_graph_launch",
                           "paged_attn_decode_graph_destroy", "attn_status_string"}
     for n in names:
@@ -49,7 +50,7 @@ def test_exports_exactly_the_declared_symbols(L):
 
 
 def test_status_strings(L):
-    for code in range(11):
+    for code in range(12):
         assert paa.attn_status_string(code) != "unknown status code"
     assert paa.attn_status_string(12345) == "unknown status code"
 
@@ -109,6 +110,33 @@ def test_decode_validation(L):
     assert call(scale=float("nan")) == SCALE
     assert call(S=0) == ATTN_OK
     assert call(S=0, q=None, ws=None) == ATTN_OK  # empty: pointers unused
+
+
+def test_decode_no_alloc_validation(L):
+    """The no-allocation decode checks what paged_attn_decode checks and refuses, before anything is
+    launched, a call whose workspace would not fit its fixed 32 MiB scratch (no GPU needed)."""
+    base = dict(q=P, kc=P, vc=P, bt=P, lens=P, o=P, lse=None, S=4, H=8, Hkv=2, d=128, ps=16, mp=10, np_=100,
+                scale=0.1)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.paged_attn_decode_no_alloc(a["q"], a["kc"], a["vc"], a["bt"], a["lens"], a["o"], a["lse"], a["S"],
+                                            a["H"], a["Hkv"], a["d"], a["ps"], a["mp"], a["np_"], a["scale"], None)
+
+    assert call(bt=None) == NULL
+    assert call(Hkv=3) == SHAPE
+    assert call(d=80) == HEAD_DIM
+    assert call(ps=32) == PAGE
+    assert call(H=64, Hkv=2) == GROUP
+    assert call(q=ctypes.c_void_p(0x10004)) == ALIGN
+    assert call(scale=0.0) == SCALE
+    assert call(S=0) == ATTN_OK and call(S=0, q=None) == ATTN_OK
+    limit = 32 << 20
+    # the largest batch of 32-head sequences whose workspace fits, and one more sequence
+    fits = max(S for S in range(1, 2000) if paa.paged_attn_decode_workspace_size(S, 32, 128, 16, 1024) <= limit)
+    assert fits * 32 >= 31000
+    assert call(S=fits + 1, H=32, Hkv=8, mp=1024, np_=40000) == SCRATCH
+    assert call(S=100000, H=32, Hkv=8, mp=1024, np_=40000) == SCRATCH
 
 
 def test_decode_fp8_validation(L):
@@ -300,3 +328,4 @@ def test_binding_paged_prefill_output_shapes():
     _expect_shape_error(lambda: paa.paged_prefill(q, kn, vn, kc, vc, bt, ctx, i32(2)), "q_start")
     _expect_shape_error(lambda: paa.paged_prefill(q, _bf(19, 2, 64), vn, kc, vc, bt, ctx, qs), "k_new")
     _expect_device_error(lambda: call(out=_bf(20, 8, 64), lse=torch.zeros(20, 8)))
+
