@@ -1,19 +1,25 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-One step = one causal bf16 prefill (attn_fwd) of the causal_b4h16n1024d64
-workload (B=4, H=16, N=1024, d=64) followed by one paged decode
-(paged_attn_decode) of the paged_decode_s64h32kv8d128 workload (64 sequences,
-H=32, Hkv=8, d=128, lengths uniform in [512, 8192], 16-token pages in a
-40000-page pool), both on the current stream, inputs resident in HBM.
+One step = one causal bf16 GQA prefill (attn_fwd) of the long workload
+causal_gqa_long_b1h32kv8n16384d128 (B=1, H=32, Hkv=8, N=16384, d=128, Q x4, 1%
+of K rows x8) followed by one paged decode (paged_attn_decode) of
+paged_decode_s64h32kv8d128 (64 sequences, H=32, Hkv=8, d=128, lengths uniform
+in [512, 8192], 16-token pages in a 40000-page pool), both on the current
+stream, inputs resident in HBM.
 
 Prints ONE JSON line.  ``value`` is the prefill throughput in TFLOP/s on
-algorithmic flops (4*d*B*H*visible pairs); the decode object reports GB/s on
-algorithmic bytes (K/V of valid tokens + Q + O + LSE + block-table entries
-and lengths read).  Each call is bracketed by HIP events on the stream it is
-launched on; the call that takes most of the step (the paged decode) gives
-the top-level ``roofline``.  ``cpu_baseline`` times the float64 oracle on the
-host cores on the step's own workload (the oracle is imported only there).
+algorithmic flops (4*d*B*H*visible pairs); the prefill kernel takes most of the
+step, so it gives the top-level ``roofline`` (against the bf16 MFMA peak).  The
+decode object reports GB/s on algorithmic bytes (K/V of valid tokens + Q + O +
+LSE + block-table entries and lengths read); its headline ``value`` is the
+cold-cache rate (the 256 MB last-level cache evicted before each call), the
+warm rate is reported beside it.  Each call is bracketed by HIP events on the
+stream it is launched on.  The other workloads (the short causal d=64 prefill,
+the 4096-token GQA prefill, the windowed, chunked and FP8 paths, the decode
+graph) are secondary entries.  ``cpu_baseline`` times the float64 oracle on the
+host cores on a bounded sample of each workload (the oracle is imported only
+there).
 
 Other modes (used to produce the summaries kept under profiles/):
   --pmc-pass                 a few launches of every kernel plus a plain copy
@@ -55,16 +61,16 @@ COPY_BYTES = 1 << 30       # calibration copy: 1 GiB read + 1 GiB written
 COPY_KERNEL_TAG = "neg_kernel"  # torch's elementwise negate, used as the plain copy kernel
 PMC_CALLS = 3              # calls of each workload in a counter pass
 
-PREFILL_DEFAULT = "causal_b4h16n1024d64"
+PREFILL_DEFAULT = "causal_gqa_long_b1h32kv8n16384d128"
 SMALL_DECODE = "paged_decode_s4h32kv8d128_short"  # launch-bound: eager calls against graph replays
 FP8_MORE = ("fp8_causal_gqa_b2h32kv8n4096d128", "fp8_causal_gqa_long_b1h32kv8n16384d128")
 FP8_DECODE_SUFFIX = "_fp8kv"  # the decode workload over an E4M3 cache
 CHUNKED = "chunked_prefill_s16h32kv8d128_ctx0to4096_q512"  # chunked prefill over a paged cache, with append
-GRAPH_LAYERS = 32
-PREWARM_S = 0.25  # untimed calls of the step before its W warm-up steps (see prewarm)  # decode calls per step in that comparison, each with its own KV cache
+GRAPH_LAYERS = 32  # decode calls per step in the graph comparison, each with its own KV cache
+PREWARM_S = 0.25  # untimed calls of the step before its W warm-up steps (see prewarm)
 DECODE_DEFAULT = "paged_decode_s64h32kv8d128"
-PREFILL_MORE = ("causal_gqa_b2h32kv8n4096d128", "causal_gqa_long_b1h32kv8n16384d128",
-                "window_gqa_b1h32kv8n16384d128_w4096_g64")
+PREFILL_MORE = ("causal_b4h16n1024d64", "causal_gqa_b2h32kv8n4096d128", "window_gqa_b1h32kv8n16384d128_w4096_g64")
+TINY_F32 = "tiny_f32_b1h2n128d64"
 
 
 # ----------------------------------------------------------------- algorithmic counts
@@ -319,38 +325,70 @@ class ChunkedCase:
 
 # ----------------------------------------------------------------- CPU baseline (oracle)
 
-def cpu_baseline(pc, dc, min_seconds=10.0):
-    """The float64 oracle on the host cores over the step's own workload.
+def _blas_threads() -> int:
+    from threadpoolctl import threadpool_info
+    return sum(p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas") or 1
 
-    Sample: the whole prefill workload and the whole decode workload, repeated
-    until at least ``min_seconds`` have passed (mean per pass reported).
+
+def cpu_baseline(seed, dc, min_seconds=10.0):
+    """The float64 oracle, as it stands, on the host cores, on a bounded sample of every workload.
+
+    Per workload the sample is: the whole tiny fp32 and d=64 causal prefills; one query head (with its
+    KV head) of the 4096- and 16384-token GQA prefills, whose heads all cost the same; the whole paged
+    decode.  Each sample is repeated until ``min_seconds`` have passed in total and the mean per pass is
+    reported, scaled to the metric's unit on the sample's own algorithmic work.  ``value`` is the rate on
+    the step's prefill workload (the long GQA prefill), ``decode`` the rate on the step's decode.
     """
     import oracle
-    from threadpoolctl import threadpool_info
+    from workloads import WORKLOADS, PrefillWorkload, prefill_inputs
 
-    threads = sum(p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas") or 1
-    pw, dw, pa, da = pc.w, dc.w, pc.a, dc.a
-    t_pre = t_dec = 0.0
+    def head_sample(name, n_heads):
+        w = WORKLOADS[name]
+        a = prefill_inputs(w, seed=seed)
+        g = w.H // w.Hkv
+        q = a["q"][:1, :n_heads]
+        k, v = a["k"][:1, : -(-n_heads // g)], a["v"][:1, : -(-n_heads // g)]
+        sw = PrefillWorkload(w.name + "_sample", 1, n_heads, k.shape[1], w.N, w.d, w.causal)
+        return sw, (lambda: oracle.attention(q, k, v, w.causal, a["scale"])), w
+
+    samples = []
+    for name, heads in ((TINY_F32, None), ("causal_b4h16n1024d64", None), ("causal_gqa_b2h32kv8n4096d128", 1),
+                        (PREFILL_DEFAULT, 1)):
+        if heads is None:
+            w = WORKLOADS[name]
+            a = prefill_inputs(w, seed=seed)
+            samples.append((name, f"whole workload", w, prefill_flops(w),
+                            (lambda a=a, w=w: oracle.attention(a["q"], a["k"], a["v"], w.causal, a["scale"]))))
+        else:
+            sw, fn, w = head_sample(name, heads)
+            samples.append((name, f"{heads} of {w.H} query heads (batch entry 0)", sw, prefill_flops(sw), fn))
+    da, dw = dc.a, dc.w
+    samples.append((dw.name, "whole workload", dw, decode_bytes(dw, da["seq_lens"]),
+                    lambda: oracle.paged_decode(da["q"], da["k_cache"], da["v_cache"], da["block_table"],
+                                                da["seq_lens"], da["scale"])))
+    per, times = [], [0.0] * len(samples)
     passes = 0
-    while passes == 0 or t_pre + t_dec < min_seconds:
-        t0 = time.perf_counter()
-        oracle.attention(pa["q"], pa["k"], pa["v"], pw.causal, pa["scale"])
-        t1 = time.perf_counter()
-        oracle.paged_decode(da["q"], da["k_cache"], da["v_cache"], da["block_table"], da["seq_lens"], da["scale"])
-        t2 = time.perf_counter()
-        t_pre += t1 - t0
-        t_dec += t2 - t1
+    while passes == 0 or sum(times) < min_seconds:
+        for i, (*_, fn) in enumerate(samples):
+            t0 = time.perf_counter()
+            fn()
+            times[i] += time.perf_counter() - t0
         passes += 1
-    t_pre /= passes
-    t_dec /= passes
-    pre_tf = prefill_flops(pw) / t_pre / 1e12
-    dec_gbs = decode_bytes(dw, da["seq_lens"]) / t_dec / 1e9
-    return {"value": round(pre_tf, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"whole {pw.name} prefill ({t_pre:.2f} s) and whole {dw.name} decode ({t_dec:.2f} s) "
-                      f"per pass, {passes} passes, mean reported",
-            "decode": {"value": round(dec_gbs, 4), "unit": "GB/s"},
-            "ms_per_step": round(1e3 * (t_pre + t_dec), 1),
-            "cpu": _cpu_model()}
+    for (name, what, w, work, _), t in zip(samples, times):
+        t /= passes
+        if name == dw.name:
+            per.append({"workload": name, "sample": what, "seconds": round(t, 4), "value": round(work / t / 1e9, 4),
+                        "unit": "GB/s"})
+        else:
+            per.append({"workload": name, "sample": what, "seconds": round(t, 4),
+                        "value": round(work / t / 1e12, 6), "unit": "TFLOP/s"})
+    head = next(e for e in per if e["workload"] == PREFILL_DEFAULT)
+    dec = next(e for e in per if e["workload"] == dw.name)
+    return {"value": head["value"], "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"{PREFILL_DEFAULT}: {head['sample']} ({head['seconds']:.2f} s per pass); the other "
+                      f"workloads' samples in per_config; {passes} passes, mean reported",
+            "decode": {"value": dec["value"], "unit": "GB/s", "sample": dec["sample"]},
+            "per_config": per, "cpu": _cpu_model()}
 
 
 def _cpu_model() -> str:
@@ -410,7 +448,6 @@ def run_bench(args, torch, paa) -> dict:
     pre_tf = pf / (pre_ms * 1e-3) / 1e12
     dec_gbs = db / (dec_ms * 1e-3) / 1e9
     pre_roof = roofline("mfma", pre_tf, PEAK_BF16_TFLOPS, "TFLOP/s", read_traffic(pw.name), read_mfma_busy(pw.name))
-    dec_roof = roofline("hbm", dec_gbs, PEAK_HBM_GBS, "GB/s", read_traffic(dw.name))
 
     # ---- decode with the 256 MB last-level cache evicted before every call ----
     # (by reading a 512 MB buffer: a read leaves clean lines, so no write-back lands inside the timed call)
@@ -428,6 +465,10 @@ def run_bench(args, torch, paa) -> dict:
             cold.append(a.elapsed_time(b))
     del scratch
     cold_ms = statistics.median(cold)
+    cold_gbs = db / (cold_ms * 1e-3) / 1e9
+    dec_roof = roofline("hbm", cold_gbs, PEAK_HBM_GBS, "GB/s", read_traffic(dw.name))
+    warm_roof = roofline("hbm", dec_gbs, PEAK_HBM_GBS, "GB/s", read_traffic(dw.name))
+    _log(f"{dw.name}: cold {cold_ms * 1e3:.1f} us ({cold_gbs:.0f} GB/s), warm {dec_ms * 1e3:.1f} us")
 
     # ---- a decode step of many layers on a small batch, where launch overhead matters: one eager call per
     # layer against one replay of a graph holding every layer's call ----
@@ -523,7 +564,7 @@ def run_bench(args, torch, paa) -> dict:
 
     base = None
     if not args.no_cpu_baseline:
-        base = cpu_baseline(pc, dc)
+        base = cpu_baseline(args.seed, dc)
         _log(f"cpu baseline: {base['sample']}")
 
     props = torch.cuda.get_device_properties(0)
@@ -547,14 +588,17 @@ def run_bench(args, torch, paa) -> dict:
                               "L": [dw.L_lo, dw.L_hi], "page_size": dw.page_size, "num_pages": dw.num_pages,
                               "tokens": int(dc.a["seq_lens"].sum())},
                    "seed": args.seed},
-        "roofline": dict(dec_roof, kernel="paged_attn_decode: decode_partial_kernel + decode_reduce_kernel",
-                         workload=dw.name, bytes_per_call=round(db)),
+        "roofline": dict(pre_roof, kernel="attn_fwd: prefill_pp_kernel<128, causal, 4 heads, 2 stages>",
+                         workload=pw.name, flops_per_call=round(pf)),
+        "targets": {"prefill_frac_of_bf16_peak": 0.5, "decode_frac_of_hbm_peak": 0.7},
         "prefill": {"workload": pw.name, "ms": round(pre_ms, 5), "value": round(pre_tf, 3), "unit": "TFLOP/s",
                     "algorithmic_gflop": round(pf / 1e9, 4), "algorithmic_mb": round(prefill_bytes(pw) / 1e6, 3),
                     "roofline": pre_roof},
-        "decode": {"workload": dw.name, "ms": round(dec_ms, 5), "value": round(dec_gbs, 2), "unit": "GB/s",
-                   "algorithmic_gb": round(db / 1e9, 5), "roofline": dec_roof,
-                   "cold_ms": round(cold_ms, 5), "cold_value": round(db / (cold_ms * 1e-3) / 1e9, 2)},
+        "decode": {"workload": dw.name, "ms": round(cold_ms, 5), "value": round(cold_gbs, 2), "unit": "GB/s",
+                   "caches": "evicted before each call (512 MB read between calls)",
+                   "algorithmic_gb": round(db / 1e9, 5), "roofline": dict(dec_roof, kernel=(
+                       "paged_attn_decode: decode_partial_kernel + decode_reduce_kernel"), bytes_per_call=round(db)),
+                   "warm_ms": round(dec_ms, 5), "warm_value": round(dec_gbs, 2), "warm_roofline": warm_roof},
         "prefill_more": more,
         "chunked_prefill": chunked,
         "fp8_prefill": fp8,

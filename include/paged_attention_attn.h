@@ -111,9 +111,14 @@ ATTN_API int attn_fwd_f32(const float* q, const float* k, const float* v, float*
  * FlashAttention: The Milestone of Fusion").  The inputs are q_scale * Q,
  * k_scale * K and v_scale * V; both products use the 8-bit matrix
  * instructions, with fp32 accumulation and softmax.  The probabilities are
- * rounded to E4M3 before the product with V (relative error up to 2^-4 each),
- * so O agrees with exact attention of the scaled inputs to within
- * 2^-4 * max|v_scale * V| per element; LSE is as precise as attn_fwd's.
+ * scaled by 2^4 (so those down to 2^-10 of the row's running maximum stay in
+ * E4M3's normal range) and rounded to E4M3 before the product with V
+ * (relative error up to 2^-4 each); O is divided by the sum of the same
+ * rounded probabilities, so it is a weighted mean of V rows (identical rows
+ * come back unchanged) and differs from exact attention of the scaled
+ * inputs by at most about 2^-4 * sum_j p_ij |v_j - O_i| per element.  LSE
+ * uses the unrounded probabilities and is as precise as attn_fwd's, up to
+ * the 8-bit matrix instruction's accumulation error in the scores.
  *
  *   q    [B, H, N, d] E4M3
  *   k    [B, Hkv, N, d] E4M3

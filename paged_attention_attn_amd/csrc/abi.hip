@@ -71,7 +71,8 @@ int check_prefill(const void* q, const void* k, const void* v, const void* o, co
     return ATTN_ERR_MISALIGNED;
   if (elems(B, H, N, d) < 0) return ATTN_ERR_TOO_LARGE;
   // query tiles x heads x batch must fit one 1-D grid
-  if ((long long)B * H * ((N + 31) / 32) > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
+  const long long units = elems(B, H, ((long long)N + 31) / 32, 1);
+  if (units < 0 || units > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
   // the kernels read one (batch entry, KV head) of K or V through a buffer resource, whose size
   // (and the lanes' offsets into it) are below 2^31 bytes
   if ((long long)N * d * 2 > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
@@ -268,7 +269,8 @@ int paged_prefill(const void* q, const void* k_new, const void* v_new, void* k_c
   if ((long long)max_pages_per_seq * page_size > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
   if (elems(num_pages, page_size, Hkv, d) < 0 || elems(num_seqs, max_pages_per_seq, 1, 1) < 0)
     return ATTN_ERR_TOO_LARGE;
-  if ((long long)num_seqs * H * ((max_q_len + 31) / 32) > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
+  const long long units = elems(num_seqs, H, ((long long)max_q_len + 31) / 32, 1);
+  if (units < 0 || units > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
   // one sequence's chunk rows of k_new / v_new are read through a buffer resource below 2^31 bytes
   if ((long long)max_q_len * Hkv * d * 2 > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
   return launch_status(paa::paged_prefill_bf16(q, k_new, v_new, k_cache, v_cache, block_table, ctx_lens, q_start, o,

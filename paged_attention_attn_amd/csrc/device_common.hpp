@@ -38,6 +38,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
+// acc + the two bf16 values packed in w (one v_dot2 against 1.0 in both halves, fp32 accumulation).
+// The kernels sum the probabilities as rounded to bf16 for the product with V this way, so that O is
+// divided by the same weights its numerator used.
+__device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, 0x3F803F80u), acc,
+                                         false);
+}
+
+// Sum of the 16 bf16 values of four packed operand registers (four chains of four).
+__device__ __forceinline__ float sum_bf16x16(const u32x4_t (&pf)[4]) {
+  float r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r[k] = add_bf16_pair(pf[k][0], 0.f);
+#pragma unroll
+  for (int j = 1; j < 4; ++j)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = add_bf16_pair(pf[k][j], r[k]);
+  return (r[0] + r[1]) + (r[2] + r[3]);
+}
+
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 

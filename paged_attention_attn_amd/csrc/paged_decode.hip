@@ -19,7 +19,9 @@
 //     at a time, keeps a running max / sum / rescaled output for the query
 //     heads of its group (the online softmax of "Kernel Fusion and Custom
 //     Kernels", section 3) and, where its range leaves a sequence, writes that
-//     sequence's partial output (normalised) and log-sum-exp to the workspace.
+//     sequence's partial output and log-sum-exp to the workspace.  The output
+//     is divided by the sum of the probabilities as rounded to bf16 for P.V
+//     (the weights its numerator used), the LSE uses their fp32 sum.
 //     The next two pages are loaded while the current two are computed; K is
 //     loaded straight into the MFMA A layout and V is staged through
 //     wave-private LDS for transposed reads.
@@ -317,7 +319,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeAr
   };
 
   float m_run = -INFINITY;
-  float l_run = 0.f;  // this lane's share of the sum for head r16
+  float l_run = 0.f;   // this lane's share of the sum for head r16
+  float lr_run = 0.f;  // ... and of the same probabilities as rounded to bf16 for P.V (O is divided by it)
   f32x4_t acc[kDBlocks];
 
   Step cur = wk.next(a);
@@ -331,6 +334,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeAr
       seg_lo = cur.p;
       m_run = -INFINITY;
       l_run = 0.f;
+      lr_run = 0.f;
 #pragma unroll
       for (int nb = 0; nb < kDBlocks; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -400,6 +404,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeAr
     l_run = l_run * alpha + psum;
     const u32x4_t pf = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                         pack_bf16x2(p[6], p[7])};
+    lr_run = lr_run * alpha + (add_bf16_pair(pf[0], add_bf16_pair(pf[1], 0.f)) +
+                               add_bf16_pair(pf[2], add_bf16_pair(pf[3], 0.f)));
 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -425,10 +431,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeAr
       // this range's partial of sequence cur.s for head r16: normalised output and log-sum-exp
       float l_tot = l_run + __shfl_xor(l_run, 16);
       l_tot += __shfl_xor(l_tot, 32);
+      float lr_tot = lr_run + __shfl_xor(lr_run, 16);
+      lr_tot += __shfl_xor(lr_tot, 32);
       const int slot = cur.s + blockIdx.x;
       if (head_ok) {
         // a segment whose pages were all rejected has no visible key: zero output, LSE = -inf
-        const float inv_l = l_tot > 0.f ? a.vscale / l_tot : 0.f;
+        const float inv_l = lr_tot > 0.f ? a.vscale / lr_tot : 0.f;
         const size_t base = (size_t)slot * a.H + head;
         float* wo = a.ws_o + base * D;
 #pragma unroll

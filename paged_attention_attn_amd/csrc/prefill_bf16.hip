@@ -28,8 +28,12 @@
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q kept in
 //    VGPRs for the whole kernel), so each lane ends up holding 16 scores of
 //    ONE query row (row l%32; the two half-waves split the keys).  Row max is
-//    a lane-local max plus one permlane32 swap; the row sum stays lane-local
-//    until the epilogue.
+//    a lane-local max plus one permlane32 swap; the row sums stay lane-local
+//    until the epilogue.  Two sums are kept: of the fp32 probabilities (for
+//    the LSE) and of the same probabilities as rounded to bf16 for P.V (one
+//    v_dot2 per packed pair), by which O is divided, so that O is a weighted
+//    mean of V rows with exactly the weights its numerator used (a row held
+//    by one key returns that key's V row).
 //  * O^T = V^T P^T with the same MFMA: B = the lane's own probabilities
 //    (bf16), A = V read with ds_read_b64_tr_b16, and the contraction order of
 //    keys is permuted to match where the score MFMA left each probability.
@@ -446,12 +450,15 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   };
 
   // ---- running state of the lane's row in each block ----
-  float m_run[RB], l_run[RB];  // reference maximum of raw scores (before scale); this lane's share of the sum
+  // reference maximum of raw scores (before scale); this lane's share of the sum of the probabilities
+  // (for the LSE) and of the same probabilities as rounded to bf16 (for O, whose numerator uses them)
+  float m_run[RB], l_run[RB], lr_run[RB];
   f32x16_t acc[RB][kDBlocks];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m_run[rb] = -INFINITY;
     l_run[rb] = 0.f;
+    lr_run[rb] = 0.f;
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db)
       for (int i = 0; i < 16; ++i) acc[rb][db][i] = 0.f;
@@ -494,6 +501,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
       const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_run[rb] - m_new) * a.scale_log2);
       m_run[rb] = m_new;
       l_run[rb] *= alpha;
+      lr_run[rb] *= alpha;
 #pragma unroll
       for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
@@ -520,6 +528,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
                                   pack_bf16x2(p[8 * sh + 4], p[8 * sh + 5]), pack_bf16x2(p[8 * sh + 6], p[8 * sh + 7])};
     }
     l_run[rb] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    lr_run[rb] += sum_bf16x16(pf);
   };
 
   // O^T += V^T P^T for every row block.  PV k-step ks covers keys 16ks..16ks+15 of the tile; logical
@@ -586,12 +595,12 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   for (int j = 0; j < n_iter; j += STAGES) for_stages<0, STAGES>(tile, j, n_iter);
   wait_vmcnt<0>();  // no load may still be writing this workgroup's LDS when it exits
 
-  // ---- epilogue: O = acc / l, LSE = scale * m + ln(l) ----
+  // ---- epilogue: O = acc / (sum of the rounded probabilities), LSE = scale * m + ln(l) ----
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int row = q0 + 32 * rb + l32;
     const float l_tot = l_run[rb] + swap_halves(l_run[rb], half);
-    const float inv_l = 1.f / l_tot;
+    const float inv_l = 1.f / (lr_run[rb] + swap_halves(lr_run[rb], half));
     if (row < n_q) {
       uint16_t* orow = a.o + q_base + (size_t)row * q_stride;
 #pragma unroll
@@ -863,7 +872,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
       voff[db][e] = r * T::kRowBytes + (((col / 8) ^ swz<D>(r)) * 16) + (col % 8) * 2;
     }
 
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f, lr_run = 0.f;  // lr: sum of the probabilities as rounded for P.V
   f32x16_t acc[kDBlocks];
 #pragma unroll
   for (int db = 0; db < kDBlocks; ++db)
@@ -947,6 +956,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
       const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_run - m_new) * a.scale_log2);
       m_run = m_new;
       l_run *= alpha;
+      lr_run *= alpha;
 #pragma unroll
       for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
@@ -968,6 +978,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
                                   pack_bf16x2(p[8 * sh + 4], p[8 * sh + 5]), pack_bf16x2(p[8 * sh + 6], p[8 * sh + 7])};
     }
     l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    lr_run += sum_bf16x16(pf);
   };
 
   // Q and stage 0 have landed (loads after them: stages 1 .. STAGES-1)
@@ -1003,7 +1014,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     // group B's partial state to group A, lane for lane (the same rows, the same accumulator
     // layout), through a stage buffer that is idle now: m, l, then the accumulators
     // one stage array per row block: K stages 0 and 1, then V stages 0 and 1
-    constexpr int kPerWave = (2 + 16 * kDBlocks) * 64;  // floats
+    constexpr int kPerWave = (3 + 16 * kDBlocks) * 64;  // floats
     static_assert(kPerWave * 4 <= kSlots * T::kTileBytes, "a row block's exchange fits in one stage array");
     static_assert(kRowWaves == 4 && STAGES >= 2, "four row blocks, four stage arrays");
     __syncthreads();  // every wave's loads have landed and every tile read is done
@@ -1014,31 +1025,34 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     if (grp == 1) {
       xch[lane] = m_run;
       xch[64 + lane] = l_run;
+      xch[128 + lane] = lr_run;
 #pragma unroll
       for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) xch[128 + (db * 16 + e) * 64 + lane] = acc[db][e];
+        for (int e = 0; e < 16; ++e) xch[192 + (db * 16 + e) * 64 + lane] = acc[db][e];
     }
     __syncthreads();
     if (grp == 1) return;  // group A writes the rows
     const float mb = xch[lane];
     const float lb = xch[64 + lane];
+    const float lrb = xch[128 + lane];
     const float m_new = fmaxf(m_run, mb);
     // a group that saw no visible key has m = -inf and contributes nothing
     const float fa = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * a.scale_log2);
     const float fb = mb == -INFINITY ? 0.f : fast_exp2((mb - m_new) * a.scale_log2);
     m_run = m_new;
     l_run = l_run * fa + lb * fb;
+    lr_run = lr_run * fa + lrb * fb;
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[db][e] = acc[db][e] * fa + xch[128 + (db * 16 + e) * 64 + lane] * fb;
+      for (int e = 0; e < 16; ++e) acc[db][e] = acc[db][e] * fa + xch[192 + (db * 16 + e) * 64 + lane] * fb;
   }
 
-  // ---- epilogue: O = acc / l, LSE = scale * m + ln(l) ----
+  // ---- epilogue: O = acc / (sum of the rounded probabilities), LSE = scale * m + ln(l) ----
   const int row = q0 + l32;
   const float l_tot = l_run + swap_halves(l_run, half);
-  const float inv_l = 1.f / l_tot;
+  const float inv_l = 1.f / (lr_run + swap_halves(lr_run, half));
   if (row < n_q) {
     uint16_t* orow = a.o + q_base + (size_t)row * q_stride;
 #pragma unroll

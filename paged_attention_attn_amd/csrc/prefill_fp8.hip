@@ -6,7 +6,16 @@
 // operands for both products, with per-tensor scales, is the FP8 path of FlashAttention v3
 // ("Kernel Fusion and Custom Kernels", section "3. FlashAttention: The Milestone of Fusion",
 // v3: FP8 for Q.K and P.V, about twice the matrix throughput of 16-bit operands).  As there, the
-// probabilities are rounded to e4m3 before the product with V; the row sum uses the fp32 values.
+// probabilities are rounded to e4m3 before the product with V.
+//
+// Probabilities in e4m3: each row's probabilities are taken relative to a reference maximum that
+// only moves when a tile's maximum exceeds it by more than 2^kFp8RescaleLog2, and are scaled up by
+// 2^kFp8ShiftLog2 (folded into the exponent, so it costs nothing): p' = 2^(s - m_ref + shift) lies
+// in (0, 2^(4 + 4)] = (0, 256], inside e4m3's range (largest 448), and probabilities down to 2^-10
+// of the reference stay normal (relative rounding error <= 2^-4).  O is normalised by the sum of
+// the ROUNDED probabilities, computed by one more 8-bit MFMA against an all-ones operand, so O is
+// a weighted mean of V rows whose weights are the rounded probabilities (identical V rows return
+// that row).  The LSE uses the fp32 sum of the unrounded values (the shift taken back out).
 //
 // Mapping: the two-group ping-pong workgroup of the bf16 kernel (8 waves; waves w and w + 4 share
 // a SIMD and run one phase apart, so one group's MFMA phase overlaps the other's softmax), with
@@ -43,6 +52,12 @@ namespace paa {
 namespace {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+constexpr float kFp8RescaleLog2 = 4.0f;  // lazy rescale threshold of this kernel (log2 units)
+constexpr float kFp8ShiftLog2 = 4.0f;    // probabilities are scaled by 2^4 before rounding to e4m3
+static_assert(kFp8RescaleLog2 + kFp8ShiftLog2 <= 8.0f, "probabilities must stay <= 256 < 448");
+constexpr int kE4m3Ones = 0x38383838;    // four e4m3 bytes of 1.0
+constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ f32x16_t mfma_fp8(i32x8_t a, i32x8_t b, f32x16_t c) {
   // formats 0/0: both operands e4m3; scale exponents 127: a factor of 1
@@ -85,7 +100,7 @@ struct Fp8Args {
   int n_qtiles, units_per_qt, mirror;
   float scale_eff;    // scale * q_scale * k_scale
   float scale_log2;   // scale_eff * log2(e)
-  float rescale_raw;  // kRescaleLog2 / scale_log2
+  float rescale_raw;  // kFp8RescaleLog2 / scale_log2
   float v_scale;
 };
 
@@ -229,6 +244,10 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
 #pragma unroll
   for (int db = 0; db < kDBlocks; ++db)
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  // sum of the rounded probabilities of column l%32 (every row of this product holds it; only
+  // element 0 is read, so only element 0 is rescaled)
+  f32x16_t acc_l = {};
+  const i32x8_t ones = {kE4m3Ones, kE4m3Ones, kE4m3Ones, kE4m3Ones, kE4m3Ones, kE4m3Ones, kE4m3Ones, kE4m3Ones};
   f32x16_t s[2];
   i32x8_t pf;
 
@@ -256,6 +275,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
         const i32x8_t vf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         acc[db] = mfma_fp8(vf, pf, acc[db]);
       }
+      acc_l = mfma_fp8(ones, pf, acc_l);
     }
   };
 
@@ -282,12 +302,13 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
       const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_run - m_new) * a.scale_log2);
       m_run = m_new;
       l_run *= alpha;
+      acc_l[0] *= alpha;
 #pragma unroll
       for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
     }
-    const float neg_ms = m_run == -INFINITY ? 0.f : -m_run * a.scale_log2;
+    const float neg_ms = m_run == -INFINITY ? 0.f : kFp8ShiftLog2 - m_run * a.scale_log2;
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
     int xy[2][4];  // e4m3 of keys 8g + 4 half + 0..3 of block mb (second block: +32)
 #pragma unroll
@@ -335,10 +356,10 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
     run(std::integral_constant<int, 1>{});
   wait_vmcnt<0>();
 
-  // ---- epilogue: O = v_scale * acc / l, LSE = scale_eff * m + ln(l) ----
+  // ---- epilogue: O = v_scale * acc / (sum of rounded p), LSE = scale_eff * m + ln(sum of p) - shift ----
   const int row = q0 + l32;
   const float l_tot = l_run + swap_halves(l_run, half);
-  const float f = a.v_scale / l_tot;
+  const float f = a.v_scale / acc_l[0];
   if (row < a.N) {
     uint16_t* orow = a.o + (((size_t)b * a.H + head) * N + row) * D;
 #pragma unroll
@@ -351,7 +372,8 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
         *(u32x2_t*)(orow + d0) = w;
       }
     }
-    if (a.lse != nullptr && half == 0) a.lse[((size_t)b * a.H + head) * N + row] = a.scale_eff * m_run + __logf(l_tot);
+    if (a.lse != nullptr && half == 0) a.lse[((size_t)b * a.H + head) * N + row] =
+        a.scale_eff * m_run + (__logf(l_tot) - kFp8ShiftLog2 * kLn2);
   }
 }
 
@@ -411,7 +433,7 @@ hipError_t prefill_fp8(const void* q, const void* k, const void* vt, void* o, fl
   a.N = N;
   a.scale_eff = scale * q_scale * k_scale;
   a.scale_log2 = a.scale_eff * kLog2e;
-  a.rescale_raw = kRescaleLog2 / a.scale_log2;
+  a.rescale_raw = kFp8RescaleLog2 / a.scale_log2;
   a.v_scale = v_scale;
   if (d == 64) return causal ? dispatch_fp8<64, true>(a, stream) : dispatch_fp8<64, false>(a, stream);
   return causal ? dispatch_fp8<128, true>(a, stream) : dispatch_fp8<128, false>(a, stream);

@@ -329,3 +329,41 @@ def test_binding_paged_prefill_output_shapes():
     _expect_shape_error(lambda: paa.paged_prefill(q, _bf(19, 2, 64), vn, kc, vc, bt, ctx, qs), "k_new")
     _expect_device_error(lambda: call(out=_bf(20, 8, 64), lse=torch.zeros(20, 8)))
 
+
+# ---- host-side sanitizer build of the C ABI ----
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROCM = "/opt/rocm"
+# instrumentation for the host pass of abi.hip only (device code is compiled as usual)
+HOST_SANITIZE = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+                 "-Xarch_host -fno-sanitize-recover=all -Xarch_host -fno-omit-frame-pointer").split()
+LINK_SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+
+
+def test_abi_host_code_under_asan_and_ubsan(L, tmp_path):
+    """abi.hip's host code built with AddressSanitizer and UndefinedBehaviorSanitizer, driven through every
+    entry point's argument checks (tests/abi_host_check.cpp), including size arithmetic near its overflow
+    limits: no report, no leak, and every status as expected.  Nothing is launched."""
+    from paged_attention_attn_amd import build as B
+    clangxx = os.path.join(ROCM, "llvm", "bin", "clang++")
+    if not (os.path.exists(B.HIPCC) and os.path.exists(clangxx)):
+        pytest.skip("ROCm compilers not installed")
+    objs = [os.path.join(B.BUILD, n + ".o") for n in ("prefill_bf16", "prefill_fp8", "prefill_f32", "paged_decode")]
+    if not all(os.path.exists(o) for o in objs):
+        B.build()
+    abi_o = str(tmp_path / "abi_sanitized.o")
+    exe = str(tmp_path / "abi_host_check")
+    compile_cmd = [B.HIPCC, "--offload-arch=gfx950", "-std=c++17", "-O1", "-g", "-fPIC",
+                   "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *HOST_SANITIZE,
+                   "-c", os.path.join(B.CSRC, "abi.hip"), "-o", abi_o]
+    r = subprocess.run(compile_cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    link_cmd = [clangxx, "-std=c++17", "-O1", "-g", *LINK_SANITIZE, "-I" + os.path.join(ROCM, "include"),
+                "-D__HIP_PLATFORM_AMD__", os.path.join(HERE, "abi_host_check.cpp"), abi_o, *objs,
+                "-L" + os.path.join(ROCM, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-o", exe]
+    r = subprocess.run(link_cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0 and "abi host checks passed" in r.stdout, r.stdout + r.stderr
