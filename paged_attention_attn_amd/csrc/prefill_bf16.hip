@@ -39,11 +39,13 @@
 //    keys is permuted to match where the score MFMA left each probability.
 //    The accumulator of lane l again belongs to query row l%32, so the
 //    rescale by exp(m_old - m_new) is lane-local.
-//  * the running maximum is only moved when some row of the wave grew by more
-//    than kRescaleLog2 (in log2 units); otherwise the old maximum stays the
-//    reference point and probabilities may exceed 1 by up to 2^kRescaleLog2.
-//    Numerator and denominator share the reference point, so the result is
-//    the same softmax; the output and LSE use the reference actually kept.
+//  * the reference maximum of a row only has to keep the numbers finite, so
+//    no row maximum is taken per tile: the probabilities of a tile are
+//    computed against the current reference, and only when some lane's share
+//    of them exceeds kMaxTileSum (or is not finite, as on a row's first
+//    visible tile) does the wave take the exact maximum, rescale its state
+//    and recompute them.  Numerator and both sums share the reference, so
+//    the result is the same softmax; the LSE uses the reference actually kept.
 //  * causal: tiles entirely above the diagonal of the workgroup are never
 //    loaded; a wave whose rows all precede a tile skips its math; only tiles
 //    crossing the diagonal (or the ragged end of the sequence) are masked.
@@ -94,7 +96,6 @@ struct PrefillArgs {
   int units_per_qt;  // B * Hkv * (group / HPW)
   float scale;       // softmax scale applied to Q.K
   float scale_log2;  // scale * log2(e)
-  float rescale_raw; // kRescaleLog2 / scale_log2: the lazy rescale threshold in raw score units
   int window;        // sliding window width (kMaskWindow only)
   int n_global;      // leading keys visible to every later query (kMaskWindow only)
   int mirror;        // 1 when the whole grid is resident at once: pair heavy and light units (see below)
@@ -464,8 +465,11 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
       for (int i = 0; i < 16; ++i) acc[rb][db][i] = 0.f;
   }
 
-  // Softmax of tile j, first half, for row block rb: mask, row max, and a rescale of the state when
-  // the reference maximum moves.  Returns -reference * scale_log2, the exponent shift of this tile.
+  // Softmax of tile j, first half, for row block rb: the mask.  Returns -reference * scale_log2, the
+  // exponent shift of this tile.  The reference only has to keep the numbers finite: it moves (see
+  // rescale) when some lane's share of a tile's probabilities exceeds kMaxTileSum or is not finite,
+  // as on a row's first visible tile while the reference is still -inf.  No row maximum is taken
+  // otherwise; numerator and both sums share the reference, so the result is the same softmax.
   auto softmax_prep = [&](int j, int rb, f32x16_t (&s)[2]) __attribute__((always_inline)) -> float {
     const int k0 = j * kBc;
     const int rq0 = qoff + q0 + 32 * rb;  // key position of the block's first query row
@@ -489,30 +493,35 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
           if (c > lim || out_of_window) s[mb][i] = -INFINITY;
         }
     }
+    return -m_run[rb] * a.scale_log2;  // +inf while the reference is still -inf
+  };
+
+  // Moves the reference maximum of row block rb to the exact running maximum (the scores' own
+  // maximum over this tile and the old reference) and rescales the state; returns the new shift.
+  auto rescale = [&](int rb, const f32x16_t (&s)[2]) __attribute__((always_inline)) -> float {
     float tmax = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[mb][i]);
     tmax = fmaxf(tmax, swap_halves(tmax, half));
-    // move the reference maximum only when some row of the wave outgrew it by the threshold
-    if (__builtin_amdgcn_ballot_w64(tmax > m_run[rb] + a.rescale_raw) != 0) {
-      const float m_new = fmaxf(m_run[rb], tmax);
-      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_run[rb] - m_new) * a.scale_log2);
-      m_run[rb] = m_new;
-      l_run[rb] *= alpha;
-      lr_run[rb] *= alpha;
+    const float m_new = fmaxf(m_run[rb], tmax);
+    const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_run[rb] - m_new) * a.scale_log2);
+    m_run[rb] = m_new;
+    l_run[rb] *= alpha;
+    lr_run[rb] *= alpha;
 #pragma unroll
-      for (int db = 0; db < kDBlocks; ++db)
+    for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[rb][db][i] *= alpha;
-    }
-    return m_run[rb] == -INFINITY ? 0.f : -m_run[rb] * a.scale_log2;
+      for (int i = 0; i < 16; ++i) acc[rb][db][i] *= alpha;
+    return m_new == -INFINITY ? 0.f : -m_new * a.scale_log2;
   };
 
   // Softmax of tile j, second half (no branches, so it can interleave with MFMAs): probabilities
-  // relative to the reference, their row sum, and the bf16 B operands of the PV product.
-  auto softmax_exp = [&](int rb, const f32x16_t (&s)[2], float neg_ms, u32x4_t (&pf)[4]) __attribute__((always_inline)) {
+  // relative to the reference and the bf16 B operands of the PV product; returns this lane's share of
+  // the tile's probabilities (the sums are only added once the tile is accepted).
+  auto softmax_exp = [&](const f32x16_t (&s)[2], float neg_ms, u32x4_t (&pf)[4]) __attribute__((always_inline))
+      -> float {
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -527,8 +536,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
         pf[2 * mb + sh] = u32x4_t{pack_bf16x2(p[8 * sh + 0], p[8 * sh + 1]), pack_bf16x2(p[8 * sh + 2], p[8 * sh + 3]),
                                   pack_bf16x2(p[8 * sh + 4], p[8 * sh + 5]), pack_bf16x2(p[8 * sh + 6], p[8 * sh + 7])};
     }
-    l_run[rb] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    lr_run[rb] += sum_bf16x16(pf);
+    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
   };
 
   // O^T += V^T P^T for every row block.  PV k-step ks covers keys 16ks..16ks+15 of the tile; logical
@@ -578,8 +586,16 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
       f32x16_t s_nxt[RB][2];
       scores(kst(Next{}), s_nxt);
       u32x4_t pf[RB][4];
+      float lt[RB];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) softmax_exp(rb, s_cur[rb], neg_ms[rb], pf[rb]);
+      for (int rb = 0; rb < RB; ++rb) lt[rb] = softmax_exp(s_cur[rb], neg_ms[rb], pf[rb]);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (__builtin_amdgcn_ballot_w64(!(lt[rb] <= kMaxTileSum)) != 0)
+          lt[rb] = softmax_exp(s_cur[rb], rescale(rb, s_cur[rb]), pf[rb]);
+        l_run[rb] += lt[rb];
+        lr_run[rb] += sum_bf16x16(pf[rb]);
+      }
       pv(vst(st_tag), pf);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
@@ -925,7 +941,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     }
   };
 
-  // VALU phase of iteration i: mask, row max, lazy rescale, exponentials, row sum, bf16 P
+  // VALU phase of iteration i: mask, exponentials against the reference (rescaled only on overflow),
+  // the two row sums, bf16 P
   auto v_phase = [&](int i) __attribute__((always_inline)) {
     if (i < 0 || i >= n_act) return;
     const int k0 = key_tile(i) * kBc;
@@ -945,13 +962,36 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
           if (c > lim || out_of_window) s[mb][e] = -INFINITY;
         }
     }
-    float tmax = -INFINITY;
+    // Probabilities against the current reference maximum, then the bf16 B operands of the next P.V.
+    auto probs = [&](float neg_ms) __attribute__((always_inline)) -> float {
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb) {
+        float p[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[mb][e]);
-    tmax = fmaxf(tmax, swap_halves(tmax, half));
-    if (__builtin_amdgcn_ballot_w64(tmax > m_run + a.rescale_raw) != 0) {
+        for (int e = 0; e < 16; ++e) {
+          p[e] = fast_exp2(fmaf(s[mb][e], a.scale_log2, neg_ms));
+          ps[e % 4] += p[e];
+        }
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh)
+          pf[2 * mb + sh] = u32x4_t{pack_bf16x2(p[8 * sh + 0], p[8 * sh + 1]), pack_bf16x2(p[8 * sh + 2], p[8 * sh + 3]),
+                                    pack_bf16x2(p[8 * sh + 4], p[8 * sh + 5]), pack_bf16x2(p[8 * sh + 6], p[8 * sh + 7])};
+      }
+      return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    };
+    // The reference only has to keep the numbers finite: it moves when some lane's share of this tile's
+    // probabilities exceeds kMaxTileSum (or is not finite, as on a row's first visible tile, while the
+    // reference is still -inf), and then to the exact running maximum.  No row maximum is taken
+    // otherwise.  Numerator and both sums share the reference, so the result is the same softmax.
+    float lt = probs(-m_run * a.scale_log2);
+    if (__builtin_amdgcn_ballot_w64(!(lt <= kMaxTileSum)) != 0) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[mb][e]);
+      tmax = fmaxf(tmax, swap_halves(tmax, half));
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_run - m_new) * a.scale_log2);
       m_run = m_new;
@@ -961,23 +1001,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
       for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
+      lt = probs(m_run == -INFINITY ? 0.f : -m_run * a.scale_log2);
     }
-    const float neg_ms = m_run == -INFINITY ? 0.f : -m_run * a.scale_log2;
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      float p[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p[e] = fast_exp2(fmaf(s[mb][e], a.scale_log2, neg_ms));
-        ps[e % 4] += p[e];
-      }
-#pragma unroll
-      for (int sh = 0; sh < 2; ++sh)
-        pf[2 * mb + sh] = u32x4_t{pack_bf16x2(p[8 * sh + 0], p[8 * sh + 1]), pack_bf16x2(p[8 * sh + 2], p[8 * sh + 3]),
-                                  pack_bf16x2(p[8 * sh + 4], p[8 * sh + 5]), pack_bf16x2(p[8 * sh + 6], p[8 * sh + 7])};
-    }
-    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    l_run += lt;
     lr_run += sum_bf16x16(pf);
   };
 
@@ -1218,7 +1244,6 @@ hipError_t paged_prefill_bf16(const void* q, const void* k_new, const void* v_ne
   a.N = max_q_len;  // sizes the grid; each sequence's own chunk length is read on the device
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
-  a.rescale_raw = kRescaleLog2 / a.scale_log2;
   a.bt = block_table;
   a.ctx_lens = ctx_lens;
   a.q_start = q_start;
@@ -1243,7 +1268,6 @@ hipError_t prefill_bf16(const void* q, const void* k, const void* v, void* o, fl
   a.N = N;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
-  a.rescale_raw = kRescaleLog2 / a.scale_log2;
   a.window = window;
   a.n_global = n_global;
   // a window that covers every earlier key is the plain causal mask

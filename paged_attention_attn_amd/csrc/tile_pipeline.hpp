@@ -10,7 +10,9 @@
 namespace paa {
 
 constexpr int kBc = 64;               // keys per tile
-constexpr float kRescaleLog2 = 8.0f;  // lazy rescale threshold (probabilities stay <= 256)
+// bf16 prefill: a lane's share of one tile's probabilities may reach 2^32 before the reference
+// maximum moves (so P, the row sums and O stay finite for |V| below 2^64).
+constexpr float kMaxTileSum = 4294967296.0f;
 
 // Third word of a raw buffer resource (gfx9 family): 32-bit data format, no swizzle, no index.
 // The tile loads read K and V through such resources (buffer_load ... lds), sized so that
