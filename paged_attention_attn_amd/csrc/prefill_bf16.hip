@@ -522,21 +522,21 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   // the tile's probabilities (the sums are only added once the tile is accepted).
   auto softmax_exp = [&](const f32x16_t (&s)[2], float neg_ms, u32x4_t (&pf)[4]) __attribute__((always_inline))
       -> float {
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    float lt = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       float p[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         p[i] = fast_exp2(fmaf(s[mb][i], a.scale_log2, neg_ms));
-        ps[i % 4] += p[i];
+        lt = (mb == 0 && i == 0) ? p[i] : lt + p[i];
       }
 #pragma unroll
       for (int sh = 0; sh < 2; ++sh)
         pf[2 * mb + sh] = u32x4_t{pack_bf16x2(p[8 * sh + 0], p[8 * sh + 1]), pack_bf16x2(p[8 * sh + 2], p[8 * sh + 3]),
                                   pack_bf16x2(p[8 * sh + 4], p[8 * sh + 5]), pack_bf16x2(p[8 * sh + 6], p[8 * sh + 7])};
     }
-    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    return lt;
   };
 
   // O^T += V^T P^T for every row block.  PV k-step ks covers keys 16ks..16ks+15 of the tile; logical
@@ -594,7 +594,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
         if (__builtin_amdgcn_ballot_w64(!(lt[rb] <= kMaxTileSum)) != 0)
           lt[rb] = softmax_exp(s_cur[rb], rescale(rb, s_cur[rb]), pf[rb]);
         l_run[rb] += lt[rb];
-        lr_run[rb] += sum_bf16x16(pf[rb]);
+        lr_run[rb] = add_bf16x16(pf[rb], lr_run[rb]);
       }
       pv(vst(st_tag), pf);
 #pragma unroll
@@ -964,21 +964,21 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     }
     // Probabilities against the current reference maximum, then the bf16 B operands of the next P.V.
     auto probs = [&](float neg_ms) __attribute__((always_inline)) -> float {
-      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+      float lt = 0.f;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         float p[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           p[e] = fast_exp2(fmaf(s[mb][e], a.scale_log2, neg_ms));
-          ps[e % 4] += p[e];
+          lt = (mb == 0 && e == 0) ? p[e] : lt + p[e];
         }
 #pragma unroll
         for (int sh = 0; sh < 2; ++sh)
           pf[2 * mb + sh] = u32x4_t{pack_bf16x2(p[8 * sh + 0], p[8 * sh + 1]), pack_bf16x2(p[8 * sh + 2], p[8 * sh + 3]),
                                     pack_bf16x2(p[8 * sh + 4], p[8 * sh + 5]), pack_bf16x2(p[8 * sh + 6], p[8 * sh + 7])};
       }
-      return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      return lt;
     };
     // The reference only has to keep the numbers finite: it moves when some lane's share of this tile's
     // probabilities exceeds kMaxTileSum (or is not finite, as on a row's first visible tile, while the
@@ -1004,7 +1004,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
       lt = probs(m_run == -INFINITY ? 0.f : -m_run * a.scale_log2);
     }
     l_run += lt;
-    lr_run += sum_bf16x16(pf);
+    lr_run = add_bf16x16(pf, lr_run);
   };
 
   // Q and stage 0 have landed (loads after them: stages 1 .. STAGES-1)
