@@ -309,15 +309,15 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
         for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
     }
     const float neg_ms = m_run == -INFINITY ? 0.f : kFp8ShiftLog2 - m_run * a.scale_log2;
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
-    int xy[2][4];  // e4m3 of keys 8g + 4 half + 0..3 of block mb (second block: +32)
+    float lt = 0.f;  // this lane's share of the tile's (unrounded) sum, one chain from the first value
+    int xy[2][4];    // e4m3 of keys 8g + 4 half + 0..3 of block mb (second block: +32)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       float p[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         p[e] = fast_exp2(fmaf(s[mb][e], a.scale_log2, neg_ms));
-        ps[e % 4] += p[e];
+        lt = (mb == 0 && e == 0) ? p[e] : lt + p[e];
       }
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) xy[mb][gq] = pack_fp8x4(p[4 * gq], p[4 * gq + 1], p[4 * gq + 2], p[4 * gq + 3]);
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
       pf[2 * gq] = r[0];
       pf[2 * gq + 1] = r[1];
     }
-    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    l_run += lt;
   };
 
   wait_vmcnt<(STAGES - 1) * kLoadsPerStage>();  // Q and stage 0 have landed
