@@ -39,13 +39,15 @@
 //    keys is permuted to match where the score MFMA left each probability.
 //    The accumulator of lane l again belongs to query row l%32, so the
 //    rescale by exp(m_old - m_new) is lane-local.
-//  * the reference maximum of a row only has to keep the numbers finite, so
-//    no row maximum is taken per tile: the probabilities of a tile are
-//    computed against the current reference, and only when some lane's share
-//    of them exceeds kMaxTileSum (or is not finite, as on a row's first
-//    visible tile) does the wave take the exact maximum, rescale its state
-//    and recompute them.  Numerator and both sums share the reference, so
-//    the result is the same softmax; the LSE uses the reference actually kept.
+//  * the reference of a row only has to keep the numbers finite, so no row
+//    maximum is taken per tile: the probabilities of a tile are computed
+//    against the current reference, and only when some lane's share of them
+//    exceeds kMaxTileSum (or is not finite, as on a row's first visible
+//    tile) does the wave take the exact maximum, move the reference to
+//    kRefHeadroomLog2 above it (so that scores may keep rising a long way
+//    before it has to move again), rescale its state and recompute them.
+//    Numerator and both sums share the reference, so the result is the same
+//    softmax; the LSE uses the reference actually kept.
 //  * causal: tiles entirely above the diagonal of the workgroup are never
 //    loaded; a wave whose rows all precede a tile skips its math; only tiles
 //    crossing the diagonal (or the ragged end of the sequence) are masked.
@@ -95,7 +97,8 @@ struct PrefillArgs {
   int n_qtiles;      // query row tiles per head group
   int units_per_qt;  // B * Hkv * (group / HPW)
   float scale;       // softmax scale applied to Q.K
-  float scale_log2;  // scale * log2(e)
+  float scale_log2;    // scale * log2(e)
+  float ref_headroom;  // kRefHeadroomLog2 / scale_log2: a moved reference sits this far above the maximum
   int window;        // sliding window width (kMaskWindow only)
   int n_global;      // leading keys visible to every later query (kMaskWindow only)
   int mirror;        // 1 when the whole grid is resident at once: pair heavy and light units (see below)
@@ -496,8 +499,8 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
     return -m_run[rb] * a.scale_log2;  // +inf while the reference is still -inf
   };
 
-  // Moves the reference maximum of row block rb to the exact running maximum (the scores' own
-  // maximum over this tile and the old reference) and rescales the state; returns the new shift.
+  // Moves the reference of row block rb to kRefHeadroomLog2 above the exact running maximum (unless it
+  // already sits higher) and rescales the state; returns the new shift.
   auto rescale = [&](int rb, const f32x16_t (&s)[2]) __attribute__((always_inline)) -> float {
     float tmax = -INFINITY;
 #pragma unroll
@@ -505,7 +508,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
 #pragma unroll
       for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[mb][i]);
     tmax = fmaxf(tmax, swap_halves(tmax, half));
-    const float m_new = fmaxf(m_run[rb], tmax);
+    const float m_new = fmaxf(m_run[rb], tmax + a.ref_headroom);
     const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_run[rb] - m_new) * a.scale_log2);
     m_run[rb] = m_new;
     l_run[rb] *= alpha;
@@ -992,7 +995,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[mb][e]);
       tmax = fmaxf(tmax, swap_halves(tmax, half));
-      const float m_new = fmaxf(m_run, tmax);
+      const float m_new = fmaxf(m_run, tmax + a.ref_headroom);
       const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((m_run - m_new) * a.scale_log2);
       m_run = m_new;
       l_run *= alpha;
@@ -1244,6 +1247,7 @@ hipError_t paged_prefill_bf16(const void* q, const void* k_new, const void* v_ne
   a.N = max_q_len;  // sizes the grid; each sequence's own chunk length is read on the device
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
+  a.ref_headroom = kRefHeadroomLog2 / a.scale_log2;
   a.bt = block_table;
   a.ctx_lens = ctx_lens;
   a.q_start = q_start;
@@ -1268,6 +1272,7 @@ hipError_t prefill_bf16(const void* q, const void* k, const void* v, void* o, fl
   a.N = N;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
+  a.ref_headroom = kRefHeadroomLog2 / a.scale_log2;
   a.window = window;
   a.n_global = n_global;
   // a window that covers every earlier key is the plain causal mask

@@ -10,9 +10,15 @@
 namespace paa {
 
 constexpr int kBc = 64;               // keys per tile
-// bf16 prefill: a lane's share of one tile's probabilities may reach 2^32 before the reference
-// maximum moves (so P, the row sums and O stay finite for |V| below 2^64).
+// bf16 prefill: a lane's share of one tile's probabilities may reach 2^32 before the reference moves
+// (so P, the row sums and O stay finite for |V| below 2^64), and a moved reference sits 80 (log2
+// units) above the row's running maximum, so later scores may rise by about 107 before it moves
+// again.  Keys more than 46 below the running maximum then underflow to 0: their weight is under
+// 2^-46 each.  The peaked long workload moved references on many tiles at a headroom of 0 (its
+// outlier keys keep setting new maxima): a headroom of 48 took it from 1965 to 1851 us on one box,
+// 80 a further 2.6%.
 constexpr float kMaxTileSum = 4294967296.0f;
+constexpr float kRefHeadroomLog2 = 80.0f;
 
 // Third word of a raw buffer resource (gfx9 family): 32-bit data format, no swizzle, no index.
 // The tile loads read K and V through such resources (buffer_load ... lds), sized so that

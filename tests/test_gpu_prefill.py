@@ -12,7 +12,7 @@ import oracle
 import paged_attention_attn_amd as paa
 import oracle_pool
 from gpu_util import assert_close_bf16, assert_close_f32, assert_close_lse, dev_bf16, dev_f32, host_f64
-from workloads import WORKLOADS, PrefillWorkload, prefill_inputs
+from workloads import WORKLOADS, PrefillWorkload, f32_to_bf16_bits, prefill_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -65,6 +65,30 @@ def test_bf16_peaked_scores_small():
     w = PrefillWorkload("peaked", 1, 8, 2, 520, 128, True, q_mult=4.0, k_outlier_frac=0.01)
     _announce("attn_fwd bf16 peaked N520")
     a = prefill_inputs(w, seed=5)
+    o, lse = _run_bf16(a, w)
+    ro, rl = oracle.attention(a["q"], a["k"], a["v"], True, a["scale"])
+    assert_close_bf16(o, ro)
+    assert_close_lse(lse, rl)
+
+
+@pytest.mark.parametrize("N,d", [(1500, 128), (700, 64)])
+def test_bf16_rising_scores_and_deep_keys(N, d):
+    """Scores that keep rising along the sequence (each key a little larger than the one before, so every
+    row's maximum keeps moving and the kernels' reference must move many times), keys far below the
+    row's maximum (whose weights underflow), and a row-block whose first tile holds only such keys:
+    every element against the oracle, both kernels (d=128 ping-pong grid shape too small, so the
+    split-key kernel; d=64 the lock-step kernel)."""
+    rng = np.random.default_rng(80 + d)
+    B, H, Hkv = 1, 4, 1
+    q = 4.0 * rng.standard_normal((B, H, N, d))
+    growth = np.linspace(1.0, 12.0, N)[:, None]
+    k = rng.standard_normal((B, Hkv, N, d)) * growth
+    k[0, 0, 10:40] *= -20.0  # very low scores for rows whose q aligns with the bulk
+    v = rng.standard_normal((B, Hkv, N, d))
+    a = {"q": f32_to_bf16_bits(q.astype(np.float32)), "k": f32_to_bf16_bits(k.astype(np.float32)),
+         "v": f32_to_bf16_bits(v.astype(np.float32)), "scale": float(np.float32(1.0 / np.sqrt(d)))}
+    w = PrefillWorkload("rising", B, H, Hkv, N, d, True)
+    _announce(f"attn_fwd rising scores N{N} d{d}")
     o, lse = _run_bf16(a, w)
     ro, rl = oracle.attention(a["q"], a["k"], a["v"], True, a["scale"])
     assert_close_bf16(o, ro)
