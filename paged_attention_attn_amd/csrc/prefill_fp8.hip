@@ -20,7 +20,9 @@
 // Mapping: the two-group ping-pong workgroup of the bf16 kernel (8 waves; waves w and w + 4 share
 // a SIMD and run one phase apart, so one group's MFMA phase overlaps the other's softmax), with
 // v_mfma_scale_f32_32x32x64_f8f6f4 (scales fixed at 1; the per-tensor scales are applied to the
-// fp32 scores and output):
+// fp32 scores and output).  Each phase takes two 64-key tiles: with 8-bit operands a tile's MFMA
+// work is half that of bf16, and one tile per phase left the barriers and waits of a period at
+// about a sixth of its time.  The layouts below are per 64-key tile:
 //  * operand pairing of that instruction (checked on gfx950): lane l supplies row l%32 of A and
 //    column l%32 of B, and byte j of lane l meets byte j of lanes with the same l/32; any
 //    assignment of contraction indices to (l/32, j) that A and B share is valid.
@@ -112,17 +114,18 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
   constexpr int kTileRows = kRowBlocks * 32;
   constexpr int kKSteps = D / 64;
   constexpr int kDBlocks = D / 32;
-  constexpr int kLoadsPerStage = T::kLoadsPerWave;
+  constexpr int kSub = 2;  // 64-key tiles per iteration (per ping-pong phase)
+  constexpr int kLoadsPerStage = kSub * T::kLoadsPerWave;
   static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
 
-  __shared__ __attribute__((aligned(1024))) char k_st0[T::kKTileBytes];
-  __shared__ __attribute__((aligned(1024))) char k_st1[T::kKTileBytes];
-  __shared__ __attribute__((aligned(1024))) char k_st2[T::kKTileBytes];
-  __shared__ __attribute__((aligned(1024))) char k_st3[T::kKTileBytes];
-  __shared__ __attribute__((aligned(1024))) char v_st0[T::kVTileBytes];
-  __shared__ __attribute__((aligned(1024))) char v_st1[T::kVTileBytes];
-  __shared__ __attribute__((aligned(1024))) char v_st2[T::kVTileBytes];
-  __shared__ __attribute__((aligned(1024))) char v_st3[T::kVTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_st0[kSub * T::kKTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_st1[kSub * T::kKTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_st2[kSub * T::kKTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_st3[kSub * T::kKTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_st0[kSub * T::kVTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_st1[kSub * T::kVTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_st2[kSub * T::kVTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_st3[kSub * T::kVTileBytes];
   auto kst = [&](auto i_tag) __attribute__((always_inline)) -> PAA_LDS char* {
     constexpr int i = decltype(i_tag)::value % STAGES;
     if constexpr (i == 0) return (PAA_LDS char*)k_st0;
@@ -168,14 +171,18 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
   const uint8_t* kh = a.k + ((size_t)b * a.Hkv + g) * N * D;
   const uint8_t* vh = a.vt + ((size_t)b * a.Hkv + g) * (size_t)D * N;
 
+  // 64-key tiles [0, n_tiles); iteration i covers tiles kSub * i .. kSub * i + kSub - 1 (a tile past
+  // n_tiles, or past this wave's last causal tile, is loaded as a repeat and fully masked)
   const int kv_end = CAUSAL ? min(a.N, q0_tile + kTileRows) : a.N;
-  const int n_iter = (kv_end + kBc - 1) / kBc;
-  const int last_tile = CAUSAL ? min(n_iter - 1, (q0 + 31) / kBc) : n_iter - 1;
-  const int n_act = last_tile + 1;
+  const int n_tiles = (kv_end + kBc - 1) / kBc;
+  const int n_iter = (n_tiles + kSub - 1) / kSub;
+  const int last_tile = CAUSAL ? min(n_tiles - 1, (q0 + 31) / kBc) : n_tiles - 1;
+  const int n_act = last_tile / kSub + 1;
 
-  // One stage: K of iteration s and V^T of iteration s - 1.  The waves' loads are numbered
-  // u = wave * kLoadsPerStage + i over the K blocks, then the V^T blocks; iterations past the end
-  // repeat the last one (the buffer is free and never read), so every stage issues the same count.
+  // One stage: the K tiles of iteration s and the V^T tiles of iteration s - 1.  The waves' loads
+  // of one tile are numbered u = wave * kLoadsPerWave + i over the K blocks, then the V^T blocks;
+  // tiles past the end repeat the last one (never read, or fully masked), so every stage issues the
+  // same count.
   // Loads go through buffer resources spanning this (batch, KV head)'s K and V^T, so each costs
   // one vector add on a lane offset fixed for the loop: K rows past the end read as zeros (they
   // are masked); V^T rows run on into the next row, so the last tile's chunks past the end are
@@ -202,9 +209,14 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
   };
   auto issue_stage = [&](auto s_tag, int s) __attribute__((always_inline)) {
     using Prev = std::integral_constant<int, decltype(s_tag)::value + STAGES - 1>;
-    const int jk = min(s, n_iter - 1), jv = min(max(s - 1, 0), n_iter - 1);
 #pragma unroll
-    for (int i = 0; i < kLoadsPerStage; ++i) load_block(wave * kLoadsPerStage + i, jk, jv, kst(s_tag), vst(Prev{}));
+    for (int sub = 0; sub < kSub; ++sub) {
+      const int jk = min(kSub * s + sub, n_tiles - 1), jv = min(max(kSub * (s - 1) + sub, 0), n_tiles - 1);
+#pragma unroll
+      for (int i = 0; i < T::kLoadsPerWave; ++i)
+        load_block(wave * T::kLoadsPerWave + i, jk, jv, kst(s_tag) + sub * T::kKTileBytes,
+                   vst(Prev{}) + sub * T::kVTileBytes);
+    }
   };
 
   // ---- Q fragments (B operand of S^T): row q0 + l32, bytes 64t + 32 half .. +31 ----
@@ -248,8 +260,8 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
   // element 0 is read, so only element 0 is rescaled)
   f32x16_t acc_l = {};
   const i32x8_t ones = {kE4m3Ones, kE4m3Ones, kE4m3Ones, kE4m3Ones, kE4m3Ones, kE4m3Ones, kE4m3Ones, kE4m3Ones};
-  f32x16_t s[2];
-  i32x8_t pf;
+  f32x16_t s[kSub][2];
+  i32x8_t pf[kSub];
 
   auto m_phase = [&](auto u_tag, int i) __attribute__((always_inline)) {
     using U = decltype(u_tag);
@@ -258,44 +270,56 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
     const PAA_LDS char* vt = vst(Prev{});
     if (i < n_act) {
 #pragma unroll
-      for (int t = 0; t < kKSteps; ++t)
+      for (int sub = 0; sub < kSub; ++sub)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const u32x4_t lo = *(const PAA_LDS u32x4_t*)(kt + koff[t][0] + mb * 32 * T::kKRowBytes);
-          const u32x4_t hi = *(const PAA_LDS u32x4_t*)(kt + koff[t][1] + mb * 32 * T::kKRowBytes);
-          const i32x8_t kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          s[mb] = t == 0 ? mfma_fp8(kf, qf[t], f32x16_t{}) : mfma_fp8(kf, qf[t], s[mb]);
-        }
+        for (int t = 0; t < kKSteps; ++t)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            const PAA_LDS char* kr = kt + sub * T::kKTileBytes + mb * 32 * T::kKRowBytes;
+            const u32x4_t lo = *(const PAA_LDS u32x4_t*)(kr + koff[t][0]);
+            const u32x4_t hi = *(const PAA_LDS u32x4_t*)(kr + koff[t][1]);
+            const i32x8_t kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            s[sub][mb] = t == 0 ? mfma_fp8(kf, qf[t], f32x16_t{}) : mfma_fp8(kf, qf[t], s[sub][mb]);
+          }
     }
     if (i >= 1 && i - 1 < n_act) {
 #pragma unroll
-      for (int db = 0; db < kDBlocks; ++db) {
-        const u32x4_t lo = *(const PAA_LDS u32x4_t*)(vt + db * 32 * T::kVRowBytes + voff[0]);
-        const u32x4_t hi = *(const PAA_LDS u32x4_t*)(vt + db * 32 * T::kVRowBytes + voff[1]);
-        const i32x8_t vf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        acc[db] = mfma_fp8(vf, pf, acc[db]);
+      for (int sub = 0; sub < kSub; ++sub) {
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db) {
+          const PAA_LDS char* vr = vt + sub * T::kVTileBytes + db * 32 * T::kVRowBytes;
+          const u32x4_t lo = *(const PAA_LDS u32x4_t*)(vr + voff[0]);
+          const u32x4_t hi = *(const PAA_LDS u32x4_t*)(vr + voff[1]);
+          const i32x8_t vf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          acc[db] = mfma_fp8(vf, pf[sub], acc[db]);
+        }
+        acc_l = mfma_fp8(ones, pf[sub], acc_l);
       }
-      acc_l = mfma_fp8(ones, pf, acc_l);
     }
   };
 
   auto v_phase = [&](int i) __attribute__((always_inline)) {
     if (i < 0 || i >= n_act) return;
-    const int k0 = i * kBc;
-    const bool need_mask = (CAUSAL && (k0 + kBc - 1 > q0)) || (k0 + kBc > a.N);
-    if (need_mask) {  // key k0 + 4 half + c, with c a constant per element
-      const int lim = (CAUSAL ? min(q0 + l32, a.N - 1) : a.N - 1) - (k0 + 4 * half);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+    for (int sub = 0; sub < kSub; ++sub) {
+      const int k0 = (kSub * i + sub) * kBc;
+      const bool need_mask = (CAUSAL && (k0 + kBc - 1 > q0)) || (k0 + kBc > a.N);
+      if (need_mask) {  // key k0 + 4 half + c, with c a constant per element
+        const int lim = (CAUSAL ? min(q0 + l32, a.N - 1) : a.N - 1) - (k0 + 4 * half);
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (32 * mb + 8 * (e / 4) + (e % 4) > lim) s[mb][e] = -INFINITY;
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (32 * mb + 8 * (e / 4) + (e % 4) > lim) s[sub][mb][e] = -INFINITY;
+      }
     }
     float tmax = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int sub = 0; sub < kSub; ++sub)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[mb][e]);
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[sub][mb][e]);
     tmax = fmaxf(tmax, swap_halves(tmax, half));
     if (__builtin_amdgcn_ballot_w64(tmax > m_run + a.rescale_raw) != 0) {
       const float m_new = fmaxf(m_run, tmax);
@@ -309,26 +333,29 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
         for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
     }
     const float neg_ms = m_run == -INFINITY ? 0.f : kFp8ShiftLog2 - m_run * a.scale_log2;
-    float lt = 0.f;  // this lane's share of the tile's (unrounded) sum, one chain from the first value
-    int xy[2][4];    // e4m3 of keys 8g + 4 half + 0..3 of block mb (second block: +32)
+    float lt = 0.f;  // this lane's share of the iteration's (unrounded) sum, one chain from the first value
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      float p[16];
+    for (int sub = 0; sub < kSub; ++sub) {
+      int xy[2][4];  // e4m3 of keys 8g + 4 half + 0..3 of block mb (second block: +32) of the tile
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p[e] = fast_exp2(fmaf(s[mb][e], a.scale_log2, neg_ms));
-        lt = (mb == 0 && e == 0) ? p[e] : lt + p[e];
+      for (int mb = 0; mb < 2; ++mb) {
+        float p[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          p[e] = fast_exp2(fmaf(s[sub][mb][e], a.scale_log2, neg_ms));
+          lt = (sub == 0 && mb == 0 && e == 0) ? p[e] : lt + p[e];
+        }
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) xy[mb][gq] = pack_fp8x4(p[4 * gq], p[4 * gq + 1], p[4 * gq + 2], p[4 * gq + 3]);
       }
+      // swap the upper half's first block with the lower half's second: the lower half then holds
+      // keys 8g .. 8g + 7 (own, then partner) and the upper half keys 32 + 8g .. +7 (partner, then own)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) xy[mb][gq] = pack_fp8x4(p[4 * gq], p[4 * gq + 1], p[4 * gq + 2], p[4 * gq + 3]);
-    }
-    // swap the upper half's first block with the lower half's second: the lower half then holds
-    // keys 8g .. 8g + 7 (own, then partner) and the upper half keys 32 + 8g .. +7 (partner, then own)
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const auto r = __builtin_amdgcn_permlane32_swap(xy[0][gq], xy[1][gq], false, false);
-      pf[2 * gq] = r[0];
-      pf[2 * gq + 1] = r[1];
+      for (int gq = 0; gq < 4; ++gq) {
+        const auto r = __builtin_amdgcn_permlane32_swap(xy[0][gq], xy[1][gq], false, false);
+        pf[sub][2 * gq] = r[0];
+        pf[sub][2 * gq + 1] = r[1];
+      }
     }
     l_run += lt;
   };
