@@ -67,3 +67,31 @@ def sample_rows(B, H, N, n_random, seed, tile=64):
     rows = [(b, h, i) for b in {0, B - 1} for h in {0, H - 1, H // 2} for i in edges]
     rows += [(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(N))) for _ in range(n_random)]
     return sorted(set(rows))
+
+
+def zero_query_expected(v, H, causal, window=0, n_global=0):
+    """Closed form of masked attention (softmax of the scaled scores plus the mask, times V: "Fast Attention
+    Kernels and Operator Fusion", "FlashAttention-Style Kernels") when Q = 0: every visible key scores 0, so
+    its weight is one over the number n_i of keys row i sees, O_i is the mean of those V rows and
+    LSE_i = ln n_i.  v: float64 [B, Hkv, N, d] (the V the kernel reads); returns O [B, H, N, d] and LSE
+    [B, H, N], query head h reading KV head h // (H / Hkv).  The mask is causal (optionally a sliding
+    window of width ``window`` plus ``n_global`` leading keys) or none."""
+    B, Hkv, N, d = v.shape
+    pre = np.concatenate([np.zeros((B, Hkv, 1, d)), np.cumsum(v, axis=2)], axis=2)  # pre[k] = sum of rows < k
+    i = np.arange(N)
+    if not causal:
+        tot = np.broadcast_to(pre[:, :, N:N + 1], (B, Hkv, N, d))
+        cnt = np.full(N, float(N))
+    elif window <= 0:
+        tot = pre[:, :, 1:]
+        cnt = (i + 1).astype(np.float64)
+    else:
+        lo = np.maximum(0, i - window + 1)             # the window: keys lo .. i
+        gl = np.minimum(n_global, lo)                  # global tokens left of the window: keys 0 .. gl - 1
+        tot = pre[:, :, i + 1] - pre[:, :, lo] + pre[:, :, gl]
+        cnt = (i + 1 - lo + gl).astype(np.float64)
+    o = tot / cnt[None, None, :, None]
+    o = np.repeat(o, H // Hkv, axis=1)                  # query head h reads KV head h // (H / Hkv)
+    lse = np.broadcast_to(np.log(cnt), (B, H, N))
+    return o, lse
+

@@ -40,7 +40,7 @@ import torch
 import oracle
 import paged_attention_attn_amd as paa
 import oracle_pool
-from gpu_util import host_f64
+from gpu_util import assert_close_bf16, assert_close_lse, host_f64, zero_query_expected
 from workloads import WORKLOADS, PrefillWorkload, prefill_inputs
 
 pytestmark = pytest.mark.gpu
@@ -220,3 +220,20 @@ def test_fp8_scales_and_determinism():
     b = dict(a, v_scale=2 * a["v_scale"])
     o2, l2 = _run(b, w)
     assert np.array_equal(l1, l2) and np.allclose(o2, 2 * o1, rtol=2.0 ** -7, atol=0)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal", [(1, 32, 8, 16384, 128, True), (2, 8, 2, 2000, 128, False)])
+def test_fp8_zero_query_closed_form(B, H, Hkv, N, d, causal):
+    """Q = 0 (all-zero E4M3 codes) at full size: every probability is the same power of two, which E4M3
+    holds exactly, so O is the mean of the dequantized V rows a query sees and LSE = ln(count); O and LSE
+    against that closed form (no oracle), every element, at the bf16 bars."""
+    w = PrefillWorkload("fp8_zq", B, H, Hkv, N, d, causal, dtype="fp8")
+    _announce(f"attn_fwd_fp8 Q=0 B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal}")
+    a = prefill_inputs(w, seed=N + 3)
+    a["q8"] = np.zeros_like(a["q8"])
+    o, lse = _run(a, w)
+    _, _, v = _dequant(a)
+    ro, rl = zero_query_expected(v, H, causal)
+    assert_close_bf16(o, ro)
+    assert_close_lse(lse, rl)

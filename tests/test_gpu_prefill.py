@@ -11,7 +11,8 @@ import torch
 import oracle
 import paged_attention_attn_amd as paa
 import oracle_pool
-from gpu_util import assert_close_bf16, assert_close_f32, assert_close_lse, dev_bf16, dev_f32, host_f64
+from gpu_util import (assert_close_bf16, assert_close_f32, assert_close_lse, dev_bf16, dev_f32, host_f64,
+                      zero_query_expected)
 from workloads import WORKLOADS, PrefillWorkload, f32_to_bf16_bits, prefill_inputs
 
 pytestmark = pytest.mark.gpu
@@ -259,3 +260,29 @@ def test_bf16_pingpong_grids_whole(B, H, Hkv, N, causal, window, n_global):
         ro, rl = oracle_pool.attention(a["q"], a["k"], a["v"], causal, a["scale"])
     assert_close_bf16(o, ro)
     assert_close_lse(lse, rl)
+
+
+# the long GQA shape (ping-pong kernel), the d=64 causal shape (four-wave kernel), a d=64 grid large
+# enough for the eight-wave kernel, a non-causal ping-pong grid, and the windowed workload's mask
+ZERO_Q = [(1, 32, 8, 16384, 128, True, 0, 0), (4, 16, 16, 1024, 64, True, 0, 0), (2, 32, 8, 4096, 64, True, 0, 0),
+          (2, 32, 8, 2000, 128, False, 0, 0), (1, 32, 8, 16384, 128, True, 4096, 64)]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal,window,n_global", ZERO_Q)
+def test_bf16_zero_query_closed_form(B, H, Hkv, N, d, causal, window, n_global):
+    """Q = 0 at full size: O and LSE against the closed form (no oracle), every element."""
+    _announce(f"attn_fwd{'_window' if window else ''} bf16 Q=0 B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal}")
+    a = prefill_inputs(PrefillWorkload("zq", B, H, Hkv, N, d, causal), seed=N + d + 7)
+    q = torch.zeros((B, H, N, d), dtype=torch.bfloat16, device="cuda:0")
+    k, v = dev_bf16(a["k"]), dev_bf16(a["v"])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda:0")
+    if window:
+        o, _ = paa.attn_fwd_window(q, k, v, window, n_global, a["scale"], lse=lse)
+    else:
+        o, _ = paa.attn_fwd(q, k, v, causal, a["scale"], lse=lse)
+    torch.cuda.synchronize()
+    vf = host_f64(v)
+    ro, rl = zero_query_expected(vf, H, causal, window, n_global)
+    assert_close_bf16(host_f64(o), ro)
+    assert_close_lse(lse.cpu().numpy().astype(np.float64), rl)

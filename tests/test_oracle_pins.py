@@ -119,3 +119,27 @@ def test_bf16_bits_to_f64_exact():
     bits = np.array([0x3F80, 0xC000, 0x3E20, 0x7F7F, 0x0080], dtype=np.uint16)
     want = np.array([1.0, -2.0, 0.15625, (2 - 2 ** -7) * 2.0 ** 127, 2.0 ** -126])
     assert np.array_equal(oracle.bf16_bits_to_f64(bits), want)
+
+
+@pytest.mark.parametrize("causal,window,n_global", [(False, 0, 0), (True, 0, 0), (True, 5, 0), (True, 5, 3),
+                                                    (True, 40, 2)])
+def test_zero_query_closed_form(causal, window, n_global):
+    """With Q = 0 every visible score is 0: the oracle gives each row the mean of the V rows it sees and
+    LSE = ln(count).  This pins the oracle's masks and weights, and the closed form the full-size GPU
+    tests compare against."""
+    from gpu_util import zero_query_expected
+    rng = np.random.default_rng(7)
+    B, H, Hkv, N, d = 2, 4, 2, 37, 8
+    q = np.zeros((B, H, N, d))
+    k = rng.standard_normal((B, Hkv, N, d))
+    v = rng.standard_normal((B, Hkv, N, d))
+    if window:
+        o, lse = oracle.attention_window(q, k, v, window, n_global, 0.3)
+    else:
+        o, lse = oracle.attention(q, k, v, causal, 0.3)
+    ro, rl = zero_query_expected(v, H, causal, window, n_global)
+    # brute force on one row: the visible set written out from the mask's definition
+    i, vis = 20, [j for j in range(N) if (not causal) or (j <= 20 and (not window or 20 - j < window or j < n_global))]
+    np.testing.assert_allclose(ro[1, 3, i], v[1, 1, vis].mean(axis=0), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-12)
