@@ -241,10 +241,12 @@ __device__ __forceinline__ GroupSource group_source(const uint16_t* src, const u
   return gs;
 }
 
-template <bool PAGED>
+// STRADDLE selects the path of a straddling paged group; callers branch once per group, not per load.
+template <bool PAGED, bool STRADDLE>
 __device__ __forceinline__ void group_load(PAA_LDS void* dst, const GroupSource& gs, const uint16_t* src, int row0,
                                            int dr, uint32_t off, int n_k, int qoff, int stride) {
-  if (!PAGED || !gs.straddles) {
+  static_assert(PAGED || !STRADDLE, "only paged groups straddle");
+  if constexpr (!STRADDLE) {
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)gs.base, (short)0, gs.bytes, kRawBufferWord3);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, (int)(off + (uint32_t)gs.shift), 0, 0, 0);
   } else {
@@ -255,6 +257,48 @@ __device__ __forceinline__ void group_load(PAA_LDS void* dst, const GroupSource&
     __builtin_amdgcn_global_load_lds((const void*)p, dst, 16, 0, 0);
   }
 }
+
+// Appending a workgroup's chunk rows (its KV head, its query tile) to the caches.  One workgroup per
+// (sequence, KV head, query tile) does it, the one holding the head group's first query heads, so
+// every new row is written exactly once.  No workgroup of the launch reads cache positions at or
+// past ctx (they read the chunk from k / v), so the writes race with nothing and can go out at any
+// time: the kernels issue the reads with their first loads and the writes once those have landed,
+// which keeps the append off the end of the workgroup.  Every thread moves up to kPer 16-byte
+// pieces; load() issues all of a thread's reads at once (the chunk rows always exist, so the data
+// loads do not wait for the page ids), store() writes the pieces whose page id lies in the pool.
+template <int D, int ROWS, int THREADS>
+struct ChunkAppend {
+  static constexpr int kChunks = D / 8;  // 16-byte pieces per row
+  static constexpr int kPer = (2 * ROWS * kChunks + THREADS - 1) / THREADS;
+  u32x4_t val[kPer];
+  uint16_t* dst[kPer];
+
+  __device__ __forceinline__ void load(const PrefillArgs& a, const uint16_t* kh, const uint16_t* vh, size_t kv_stride,
+                                       int b, int g, int q0_tile, int rows, int qoff, int tid) {
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int e = tid + r * THREADS;
+      dst[r] = nullptr;
+      if (e < 2 * rows * kChunks) {
+        const bool is_v = e >= rows * kChunks;
+        const int f = is_v ? e - rows * kChunks : e;
+        const int i = q0_tile + f / kChunks;  // chunk row
+        const int c = f % kChunks;
+        const int pos = qoff + i;
+        const int blk = pos / kPageTokens;
+        const int page = blk < a.max_pages ? a.bt[(size_t)b * a.max_pages + blk] : -1;
+        val[r] = *(const u32x4_t*)((is_v ? vh : kh) + (size_t)i * kv_stride + c * 8);
+        if (page >= 0 && page < a.num_pages)
+          dst[r] = (is_v ? a.vc : a.kc) + (((size_t)page * kPageTokens + pos % kPageTokens) * a.Hkv + g) * D + c * 8;
+      }
+    }
+  }
+  __device__ __forceinline__ void store() const {
+#pragma unroll
+    for (int r = 0; r < kPer; ++r)
+      if (dst[r] != nullptr) *(u32x4_t*)dst[r] = val[r];
+  }
+};
 
 template <int D, int MASK, int HPW, int WAVES, int RB, int STAGES>
 __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_kernel(
@@ -365,13 +409,22 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   auto dma = [&](const uint16_t* src, uint16_t* cache, int j, int page, PAA_LDS char* dst) __attribute__((always_inline)) {
     const int row0 = j * kBc + group_r0;
     const GroupSource gs = group_source<PAGED>(src, cache, row0, kGroupRows, n_k, qoff, (int)kv_stride, page, g * D);
+    auto loads = [&](auto straddle_tag) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < C::kBlocksPerWave; ++i) {
-      const int blk = wave * C::kBlocksPerWave + i;
-      const int dr = i * T::kRowsPerBlock + lane / T::kCpr;  // tile row written by this lane: group_r0 + dr
-      const int c = (lane % T::kCpr) ^ swz<D>(group_r0 + dr);  // data chunk stored at this lane's position
-      const uint32_t off = (uint32_t)((dr * kv_stride + c * 8) * 2);
-      group_load<PAGED>((PAA_LDS void*)(dst + blk * 1024), gs, src, row0, dr, off, n_k, qoff, (int)kv_stride);
+      for (int i = 0; i < C::kBlocksPerWave; ++i) {
+        const int blk = wave * C::kBlocksPerWave + i;
+        const int dr = i * T::kRowsPerBlock + lane / T::kCpr;  // tile row written by this lane: group_r0 + dr
+        const int c = (lane % T::kCpr) ^ swz<D>(group_r0 + dr);  // data chunk stored at this lane's position
+        const uint32_t off = (uint32_t)((dr * kv_stride + c * 8) * 2);
+        group_load<PAGED, decltype(straddle_tag)::value>((PAA_LDS void*)(dst + blk * 1024), gs, src, row0, dr, off,
+                                                         n_k, qoff, (int)kv_stride);
+      }
+    };
+    if constexpr (PAGED) {
+      if (gs.straddles) loads(std::true_type{});
+      else loads(std::false_type{});
+    } else {
+      loads(std::false_type{});
     }
   };
   // cache page holding this wave's rows of tile j (0 when not paged); an id outside the pool is
@@ -393,6 +446,11 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
       return 0;
     }
   };
+
+  // ---- paged: the append's reads go out first; its writes follow once the prologue has landed ----
+  ChunkAppend<D, kTileRows, 64 * WAVES> app;
+  if constexpr (PAGED)
+    if (hsub == 0) app.load(a, kh, vh, kv_stride, b, g, q0_tile, min(kTileRows, n_q - q0_tile), qoff, tid);
 
   // prologue loads: K_0 .. K_{STAGES-1} and V_0 .. V_{STAGES-2}
   auto prologue = [&](auto i_tag, int j) __attribute__((always_inline)) {
@@ -561,6 +619,8 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if constexpr (PAGED)
+    if (hsub == 0) app.store();
   f32x16_t s_cur[RB][2];
   scores(kst(I0{}), s_cur);  // tile 0 is visible to every row
   __syncthreads();           // everyone is done with K stage 0 before it is refilled
@@ -635,31 +695,6 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
       if (a.lse != nullptr && half == 0) {
         const size_t li = PAGED ? q_base / D + (size_t)row * a.H : ((size_t)b * a.H + head) * N + row;
         a.lse[li] = a.scale * m_run[rb] + __logf(l_tot);
-      }
-    }
-  }
-
-  // ---- paged: append this workgroup's chunk rows (its KV head) to the caches ----
-  // One workgroup per (sequence, KV head, query tile) does it, the one holding the head group's
-  // first query heads, so every new row is written exactly once.  No workgroup of this launch
-  // reads cache positions at or past ctx (they read the chunk from k / v), so the writes race
-  // with nothing.  A row whose page id is outside the pool is not written.
-  if constexpr (PAGED) {
-    if (hsub == 0) {
-      constexpr int kChunks = D / 8;  // 16-byte pieces per row
-      const int rows = min(kTileRows, n_q - q0_tile);
-      for (int e = tid; e < 2 * rows * kChunks; e += 64 * WAVES) {
-        const bool is_v = e >= rows * kChunks;
-        const int f = is_v ? e - rows * kChunks : e;
-        const int i = q0_tile + f / kChunks;  // chunk row
-        const int c = f % kChunks;
-        const int pos = qoff + i;
-        const int blk = pos / kPageTokens;
-        const int page = blk < a.max_pages ? a.bt[(size_t)b * a.max_pages + blk] : -1;
-        if (page < 0 || page >= a.num_pages) continue;
-        const u32x4_t val = *(const u32x4_t*)((is_v ? vh : kh) + (size_t)i * kv_stride + c * 8);
-        uint16_t* dst = (is_v ? a.vc : a.kc) + (((size_t)page * kPageTokens + pos % kPageTokens) * a.Hkv + g) * D + c * 8;
-        *(u32x4_t*)dst = val;
       }
     }
   }
@@ -805,12 +840,13 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   const int group_r0 = (w0 % T::kBlocks) * T::kRowsPerBlock;  // first tile row of the wave's group
   const int wave_page = group_r0 / kPageTokens;
   const uint16_t* load_src = loads_v ? vh : kh;
-  auto load_block = [&](int i, int row0, const GroupSource& gs, PAA_LDS char* kdst, PAA_LDS char* vdst) __attribute__((always_inline)) {
+  auto load_block = [&](auto straddle_tag, int i, int row0, const GroupSource& gs, PAA_LDS char* kdst, PAA_LDS char* vdst) __attribute__((always_inline)) {
     const int dr = i * T::kRowsPerBlock + lane / T::kCpr;   // tile row written by this lane: group_r0 + dr
     const int c = (lane % T::kCpr) ^ swz<D>(group_r0 + dr);
     const uint32_t off = (uint32_t)((dr * kv_stride + c * 8) * 2);
     PAA_LDS char* dst = (loads_v ? vdst : kdst) + load_slot * T::kTileBytes + (group_r0 / T::kRowsPerBlock + i) * 1024;
-    group_load<PAGED>((PAA_LDS void*)dst, gs, load_src, row0, dr, off, n_k, qoff, (int)kv_stride);
+    group_load<PAGED, decltype(straddle_tag)::value>((PAA_LDS void*)dst, gs, load_src, row0, dr, off, n_k, qoff,
+                                                     (int)kv_stride);
   };
   // Paged: lane k of pw holds the page of this wave's rows of tile pw_t0 + k, so a tile's page is a
   // lane read.  A scalar load per tile would be retired by the next tile barrier's lgkmcnt(0) and
@@ -856,10 +892,22 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     const int row0 = ((loads_v ? jv : jk) + load_slot) * kBc + group_r0;
     const GroupSource gs = group_source<PAGED>(load_src, loads_v ? a.vc : a.kc, row0, kGroupRows, n_k, qoff,
                                                (int)kv_stride, page, g * D);
+    auto loads = [&](auto straddle_tag) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kLoadsPerStage; ++i) load_block(i, row0, gs, kst(s_tag), vst(Prev{}));
+      for (int i = 0; i < kLoadsPerStage; ++i) load_block(straddle_tag, i, row0, gs, kst(s_tag), vst(Prev{}));
+    };
+    if constexpr (PAGED) {
+      if (gs.straddles) loads(std::true_type{});
+      else loads(std::false_type{});
+    } else {
+      loads(std::false_type{});
+    }
   };
 
+  // ---- paged: the append's reads go out first; its writes follow once the first stage has landed ----
+  ChunkAppend<D, kTileRows, 512> app;
+  if constexpr (PAGED)
+    if (hsub == 0) app.load(a, kh, vh, kv_stride, b, g, q0_tile, min(kTileRows, n_q - q0_tile), qoff, tid);
   // ---- Q fragments first (their loads then retire before the ring's) ----
   u32x4_t qf[kKSteps];
   {
@@ -1013,6 +1061,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   // Q and stage 0 have landed (loads after them: stages 1 .. STAGES-1)
   wait_vmcnt<(STAGES - 1) * kLoadsPerStage>();
   tile_barrier();
+  if constexpr (PAGED)
+    if (hsub == 0) app.store();
 
   // Periods 2i and 2i + 1 use stage i (u = i % STAGES).  Each group runs its own copy of the loop
   // (same barriers, in the same number), so the state flows straight from one phase to the next.
@@ -1097,27 +1147,6 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     if (a.lse != nullptr && half == 0) {
       const size_t li = PAGED ? q_base / D + (size_t)row * a.H : ((size_t)b * a.H + head) * N + row;
       a.lse[li] = a.scale * m_run + __logf(l_tot);
-    }
-  }
-
-  // ---- paged: append this workgroup's chunk rows to the caches (as in the lock-step kernel) ----
-  if constexpr (PAGED) {
-    if (hsub == 0) {
-      constexpr int kChunks = D / 8;
-      const int rows = min(kTileRows, n_q - q0_tile);
-      for (int e = tid; e < 2 * rows * kChunks; e += 64 * WAVES) {
-        const bool is_v = e >= rows * kChunks;
-        const int f = is_v ? e - rows * kChunks : e;
-        const int i = q0_tile + f / kChunks;
-        const int c = f % kChunks;
-        const int pos = qoff + i;
-        const int blk = pos / kPageTokens;
-        const int page = blk < a.max_pages ? a.bt[(size_t)b * a.max_pages + blk] : -1;
-        if (page < 0 || page >= a.num_pages) continue;
-        const u32x4_t val = *(const u32x4_t*)((is_v ? vh : kh) + (size_t)i * kv_stride + c * 8);
-        uint16_t* dst = (is_v ? a.vc : a.kc) + (((size_t)page * kPageTokens + pos % kPageTokens) * a.Hkv + g) * D + c * 8;
-        *(u32x4_t*)dst = val;
-      }
     }
   }
 }
