@@ -1132,16 +1132,47 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   const int row = q0 + l32;
   const float l_tot = l_run + swap_halves(l_run, half);
   const float inv_l = 1.f / (lr_run + swap_halves(lr_run, half));
-  if (row < n_q) {
-    uint16_t* orow = a.o + q_base + (size_t)row * q_stride;
+  if constexpr (!KSPLIT) {
+    // O leaves through LDS, so that every store instruction writes whole rows (16 lanes x 16 bytes
+    // per row) instead of 8 bytes in each of 32 rows.  The ring is idle: the last period pair ended
+    // with every load landed and a barrier after every read.  Each wave stages its own 32 x D tile
+    // (8 KB) in its accumulator layout, 16-byte chunk c of row r at chunk c ^ (r % 16), which keeps
+    // both the 8-byte writes and the 16-byte reads free of bank conflicts.
+    static_assert(D == 128 && kSlots == 1, "a wave's O tile is half a stage array");
+    PAA_LDS char* ot = (wave / 2 == 0   ? (PAA_LDS char*)k_st0
+                        : wave / 2 == 1 ? (PAA_LDS char*)k_st1
+                        : wave / 2 == 2 ? (PAA_LDS char*)v_st0
+                                        : (PAA_LDS char*)v_st1) + (wave % 2) * (32 * T::kRowBytes);
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const int d0 = 32 * db + 8 * gq + 4 * half;
+        const int chunk = 4 * db + gq;  // columns 32db + 8gq .. +7; this half-wave's 4 start at 4 * half
         u32x2_t w = {pack_bf16x2(acc[db][4 * gq + 0] * inv_l, acc[db][4 * gq + 1] * inv_l),
                      pack_bf16x2(acc[db][4 * gq + 2] * inv_l, acc[db][4 * gq + 3] * inv_l)};
-        *(u32x2_t*)(orow + d0) = w;
+        *(PAA_LDS u32x2_t*)(ot + l32 * T::kRowBytes + ((chunk ^ (l32 % 16)) * 16) + 8 * half) = w;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 32 / 4; ++k) {
+      const int r = 4 * k + lane / 16;  // tile row
+      const int c = lane % 16;          // 16-byte chunk of the row
+      const u32x4_t v = *(const PAA_LDS u32x4_t*)(ot + r * T::kRowBytes + ((c ^ (r % 16)) * 16));
+      if (q0 + r < n_q) *(u32x4_t*)(a.o + q_base + (size_t)(q0 + r) * q_stride + c * 8) = v;
+    }
+  }
+  if (row < n_q) {
+    if constexpr (KSPLIT) {
+      uint16_t* orow = a.o + q_base + (size_t)row * q_stride;
+#pragma unroll
+      for (int db = 0; db < kDBlocks; ++db) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d0 = 32 * db + 8 * gq + 4 * half;
+          u32x2_t w = {pack_bf16x2(acc[db][4 * gq + 0] * inv_l, acc[db][4 * gq + 1] * inv_l),
+                       pack_bf16x2(acc[db][4 * gq + 2] * inv_l, acc[db][4 * gq + 3] * inv_l)};
+          *(u32x2_t*)(orow + d0) = w;
+        }
       }
     }
     if (a.lse != nullptr && half == 0) {
