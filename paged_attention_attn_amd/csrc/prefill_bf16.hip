@@ -258,6 +258,35 @@ __device__ __forceinline__ void group_load(PAA_LDS void* dst, const GroupSource&
   }
 }
 
+// O leaves through LDS, so that every store instruction writes whole rows (D / 8 lanes x 16 bytes
+// per row) instead of 8 bytes in each of 32 rows: a wave stages its 32 x D output tile (bf16, already
+// divided by the row sums) in its accumulator layout, 16-byte chunk c of row r at position
+// c ^ (r % (D / 8)), and reads it back row by row.  The staging area (32 rows of D bf16) is the
+// wave's own; rows at or past `rows` are not written.
+template <int D>
+__device__ __forceinline__ void store_o_tile(PAA_LDS char* ot, const f32x16_t (&acc)[D / 32], float inv_l, int lane,
+                                             uint16_t* o_row0, size_t row_stride, int rows) {
+  using T = TileLayout<D>;
+  const int l32 = lane % 32, half = lane / 32;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int chunk = 4 * db + gq;  // columns 32db + 8gq .. +7; this half-wave's 4 start at 4 * half
+      const u32x2_t w = {pack_bf16x2(acc[db][4 * gq + 0] * inv_l, acc[db][4 * gq + 1] * inv_l),
+                         pack_bf16x2(acc[db][4 * gq + 2] * inv_l, acc[db][4 * gq + 3] * inv_l)};
+      *(PAA_LDS u32x2_t*)(ot + l32 * T::kRowBytes + ((chunk ^ (l32 % T::kCpr)) * 16) + 8 * half) = w;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 32 / T::kRowsPerBlock; ++k) {
+    const int r = k * T::kRowsPerBlock + lane / T::kCpr;  // tile row
+    const int c = lane % T::kCpr;                        // 16-byte chunk of the row
+    const u32x4_t v = *(const PAA_LDS u32x4_t*)(ot + r * T::kRowBytes + ((c ^ (r % T::kCpr)) * 16));
+    if (r < rows) *(u32x4_t*)(o_row0 + (size_t)r * row_stride + c * 8) = v;
+  }
+}
+
 // Appending a workgroup's chunk rows (its KV head, its query tile) to the caches.  One workgroup per
 // (sequence, KV head, query tile) does it, the one holding the head group's first query heads, so
 // every new row is written exactly once.  No workgroup of the launch reads cache positions at or
@@ -675,23 +704,22 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
   wait_vmcnt<0>();  // no load may still be writing this workgroup's LDS when it exits
 
   // ---- epilogue: O = acc / (sum of the rounded probabilities), LSE = scale * m + ln(l) ----
+  // O leaves through LDS (store_o_tile); wave w stages each of its row blocks in half of one stage
+  // array, once every wave is past its last tile (every load landed, every tile read done).
+  static_assert(RB == 1 && WAVES <= 2 * 2 * STAGES, "each wave's O tile is half of its own stage array");
+  __syncthreads();
+  PAA_LDS char* ot = (wave / 2 == 0   ? (PAA_LDS char*)k_st0
+                      : wave / 2 == 1 ? (PAA_LDS char*)k_st1
+                      : wave / 2 == 2 ? (PAA_LDS char*)v_st0
+                                      : (PAA_LDS char*)v_st1) + (wave % 2) * (32 * T::kRowBytes);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int row = q0 + 32 * rb + l32;
     const float l_tot = l_run[rb] + swap_halves(l_run[rb], half);
     const float inv_l = 1.f / (lr_run[rb] + swap_halves(lr_run[rb], half));
+    store_o_tile<D>(ot, acc[rb], inv_l, lane, a.o + q_base + (size_t)(q0 + 32 * rb) * q_stride, q_stride,
+                    n_q - q0 - 32 * rb);
     if (row < n_q) {
-      uint16_t* orow = a.o + q_base + (size_t)row * q_stride;
-#pragma unroll
-      for (int db = 0; db < kDBlocks; ++db) {
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int d0 = 32 * db + 8 * gq + 4 * half;
-          u32x2_t w = {pack_bf16x2(acc[rb][db][4 * gq + 0] * inv_l, acc[rb][db][4 * gq + 1] * inv_l),
-                       pack_bf16x2(acc[rb][db][4 * gq + 2] * inv_l, acc[rb][db][4 * gq + 3] * inv_l)};
-          *(u32x2_t*)(orow + d0) = w;
-        }
-      }
       if (a.lse != nullptr && half == 0) {
         const size_t li = PAGED ? q_base / D + (size_t)row * a.H : ((size_t)b * a.H + head) * N + row;
         a.lse[li] = a.scale * m_run[rb] + __logf(l_tot);
@@ -1133,33 +1161,14 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   const float l_tot = l_run + swap_halves(l_run, half);
   const float inv_l = 1.f / (lr_run + swap_halves(lr_run, half));
   if constexpr (!KSPLIT) {
-    // O leaves through LDS, so that every store instruction writes whole rows (16 lanes x 16 bytes
-    // per row) instead of 8 bytes in each of 32 rows.  The ring is idle: the last period pair ended
-    // with every load landed and a barrier after every read.  Each wave stages its own 32 x D tile
-    // (8 KB) in its accumulator layout, 16-byte chunk c of row r at chunk c ^ (r % 16), which keeps
-    // both the 8-byte writes and the 16-byte reads free of bank conflicts.
+    // The ring is idle: the last period pair ended with every load landed and a barrier after
+    // every read.  Wave w stages its tile in half of one stage array.
     static_assert(D == 128 && kSlots == 1, "a wave's O tile is half a stage array");
     PAA_LDS char* ot = (wave / 2 == 0   ? (PAA_LDS char*)k_st0
                         : wave / 2 == 1 ? (PAA_LDS char*)k_st1
                         : wave / 2 == 2 ? (PAA_LDS char*)v_st0
                                         : (PAA_LDS char*)v_st1) + (wave % 2) * (32 * T::kRowBytes);
-#pragma unroll
-    for (int db = 0; db < kDBlocks; ++db) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int chunk = 4 * db + gq;  // columns 32db + 8gq .. +7; this half-wave's 4 start at 4 * half
-        u32x2_t w = {pack_bf16x2(acc[db][4 * gq + 0] * inv_l, acc[db][4 * gq + 1] * inv_l),
-                     pack_bf16x2(acc[db][4 * gq + 2] * inv_l, acc[db][4 * gq + 3] * inv_l)};
-        *(PAA_LDS u32x2_t*)(ot + l32 * T::kRowBytes + ((chunk ^ (l32 % 16)) * 16) + 8 * half) = w;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < 32 / 4; ++k) {
-      const int r = 4 * k + lane / 16;  // tile row
-      const int c = lane % 16;          // 16-byte chunk of the row
-      const u32x4_t v = *(const PAA_LDS u32x4_t*)(ot + r * T::kRowBytes + ((c ^ (r % 16)) * 16));
-      if (q0 + r < n_q) *(u32x4_t*)(a.o + q_base + (size_t)(q0 + r) * q_stride + c * 8) = v;
-    }
+    store_o_tile<D>(ot, acc, inv_l, lane, a.o + q_base + (size_t)q0 * q_stride, q_stride, n_q - q0);
   }
   if (row < n_q) {
     if constexpr (KSPLIT) {
