@@ -84,4 +84,35 @@ __device__ __forceinline__ float swap_halves(float x, bool upper) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Stores a wave's 32 x D output tile through LDS, so that every store instruction writes whole rows
+// (D / 8 lanes x 16 bytes per row) instead of 8 bytes in each of 32 rows.  acc is O^T in the
+// 32x32x16 accumulator layout (lane l, block db, element i: row l % 32, column 32db + 8(i/4) +
+// 4(l/32) + i%4), scaled by f and rounded to bf16; the tile is staged at `ot` (32 rows of 2D bytes,
+// the wave's own) with 16-byte chunk c of row r at position c ^ (r % (D / 8)), which keeps the
+// 8-byte writes and the 16-byte reads free of most bank conflicts, then read back row by row.  Rows
+// at or past `rows` are not written.
+template <int D>
+__device__ __forceinline__ void store_o_tile(PAA_LDS char* ot, const f32x16_t (&acc)[D / 32], float f, int lane,
+                                             uint16_t* o_row0, size_t row_stride, int rows) {
+  constexpr int kRowBytes = 2 * D, kCpr = D / 8, kRowsPerBlock = 64 / kCpr;
+  const int l32 = lane % 32, half = lane / 32;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int chunk = 4 * db + gq;  // columns 32db + 8gq .. +7; this half-wave's 4 start at 4 * half
+      const u32x2_t w = {pack_bf16x2(acc[db][4 * gq + 0] * f, acc[db][4 * gq + 1] * f),
+                         pack_bf16x2(acc[db][4 * gq + 2] * f, acc[db][4 * gq + 3] * f)};
+      *(PAA_LDS u32x2_t*)(ot + l32 * kRowBytes + ((chunk ^ (l32 % kCpr)) * 16) + 8 * half) = w;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 32 / kRowsPerBlock; ++k) {
+    const int r = k * kRowsPerBlock + lane / kCpr;  // tile row
+    const int c = lane % kCpr;                        // 16-byte chunk of the row
+    const u32x4_t v = *(const PAA_LDS u32x4_t*)(ot + r * kRowBytes + ((c ^ (r % kCpr)) * 16));
+    if (r < rows) *(u32x4_t*)(o_row0 + (size_t)r * row_stride + c * 8) = v;
+  }
+}
+
 }  // namespace paa

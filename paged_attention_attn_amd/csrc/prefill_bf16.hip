@@ -258,35 +258,6 @@ __device__ __forceinline__ void group_load(PAA_LDS void* dst, const GroupSource&
   }
 }
 
-// O leaves through LDS, so that every store instruction writes whole rows (D / 8 lanes x 16 bytes
-// per row) instead of 8 bytes in each of 32 rows: a wave stages its 32 x D output tile (bf16, already
-// divided by the row sums) in its accumulator layout, 16-byte chunk c of row r at position
-// c ^ (r % (D / 8)), and reads it back row by row.  The staging area (32 rows of D bf16) is the
-// wave's own; rows at or past `rows` are not written.
-template <int D>
-__device__ __forceinline__ void store_o_tile(PAA_LDS char* ot, const f32x16_t (&acc)[D / 32], float inv_l, int lane,
-                                             uint16_t* o_row0, size_t row_stride, int rows) {
-  using T = TileLayout<D>;
-  const int l32 = lane % 32, half = lane / 32;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int chunk = 4 * db + gq;  // columns 32db + 8gq .. +7; this half-wave's 4 start at 4 * half
-      const u32x2_t w = {pack_bf16x2(acc[db][4 * gq + 0] * inv_l, acc[db][4 * gq + 1] * inv_l),
-                         pack_bf16x2(acc[db][4 * gq + 2] * inv_l, acc[db][4 * gq + 3] * inv_l)};
-      *(PAA_LDS u32x2_t*)(ot + l32 * T::kRowBytes + ((chunk ^ (l32 % T::kCpr)) * 16) + 8 * half) = w;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < 32 / T::kRowsPerBlock; ++k) {
-    const int r = k * T::kRowsPerBlock + lane / T::kCpr;  // tile row
-    const int c = lane % T::kCpr;                        // 16-byte chunk of the row
-    const u32x4_t v = *(const PAA_LDS u32x4_t*)(ot + r * T::kRowBytes + ((c ^ (r % T::kCpr)) * 16));
-    if (r < rows) *(u32x4_t*)(o_row0 + (size_t)r * row_stride + c * 8) = v;
-  }
-}
-
 // Appending a workgroup's chunk rows (its KV head, its query tile) to the caches.  One workgroup per
 // (sequence, KV head, query tile) does it, the one holding the head group's first query heads, so
 // every new row is written exactly once.  No workgroup of the launch reads cache positions at or

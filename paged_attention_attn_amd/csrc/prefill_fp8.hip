@@ -384,24 +384,22 @@ __global__ __launch_bounds__(512, 1) void prefill_fp8_kernel(Fp8Args a) {
   wait_vmcnt<0>();
 
   // ---- epilogue: O = v_scale * acc / (sum of rounded p), LSE = scale_eff * m + ln(sum of p) - shift ----
+  // O leaves through LDS (store_o_tile), wave w's tile in half of one stage array, once every wave is
+  // past its last tile (every load landed, every tile read done).
   const int row = q0 + l32;
   const float l_tot = l_run + swap_halves(l_run, half);
   const float f = a.v_scale / acc_l[0];
-  if (row < a.N) {
-    uint16_t* orow = a.o + (((size_t)b * a.H + head) * N + row) * D;
-#pragma unroll
-    for (int db = 0; db < kDBlocks; ++db) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d0 = 32 * db + 8 * gq + 4 * half;
-        u32x2_t w = {pack_bf16x2(acc[db][4 * gq + 0] * f, acc[db][4 * gq + 1] * f),
-                     pack_bf16x2(acc[db][4 * gq + 2] * f, acc[db][4 * gq + 3] * f)};
-        *(u32x2_t*)(orow + d0) = w;
-      }
-    }
-    if (a.lse != nullptr && half == 0) a.lse[((size_t)b * a.H + head) * N + row] =
-        a.scale_eff * m_run + (__logf(l_tot) - kFp8ShiftLog2 * kLn2);
-  }
+  static_assert(WAVES * 32 * 2 * D <= 2 * STAGES * kSub * T::kKTileBytes && T::kKTileBytes == T::kVTileBytes &&
+                    kSub * T::kKTileBytes == 2 * 32 * 2 * D,
+                "two waves' O tiles fill one stage array");
+  __syncthreads();
+  PAA_LDS char* ot = (wave / 2 == 0   ? (PAA_LDS char*)k_st0
+                      : wave / 2 == 1 ? (PAA_LDS char*)k_st1
+                      : wave / 2 == 2 ? (PAA_LDS char*)v_st0
+                                      : (PAA_LDS char*)v_st1) + (wave % 2) * (32 * 2 * D);
+  store_o_tile<D>(ot, acc, f, lane, a.o + (((size_t)b * a.H + head) * N + q0) * D, D, a.N - q0);
+  if (row < a.N && a.lse != nullptr && half == 0)
+    a.lse[((size_t)b * a.H + head) * N + row] = a.scale_eff * m_run + (__logf(l_tot) - kFp8ShiftLog2 * kLn2);
 }
 
 template <typename Kernel>
