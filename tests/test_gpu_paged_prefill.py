@@ -194,3 +194,43 @@ def test_paged_prefill_full_workload_whole():
     st.update(assert_close_lse(lse, rl))
     assert np.array_equal(kc, rkc) and np.array_equal(vc, rvc)
     _announce(f"{w.name}: {st}")
+
+
+# (ctx lengths, chunk lengths, H, Hkv): a small grid (lock-step kernel) and one of 1024 eight-wave units
+# (ping-pong kernel: 64 sequences x 8 KV heads x 2 query tiles)
+OOB = [([37, 0, 300, 64], [50, 20, 129, 1], 8, 2),
+       ([(37 * s) % 301 for s in range(64)], [128 if s % 3 else 65 for s in range(64)], 32, 8)]
+
+
+@pytest.mark.parametrize("bad", [-1, "pool"])
+@pytest.mark.parametrize("case", range(len(OOB)))
+def test_paged_prefill_pages_outside_pool_are_not_written(case, bad):
+    """Block-table entries of the chunk-only blocks set outside [0, num_pages) (no room reserved for the
+    chunk): those rows are not appended and no other cache byte changes; rows that fall in the last
+    context block (a valid page) are appended; O and LSE are unaffected, since no key position at or
+    past the context length is read from the cache."""
+    ctxs, qlens, H, Hkv = OOB[case]
+    w = ChunkedPrefillWorkload("oob", len(ctxs), H, Hkv, 128, 0, 300, 0, num_pages=2048)
+    a = chunked_prefill_inputs(w, seed=21 + case, ctx_lens=ctxs, q_lens=qlens)
+    _announce(f"paged_prefill pages outside the pool: {len(ctxs)} sequences, H{H} Hkv{Hkv} ({bad})")
+    ro, rl, _, _ = _oracle(a)
+    bt = a["block_table"].copy()
+    num_pages = a["k_cache"].shape[0]
+    for s, c in enumerate(ctxs):
+        first_chunk_only = -(-c // 16)  # blocks from here on hold no context token
+        bt[s, first_chunk_only:] = -1 if bad == -1 else num_pages + 5 + s
+    b = dict(a, block_table=bt)
+    o, lse, kc, vc = _run(b)
+    assert_close_bf16(o, ro)
+    assert_close_lse(lse, rl)
+    # expected caches: the inputs with only the rows whose page is valid appended
+    ekc, evc = a["k_cache"].copy(), a["v_cache"].copy()
+    for s, c in enumerate(ctxs):
+        lo = int(a["q_start"][s])
+        for i in range(qlens[s]):
+            pos = c + i
+            page = int(bt[s, pos // 16])
+            if 0 <= page < num_pages:
+                ekc[page, pos % 16] = a["k_new"][lo + i]
+                evc[page, pos % 16] = a["v_new"][lo + i]
+    assert np.array_equal(kc, ekc) and np.array_equal(vc, evc)
