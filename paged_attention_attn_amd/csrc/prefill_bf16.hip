@@ -1135,6 +1135,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     // The ring is idle: the last period pair ended with every load landed and a barrier after
     // every read.  Wave w stages its tile in half of one stage array.
     static_assert(D == 128 && kSlots == 1, "a wave's O tile is half a stage array");
+    static_assert(STAGES == 2, "every period pair ends with vmcnt(0) and a barrier only with two stages");
     PAA_LDS char* ot = (wave / 2 == 0   ? (PAA_LDS char*)k_st0
                         : wave / 2 == 1 ? (PAA_LDS char*)k_st1
                         : wave / 2 == 2 ? (PAA_LDS char*)v_st0
