@@ -95,3 +95,25 @@ def zero_query_expected(v, H, causal, window=0, n_global=0):
     lse = np.broadcast_to(np.log(cnt), (B, H, N))
     return o, lse
 
+
+
+def decode_zero_query_expected(v_rows_f64, v_cache, block_table, seq_lens, H):
+    """Closed form of paged decode (one query per sequence over its cached keys, gathered through the
+    block table: "Fast Attention Kernels and Operator Fusion", "Paged Attention Kernels") when q = 0:
+    every cached key scores 0, so each head's output is the mean of its KV head's V rows over the
+    sequence's L tokens and LSE = ln L (an empty sequence gives O = 0 and LSE = -inf).  v_cache is
+    the raw pool [num_pages, page_size, Hkv, d]; v_rows_f64 turns gathered raw rows into float64
+    values.  Returns O [S, H, d] and LSE [S, H]."""
+    num_pages, page_size, Hkv, d = v_cache.shape
+    S = len(seq_lens)
+    o = np.zeros((S, H, d))
+    lse = np.full((S, H), -np.inf)
+    for s in range(S):
+        L = int(seq_lens[s])
+        if L <= 0:
+            continue
+        pages = np.asarray(block_table[s][: -(-L // page_size)])
+        rows = v_rows_f64(v_cache[pages]).reshape(-1, Hkv, d)[:L]  # token t at page t // page_size
+        o[s] = np.repeat(rows.mean(axis=0), H // Hkv, axis=0)      # query head h reads KV head h // group
+        lse[s] = np.log(L)
+    return o, lse

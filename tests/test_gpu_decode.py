@@ -13,7 +13,7 @@ import torch
 import oracle
 import oracle_pool
 import paged_attention_attn_amd as paa
-from gpu_util import assert_close_bf16, assert_close_lse, dev_bf16, dev_i32, host_f64
+from gpu_util import assert_close_bf16, assert_close_lse, decode_zero_query_expected, dev_bf16, dev_i32, host_f64
 from workloads import WORKLOADS, DecodeWorkload, decode_inputs
 
 pytestmark = pytest.mark.gpu
@@ -392,3 +392,17 @@ def test_decode_graph_layers_in_one_submission():
                 assert_close_lse(l_g.cpu().numpy().astype(np.float64), rl)
     finally:
         g.close()
+
+
+@pytest.mark.timeout(300)
+def test_decode_zero_query_closed_form_full_size():
+    """q = 0 on the full 64-sequence workload: every head returns the mean of its KV head's V rows over
+    the sequence and LSE = ln L (closed form, no oracle), every element."""
+    w = WORKLOADS["paged_decode_s64h32kv8d128"]
+    _announce(f"{w.name} q=0")
+    a = decode_inputs(w, seed=3)
+    a["q"] = np.zeros_like(a["q"])
+    o, lse, _ = _run(a, w.H)
+    ro, rl = decode_zero_query_expected(oracle.bf16_bits_to_f64, a["v_cache"], a["block_table"], a["seq_lens"], w.H)
+    assert_close_bf16(o, ro)
+    assert_close_lse(lse, rl)

@@ -11,7 +11,7 @@ import torch
 import oracle
 import oracle_pool
 import paged_attention_attn_amd as paa
-from gpu_util import assert_close_bf16, assert_close_lse, dev_bf16, dev_i32, host_f64
+from gpu_util import assert_close_bf16, assert_close_lse, decode_zero_query_expected, dev_bf16, dev_i32, host_f64
 from workloads import WORKLOADS, DecodeWorkload, decode_inputs_fp8
 
 pytestmark = pytest.mark.gpu
@@ -128,5 +128,20 @@ def test_fp8_decode_out_of_range_page_id_is_not_read():
     two["block_table"] = np.array([[2, 7, -1]], dtype=np.int32)
     two["seq_lens"] = np.array([32], dtype=np.int32)
     ro, rl = _oracle(two)
+    assert_close_bf16(o, ro)
+    assert_close_lse(lse, rl)
+
+
+@pytest.mark.timeout(300)
+def test_fp8_decode_zero_query_closed_form_full_size():
+    """q = 0 on the full 64-sequence workload over the E4M3 cache: every head returns v_scale times the
+    mean of its KV head's decoded V rows and LSE = ln L (closed form, no oracle), every element."""
+    w = WORKLOADS["paged_decode_s64h32kv8d128"]
+    _announce(f"{w.name} fp8 cache q=0")
+    a = decode_inputs_fp8(w, seed=3)
+    a["q"] = np.zeros_like(a["q"])
+    o, lse, _ = _run(a, w.H)
+    ro, rl = decode_zero_query_expected(lambda raw: oracle.e4m3_bits_to_f64(raw) * a["v_scale"], a["v_cache"],
+                                        a["block_table"], a["seq_lens"], w.H)
     assert_close_bf16(o, ro)
     assert_close_lse(lse, rl)

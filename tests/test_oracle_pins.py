@@ -143,3 +143,25 @@ def test_zero_query_closed_form(causal, window, n_global):
     np.testing.assert_allclose(ro[1, 3, i], v[1, 1, vis].mean(axis=0), rtol=0, atol=1e-12)
     np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
     np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-12)
+
+
+def test_decode_zero_query_closed_form():
+    """q = 0 in decode: the oracle returns each head the mean of its KV head's V rows over the sequence
+    (gathered through the block table) and LSE = ln L; this pins the oracle's decode gather and the
+    closed form the full-size GPU tests compare against."""
+    from gpu_util import decode_zero_query_expected
+    from workloads import DecodeWorkload, decode_inputs
+    lens = [1, 15, 16, 17, 40, 0, 100]
+    w = DecodeWorkload("zq", len(lens), 8, 2, 16, 1, 128, 16, 64)
+    a = decode_inputs(w, seed=5, seq_lens=lens)
+    a["q"] = np.zeros_like(a["q"])
+    o, lse = oracle.paged_decode(a["q"], a["k_cache"], a["v_cache"], a["block_table"], a["seq_lens"], a["scale"])
+    ro, rl = decode_zero_query_expected(oracle.bf16_bits_to_f64, a["v_cache"], a["block_table"], a["seq_lens"], 8)
+    # brute force for sequence 4, head 5 (KV head 1): token t from page bt[4][t // 16], slot t % 16
+    v = oracle.bf16_bits_to_f64(a["v_cache"])
+    rows = [v[a["block_table"][4][t // 16], t % 16, 1] for t in range(40)]
+    np.testing.assert_allclose(ro[4, 5], np.mean(rows, axis=0), rtol=0, atol=1e-12)
+    live = np.asarray(lens) > 0
+    np.testing.assert_allclose(o[live], ro[live], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[live], rl[live], rtol=0, atol=1e-12)
+    assert np.all(np.isneginf(rl[~live])) and np.all(ro[~live] == 0)
