@@ -52,6 +52,7 @@ sys.path.insert(0, ROOT)
 METRIC = "causal prefill attention TFLOP/s + paged decode KV GB/s, % of roofline"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0  # dense fp8 MFMA
+PEAK_CLOCK_GHZ = 2.4  # the engine clock both MFMA peaks are quoted at
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_counters.txt")
@@ -144,25 +145,32 @@ def read_traffic(workload: str):
 
 
 def read_mfma_busy(workload: str):
-    """MfmaUtil (%) of the workload's attention kernel from the committed counter summary, if taken on these
-    sources."""
+    """(MfmaUtil %, MFMA flops executed per algorithmic flop) of the workload's attention kernel from the
+    committed counter summary, if taken on these sources; (None, None) otherwise."""
     if not os.path.exists(MFMA_FILE):
-        return None
+        return None, None
     with open(MFMA_FILE) as f:
         for line in f:
             if line.startswith("{"):
                 e = json.loads(line)
                 if e.get("workload") == workload and e.get("sources") == source_digest() and \
                         e.get("mfma_tflop_per_call", 0) > 0:
-                    return e["mfma_util_pct"]
-    return None
+                    alg = e.get("algorithmic_tflop")
+                    return e["mfma_util_pct"], (e["mfma_tflop_per_call"] / alg if alg else None)
+    return None, None
 
 
-def roofline(kind, achieved, peak, unit, traffic, mfma_busy_pct=None):
+def roofline(kind, achieved, peak, unit, traffic, mfma=(None, None)):
     r = {"bound": kind, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
          "frac": round(achieved / peak, 4), "traffic": traffic}
     if kind == "mfma":
-        r["mfma_busy_pct"] = mfma_busy_pct  # matrix-core busy share of active cycles (counters), or None
+        busy, executed_per_alg = mfma
+        r["mfma_busy_pct"] = busy  # matrix-core busy share of active cycles (counters), or None
+        if busy and executed_per_alg and peak == PEAK_BF16_TFLOPS:
+            # the peak assumes every matrix-core cycle busy at PEAK_CLOCK_GHZ; the counters give the busy
+            # share, so the clock the kernel ran at is what reconciles the two (bf16 MFMAs only: the busy
+            # cycles of the 8-bit MFMA do not scale the same way)
+            r["implied_clock_ghz"] = round(PEAK_CLOCK_GHZ * achieved * executed_per_alg / peak / (busy / 100.0), 2)
     return r
 
 
