@@ -907,9 +907,11 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
   ChunkAppend<D, kTileRows, 512> app;
   if constexpr (PAGED)
     if (hsub == 0) app.load(a, kh, vh, kv_stride, b, g, q0_tile, min(kTileRows, n_q - q0_tile), qoff, tid);
-  // ---- Q fragments first (their loads then retire before the ring's) ----
+  // ---- Q first, through the idle ring: each wave's 32 rows go to half of one stage array by direct
+  // loads (whole rows per instruction, chunk-swizzled as the K tiles are), reach the VGPRs (the MFMA
+  // B operand) once landed, and the ring is refilled only after every wave has read its rows ----
   u32x4_t qf[kKSteps];
-  {
+  if constexpr (KSPLIT) {
     const int row = q0 + l32;
 #pragma unroll
     for (int t = 0; t < kKSteps; ++t) {
@@ -918,6 +920,28 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
       else
         qf[t] = u32x4_t{0, 0, 0, 0};
     }
+  } else {
+    PAA_LDS char* qs = (wave / 2 == 0   ? (PAA_LDS char*)k_st0
+                        : wave / 2 == 1 ? (PAA_LDS char*)k_st1
+                        : wave / 2 == 2 ? (PAA_LDS char*)v_st0
+                                        : (PAA_LDS char*)v_st1) + (wave % 2) * (32 * T::kRowBytes);
+    const int rows = max(0, min(32, n_q - q0));
+    const int bytes = rows > 0 ? (int)(((size_t)(rows - 1) * q_stride + D) * 2) : 0;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(qh + (size_t)max(0, min(q0, n_q)) * q_stride), (short)0, bytes,
+                                          kRawBufferWord3);
+#pragma unroll
+    for (int k = 0; k < 32 / T::kRowsPerBlock; ++k) {
+      const int r = k * T::kRowsPerBlock + lane / T::kCpr;
+      const int c = (lane % T::kCpr) ^ swz<D>(r);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (PAA_LDS void*)(qs + k * 1024), 16,
+                                               (int)((r * q_stride + c * 8) * 2), 0, 0, 0);
+    }
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int t = 0; t < kKSteps; ++t)
+      qf[t] = *(const PAA_LDS u32x4_t*)(qs + l32 * T::kRowBytes + (((2 * t + half) ^ swz<D>(l32)) * 16));
+    __syncthreads();  // every wave holds its Q before the ring's first loads overwrite it
   }
   // prologue: stages 0 .. STAGES-1 (stage 0's V half repeats tile 0 into a free buffer)
   issue_stage(std::integral_constant<int, 0>{}, 0, stage_page(0));
