@@ -406,3 +406,28 @@ def test_decode_zero_query_closed_form_full_size():
     ro, rl = decode_zero_query_expected(oracle.bf16_bits_to_f64, a["v_cache"], a["block_table"], a["seq_lens"], w.H)
     assert_close_bf16(o, ro)
     assert_close_lse(lse, rl)
+
+
+def test_decode_gqa_equals_mha_with_repeated_kv():
+    """Decode with 32 query heads over 8 KV heads against the same call with each KV head repeated for its
+    4 query heads (32 KV heads in the pool). The number of equal page ranges is the smaller of the pages
+    the block table spans and the launch's wave budget over the KV heads, so it depends on Hkv: where the
+    table spans few pages both calls cut the same ranges and agree bit for bit; where it spans many, the
+    two calls merge different ranges and each stays within the oracle's bars."""
+    small = DecodeWorkload("gqa_mha_small", 4, 32, 8, 128, 100, 250, 16, 400)
+    large = DecodeWorkload("gqa_mha_large", 16, 32, 8, 128, 100, 2000, 16, 4000)
+    for w, seed, bitwise in ((small, 77, True), (large, 78, False)):
+        _announce(f"decode GQA vs MHA repeated {w.name}")
+        a = decode_inputs(w, seed=seed)
+        if bitwise:
+            assert a["block_table"].size <= 64  # both calls cut one range per page
+        o_g, l_g, _ = _run(a, w.H)
+        b = dict(a, k_cache=np.repeat(a["k_cache"], 4, axis=2), v_cache=np.repeat(a["v_cache"], 4, axis=2))
+        o_m, l_m, _ = _run(b, w.H)
+        if bitwise:
+            assert np.array_equal(o_g, o_m) and np.array_equal(l_g, l_m)
+        else:
+            ro, rl = _oracle(a)
+            for o, lse in ((o_g, l_g), (o_m, l_m)):
+                assert_close_bf16(o, ro)
+                assert_close_lse(lse, rl)

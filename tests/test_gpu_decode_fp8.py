@@ -145,3 +145,20 @@ def test_fp8_decode_zero_query_closed_form_full_size():
                                         a["block_table"], a["seq_lens"], w.H)
     assert_close_bf16(o, ro)
     assert_close_lse(lse, rl)
+
+
+def test_fp8_decode_gqa_equals_mha_with_repeated_kv():
+    """E4M3-cache decode with 32 query heads over 8 KV heads against the same call with each KV head
+    repeated for its 4 query heads. The block table spans 64 pages or fewer, so both calls cut one
+    range per page and each query head's O and LSE agree bit for bit."""
+    w = DecodeWorkload("fp8_gqa_mha", 4, 32, 8, 128, 100, 250, 16, 400)
+    _announce("fp8 decode GQA vs MHA repeated")
+    a = decode_inputs_fp8(w, seed=81)
+    assert a["block_table"].size <= 64
+    o_g, l_g, _ = _run(a, w.H)
+    b = dict(a, k_cache=np.repeat(a["k_cache"], 4, axis=2), v_cache=np.repeat(a["v_cache"], 4, axis=2))
+    o_m, l_m, _ = _run(b, w.H)
+    assert np.array_equal(o_g, o_m) and np.array_equal(l_g, l_m)
+    ro, rl = _oracle(a)
+    assert_close_bf16(o_g, ro)
+    assert_close_lse(l_g, rl)

@@ -237,3 +237,15 @@ def test_fp8_zero_query_closed_form(B, H, Hkv, N, d, causal):
     ro, rl = zero_query_expected(v, H, causal)
     assert_close_bf16(o, ro)
     assert_close_lse(lse, rl)
+
+
+def test_fp8_gqa_equals_mha_with_repeated_kv():
+    """FP8 prefill with 32 query heads over 8 KV heads against the same call with each KV head repeated
+    for its 4 query heads: O and LSE agree bit for bit (B=2, N=2048, causal)."""
+    w = PrefillWorkload("fp8_gqa_mha", 2, 32, 8, 2048, 128, True, dtype="fp8")
+    _announce("attn_fwd_fp8 GQA vs MHA repeated")
+    a = prefill_inputs(w, seed=79)
+    o_g, l_g = _run(a, w)
+    b = dict(a, k8=np.repeat(a["k8"], 4, axis=1), vt8=np.repeat(a["vt8"], 4, axis=1))
+    o_m, l_m = _run(b, PrefillWorkload("fp8_gqa_mha", 2, 32, 32, 2048, 128, True, dtype="fp8"))
+    assert np.array_equal(o_g, o_m) and np.array_equal(l_g, l_m)

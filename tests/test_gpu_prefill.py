@@ -286,3 +286,23 @@ def test_bf16_zero_query_closed_form(B, H, Hkv, N, d, causal, window, n_global):
     ro, rl = zero_query_expected(vf, H, causal, window, n_global)
     assert_close_bf16(host_f64(o), ro)
     assert_close_lse(lse.cpu().numpy().astype(np.float64), rl)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("causal", [True, False])
+def test_gqa_equals_mha_with_repeated_kv(causal):
+    """GQA (32 query heads over 8 KV heads) against the same call with each KV head repeated for its 4
+    query heads (32 KV heads): every row walks the same key tiles in the same order whichever heads share
+    its workgroup, so O and LSE agree bit for bit (B=2, N=4096, d=128: 1024 eight-wave units either way)."""
+    w = PrefillWorkload("gqa_mha", 2, 32, 8, 4096, 128, causal)
+    _announce(f"attn_fwd GQA vs MHA repeated, causal={causal}")
+    a = prefill_inputs(w, seed=77)
+    q, k, v = dev_bf16(a["q"]), dev_bf16(a["k"]), dev_bf16(a["v"])
+    lse_g = torch.empty((2, 32, 4096), dtype=torch.float32, device="cuda:0")
+    lse_m = torch.empty_like(lse_g)
+    o_g, _ = paa.attn_fwd(q, k, v, causal, a["scale"], lse=lse_g)
+    k4, v4 = k.repeat_interleave(4, dim=1).contiguous(), v.repeat_interleave(4, dim=1).contiguous()
+    o_m, _ = paa.attn_fwd(q, k4, v4, causal, a["scale"], lse=lse_m)
+    torch.cuda.synchronize()
+    assert torch.equal(o_g.view(torch.int16), o_m.view(torch.int16))
+    assert torch.equal(lse_g, lse_m)
