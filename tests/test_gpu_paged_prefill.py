@@ -91,12 +91,15 @@ LARGE = [
     ([700, 0, 48, 1], [700, 0, 257, 1], 8, 8, 128, 8192),
     # d = 64 (eight-wave lock-step kernel) with contexts past 64 key tiles
     ([4200, 0, 70, 3000], [10, 100, 300, 1], 8, 8, 64, 8192),
+    # ping-pong kernel past 128 key tiles: the per-wave window of page ids moves twice
+    ([9000, 100, 0, 5000], [64, 300, 2048, 1], 32, 8, 128, 2048),
 ]
 
 
 @pytest.mark.parametrize("ctxs,qlens,H,Hkv,d,max_q_len", LARGE)
 def test_paged_prefill_large_grid_full_parity(ctxs, qlens, H, Hkv, d, max_q_len):
-    w = ChunkedPrefillWorkload("large", len(ctxs), H, Hkv, d, 0, 0, 1, num_pages=600)
+    pages = sum(-(-(c + q) // 16) for c, q in zip(ctxs, qlens))
+    w = ChunkedPrefillWorkload("large", len(ctxs), H, Hkv, d, 0, 0, 1, num_pages=max(600, pages + 64))
     _announce(f"paged prefill ctx{ctxs} q{qlens} H{H} Hkv{Hkv} d{d} max_q_len {max_q_len}")
     a = chunked_prefill_inputs(w, seed=sum(ctxs) + H, ctx_lens=ctxs, q_lens=qlens)
     _check_all(a, max_q_len)
