@@ -71,8 +71,8 @@ def test_fp8_decode_full_size_whole():
 
 def test_fp8_decode_matches_bf16_decode_of_the_same_values():
     """With unit scales the FP8 decode turns each code into the bf16 value the bf16 decode reads from a bf16
-    cache holding the same numbers; only the order of the sum over d in the scores differs, so outputs agree
-    within one bf16 rounding and LSEs within fp32 rounding."""
+    cache holding the same numbers; only the order of the sum over d in the scores differs, so LSEs agree
+    within fp32 rounding and outputs within the bound derived below."""
     w = DecodeWorkload("fp8eq", 5, 32, 8, 128, 1, 700, 16, 300)
     a = decode_inputs_fp8(w, seed=31)
     lse8 = torch.empty((5, 32), dtype=torch.float32, device="cuda:0")
@@ -85,7 +85,12 @@ def test_fp8_decode_matches_bf16_decode_of_the_same_values():
                                    dev_i32(a["block_table"]), dev_i32(a["seq_lens"]), a["scale"], lse=lse16)
     torch.cuda.synchronize()
     x, y = host_f64(o8), host_f64(o16)
-    assert np.all(np.abs(x - y) <= 2.0 ** -7 * np.maximum(np.abs(x), np.abs(y)))
+    # a score that differs in its last fp32 bit can move a probability's bf16 rounding by one step (2^-7 of
+    # its value), so O may differ by 2^-7 of (the softmax-weighted mean of |v| + |O|) besides the two
+    # outputs' own rounding; the weighted mean comes from the oracle over |V| (sign bits cleared)
+    a_abs = oracle.paged_decode_fp8(a["q"], a["k_cache"], a["v_cache"] & np.uint8(0x7F), 1.0, 1.0,
+                                    a["block_table"], a["seq_lens"], a["scale"])[0]
+    assert np.all(np.abs(x - y) <= 2.0 ** -7 * a_abs + 2.0 ** -6 * np.maximum(np.abs(x), np.abs(y)))
     # scores here reach the hundreds (E4M3 values up to 448 with unit scales): a few fp32 ulps of the LSE
     ulp = np.finfo(np.float32).eps * np.abs(lse16.cpu().numpy())
     assert np.all(np.abs(lse8.cpu().numpy() - lse16.cpu().numpy()) <= 4 * ulp)
