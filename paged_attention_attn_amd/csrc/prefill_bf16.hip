@@ -27,9 +27,9 @@
 //    fetches, so the loads stay coalesced.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q kept in
 //    VGPRs for the whole kernel), so each lane ends up holding 16 scores of
-//    ONE query row (row l%32; the two half-waves split the keys).  Row max is
-//    a lane-local max plus one permlane32 swap; the row sums stay lane-local
-//    until the epilogue.  Two sums are kept: of the fp32 probabilities (for
+//    ONE query row (row l%32; the two half-waves split the keys).  A row
+//    maximum, when one is taken (below), is a lane-local max plus one
+//    permlane32 swap; the row sums stay lane-local until the epilogue.  Two sums are kept: of the fp32 probabilities (for
 //    the LSE) and of the same probabilities as rounded to bf16 for P.V (one
 //    v_dot2 per packed pair), by which O is divided, so that O is a weighted
 //    mean of V rows with exactly the weights its numerator used (a row held
@@ -702,7 +702,7 @@ __global__ __launch_bounds__(64 * WAVES, (RB == 1 ? 2 : 1)) void prefill_bf16_ke
 // ---------------------------------------------------------------------------------------------
 // Ping-pong variant: 8 waves in two groups of 4 (waves w and w + 4 share a SIMD).  A wave's
 // work per key tile is an MFMA phase (scores of tile i, and O += P V of tile i - 1) and a VALU
-// phase (mask, row max and exponentials of tile i).  A single wave cannot overlap its own MFMA
+// phase (mask, exponentials and row sums of tile i).  A single wave cannot overlap its own MFMA
 // and VALU work, but a SIMD overlaps an MFMA wave with a VALU wave, so group B runs one phase
 // behind group A: in every period one group is in its MFMA phase and the other in its VALU
 // phase, and a workgroup barrier ends each period.  Stage s of the LDS ring holds K_s and
