@@ -199,6 +199,26 @@ def test_paged_prefill_full_workload_whole():
     _announce(f"{w.name}: {st}")
 
 
+def test_paged_prefill_repeat_is_bitwise_identical():
+    """The full chunked workload twice on the same buffers: the second call appends the same rows again, so
+    the caches are unchanged, and O and LSE repeat bit for bit (no atomics; fixed summation order)."""
+    w = WORKLOADS["chunked_prefill_s16h32kv8d128_ctx0to4096_q512"]
+    _announce(f"{w.name}: two calls")
+    a = chunked_prefill_inputs(w, seed=4)
+    t = _to_dev(a)
+    H = a["q"].shape[1]
+    outs = []
+    for _ in range(2):
+        lse = torch.empty((a["q"].shape[0], H), dtype=torch.float32, device="cuda:0")
+        o, _ = paa.paged_prefill(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["block_table"],
+                                 t["ctx_lens"], t["q_start"], max_q_len=a["max_q_len"], scale=a["scale"], lse=lse)
+        torch.cuda.synchronize()
+        outs.append((o.view(torch.int16).cpu().numpy(), lse.cpu().numpy().view(np.uint32),
+                     t["k_cache"].view(torch.int16).cpu().numpy(), t["v_cache"].view(torch.int16).cpu().numpy()))
+    for x, y in zip(outs[0], outs[1]):
+        assert np.array_equal(x, y)
+
+
 # (ctx lengths, chunk lengths, H, Hkv): a small grid (lock-step kernel) and one of 1024 eight-wave units
 # (ping-pong kernel: 64 sequences x 8 KV heads x 2 query tiles)
 OOB = [([37, 0, 300, 64], [50, 20, 129, 1], 8, 2),
