@@ -447,3 +447,13 @@ def test_decode_gqa_equals_mha_with_repeated_kv():
             bound = _partition_bound(a)
             assert np.all(np.abs(o_g - o_m) <= bound + 2.0 ** -6 * np.maximum(np.abs(o_g), np.abs(o_m)))
             assert np.max(np.abs(l_g - l_m)) <= 1e-5
+
+
+def test_decode_poisoned_slots_change_no_bit():
+    """NaN in every slot no token occupies (the tail of each last page, every unreferenced page) against
+    zeros there: the same bits out, so no kernel reads or multiplies a slot past a sequence's end."""
+    w = DecodeWorkload("poison", 32, 32, 8, 128, 1, 2000, 16, 5000)
+    _announce("decode poisoned against zero-filled slots")
+    o1, l1, _ = _run(decode_inputs(w, seed=5, poison=True), w.H)
+    o0, l0, _ = _run(decode_inputs(w, seed=5, poison=False), w.H)
+    assert np.all(np.isfinite(o1)) and np.array_equal(o1, o0) and np.array_equal(l1, l0)

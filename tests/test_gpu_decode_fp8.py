@@ -167,3 +167,12 @@ def test_fp8_decode_gqa_equals_mha_with_repeated_kv():
     ro, rl = _oracle(a)
     assert_close_bf16(o_g, ro)
     assert_close_lse(l_g, rl)
+
+
+def test_fp8_decode_poisoned_slots_change_no_bit():
+    """The E4M3 NaN code in every slot no token occupies against zero codes there: the same bits out."""
+    w = DecodeWorkload("fp8poison", 32, 32, 8, 128, 1, 2000, 16, 5000)
+    _announce("fp8 decode poisoned against zero-filled slots")
+    o1, l1, _ = _run(decode_inputs_fp8(w, seed=6, poison=True), w.H)
+    o0, l0, _ = _run(decode_inputs_fp8(w, seed=6, poison=False), w.H)
+    assert np.all(np.isfinite(o1)) and np.array_equal(o1, o0) and np.array_equal(l1, l0)

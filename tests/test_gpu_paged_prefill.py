@@ -219,6 +219,21 @@ def test_paged_prefill_repeat_is_bitwise_identical():
         assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_paged_prefill_poisoned_slots_change_no_bit(d):
+    """NaN in every cache slot no context token occupies (including the slots the chunk is appended to)
+    against zeros there: O and LSE come out with the same bits, on a small grid (lock-step kernel, d=64)
+    and the full workload's shape (ping-pong kernel, d=128)."""
+    if d == 128:
+        w = WORKLOADS["chunked_prefill_s16h32kv8d128_ctx0to4096_q512"]
+    else:
+        w = ChunkedPrefillWorkload("poison64", 6, 8, 2, 64, 0, 1500, 300, num_pages=1000)
+    _announce(f"paged prefill d{d}: poisoned against zero-filled slots")
+    o1, l1, _, _ = _run(chunked_prefill_inputs(w, seed=8, poison=True))
+    o0, l0, _, _ = _run(chunked_prefill_inputs(w, seed=8, poison=False))
+    assert np.all(np.isfinite(o1)) and np.array_equal(o1, o0) and np.array_equal(l1, l0)
+
+
 # (ctx lengths, chunk lengths, H, Hkv): a small grid (lock-step kernel) and one of 1024 eight-wave units
 # (ping-pong kernel: 64 sequences x 8 KV heads x 2 query tiles)
 OOB = [([37, 0, 300, 64], [50, 20, 129, 1], 8, 2),
