@@ -521,6 +521,7 @@ def run_bench(args, torch, paa) -> dict:
     c_tf = chunked_flops(cc.w, cc.a["ctx_lens"]) / (mean * 1e-3) / 1e12
     chunked = {"workload": CHUNKED, "ms": round(mean, 4), "ms_median": round(med, 4), "value": round(c_tf, 2),
                "unit": "TFLOP/s", "algorithmic_gflop": round(chunked_flops(cc.w, cc.a["ctx_lens"]) / 1e9, 3),
+               "exponentials_g": round(chunked_flops(cc.w, cc.a["ctx_lens"]) / (4.0 * cc.w.d) / 1e9, 4),
                "algorithmic_mb": round(chunked_bytes(cc.w, cc.a["ctx_lens"]) / 1e6, 3),
                "roofline": roofline("mfma", c_tf, PEAK_BF16_TFLOPS, "TFLOP/s", read_traffic(CHUNKED),
                                     read_mfma_busy(CHUNKED))}
@@ -601,7 +602,7 @@ def run_bench(args, torch, paa) -> dict:
         "targets": {"prefill_frac_of_bf16_peak": 0.5, "decode_frac_of_hbm_peak": 0.7},
         "prefill": {"workload": pw.name, "ms": round(pre_ms, 5), "value": round(pre_tf, 3), "unit": "TFLOP/s",
                     "algorithmic_gflop": round(pf / 1e9, 4), "algorithmic_mb": round(prefill_bytes(pw) / 1e6, 3),
-                    "roofline": pre_roof},
+                    "exponentials_g": round(pw.B * pw.H * pw.visible_pairs() / 1e9, 4), "roofline": pre_roof},
         "decode": {"workload": dw.name, "ms": round(cold_ms, 5), "value": round(cold_gbs, 2), "unit": "GB/s",
                    "caches": "evicted before each call (512 MB read between calls)",
                    "algorithmic_gb": round(db / 1e9, 5), "roofline": dict(dec_roof, kernel=(
