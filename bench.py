@@ -53,6 +53,7 @@ METRIC = "causal prefill attention TFLOP/s + paged decode KV GB/s, % of roofline
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0  # dense fp8 MFMA
 PEAK_CLOCK_GHZ = 2.4  # the engine clock both MFMA peaks are quoted at
+CLOCK_SAMPLE_S = 2.0  # seconds of back-to-back prefill calls while the shader clocks are sampled
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_counters.txt")
@@ -164,13 +165,7 @@ def roofline(kind, achieved, peak, unit, traffic, mfma=(None, None)):
     r = {"bound": kind, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
          "frac": round(achieved / peak, 4), "traffic": traffic}
     if kind == "mfma":
-        busy, executed_per_alg = mfma
-        r["mfma_busy_pct"] = busy  # matrix-core busy share of active cycles (counters), or None
-        if busy and executed_per_alg and peak == PEAK_BF16_TFLOPS:
-            # the peak assumes every matrix-core cycle busy at PEAK_CLOCK_GHZ; the counters give the busy
-            # share, so the clock the kernel ran at is what reconciles the two (bf16 MFMAs only: the busy
-            # cycles of the 8-bit MFMA do not scale the same way)
-            r["implied_clock_ghz"] = round(PEAK_CLOCK_GHZ * achieved * executed_per_alg / peak / (busy / 100.0), 2)
+        r["mfma_busy_pct"] = mfma[0]  # matrix-core busy share of active cycles (counters), or None
     return r
 
 
@@ -211,6 +206,79 @@ def timed(torch, fn, iters, warmup):
     torch.cuda.synchronize()
     ts = [a.elapsed_time(b) for a, b in evs]
     return statistics.median(ts), statistics.fmean(ts)
+
+
+def gfx_clocks_from_amd_smi(data):
+    """{gpu: [MHz of gfx_0, gfx_1, ...]} from the JSON of `amd-smi metric -c --json` (a dict holding
+    "gpu_data", or the list itself), or None if it holds no shader clock."""
+    gpus = data.get("gpu_data", []) if isinstance(data, dict) else data
+    out = {}
+    for g in gpus if isinstance(gpus, list) else []:
+        clk = g.get("clock", {}) if isinstance(g, dict) else {}
+        names = [k for k in clk if k.startswith("gfx_") and k[4:].isdigit()]
+        vals = []
+        for k in sorted(names, key=lambda k: int(k[4:])):
+            inner = clk[k].get("clk") if isinstance(clk[k], dict) else None
+            v = inner.get("value") if isinstance(inner, dict) else None
+            if isinstance(v, (int, float)):
+                vals.append(float(v))
+        if vals:
+            out[g.get("gpu")] = vals
+    return out or None
+
+
+def sample_gfx_clocks(torch, fn, seconds=CLOCK_SAMPLE_S):
+    """Shader clocks while fn runs back to back: `amd-smi metric -c` read about every 0.1 s from a second
+    thread, averaged per die (gfx_0, gfx_1, ...) over the samples after the first quarter second.  Of the
+    GPUs amd-smi lists, the one with the highest clocks is taken (the busy one).  None where amd-smi is not
+    installed or its output cannot be read."""
+    import shutil
+    import subprocess
+    import threading
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+
+    def read():
+        try:
+            r = subprocess.run([exe, "metric", "-c", "--json"], capture_output=True, text=True, timeout=30)
+            return gfx_clocks_from_amd_smi(json.loads(r.stdout))
+        except (OSError, subprocess.SubprocessError, ValueError):
+            return None
+
+    samples, stop = [], threading.Event()
+
+    def loop():
+        t0 = time.perf_counter()
+        while not stop.is_set():
+            got = read()
+            if got is None:
+                return
+            samples.append((time.perf_counter() - t0, got))
+            stop.wait(0.1)
+
+    th = threading.Thread(target=loop, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=60)
+    use = [got for t, got in samples if t >= 0.25]
+    if not use:
+        return None
+
+    def per_die(g):
+        rows = [got[g] for got in use if g in got]
+        return [statistics.fmean(r[i] for r in rows) for i in range(min(len(r) for r in rows))]
+
+    best = max({g for got in use for g in got}, key=lambda g: statistics.fmean(per_die(g)))
+    dies = per_die(best)
+    return {"mean_mhz": round(statistics.fmean(dies), 1), "per_die_mhz": [round(x, 1) for x in dies],
+            "samples": len(use), "seconds": seconds, "gpu_index_in_amd_smi": best,
+            "source": "amd-smi metric -c about every 0.1 s while the workload ran back to back"}
 
 
 class Phases:
@@ -457,6 +525,15 @@ def run_bench(args, torch, paa) -> dict:
     dec_gbs = db / (dec_ms * 1e-3) / 1e9
     pre_roof = roofline("mfma", pre_tf, PEAK_BF16_TFLOPS, "TFLOP/s", read_traffic(pw.name), read_mfma_busy(pw.name))
 
+    # ---- the shader clocks the prefill runs at (outside the timed region) ----
+    phases.start(f"prefill {pw.name} back to back, shader clocks sampled")
+    clocks = sample_gfx_clocks(torch, pc)
+    pre_roof["measured_clock_ghz"] = round(clocks["mean_mhz"] / 1000.0, 3) if clocks else None
+    # the same rate against the peak scaled to that clock (the peak is quoted at PEAK_CLOCK_GHZ)
+    pre_roof["frac_at_measured_clock"] = (round(pre_tf / (PEAK_BF16_TFLOPS * clocks["mean_mhz"] / 1000.0 / PEAK_CLOCK_GHZ), 4)
+                                          if clocks else None)
+    _log(f"shader clocks under {pw.name}: {clocks['per_die_mhz'] if clocks else 'not available'}")
+
     # ---- decode with the 256 MB last-level cache evicted before every call ----
     # (by reading a 512 MB buffer: a read leaves clean lines, so no write-back lands inside the timed call)
     phases.start(f"decode {dw.name}, caches evicted before each call")
@@ -602,7 +679,8 @@ def run_bench(args, torch, paa) -> dict:
         "targets": {"prefill_frac_of_bf16_peak": 0.5, "decode_frac_of_hbm_peak": 0.7},
         "prefill": {"workload": pw.name, "ms": round(pre_ms, 5), "value": round(pre_tf, 3), "unit": "TFLOP/s",
                     "algorithmic_gflop": round(pf / 1e9, 4), "algorithmic_mb": round(prefill_bytes(pw) / 1e6, 3),
-                    "exponentials_g": round(pw.B * pw.H * pw.visible_pairs() / 1e9, 4), "roofline": pre_roof},
+                    "exponentials_g": round(pw.B * pw.H * pw.visible_pairs() / 1e9, 4), "roofline": pre_roof,
+                    "clocks": clocks},
         "decode": {"workload": dw.name, "ms": round(cold_ms, 5), "value": round(cold_gbs, 2), "unit": "GB/s",
                    "caches": "evicted before each call (512 MB read between calls)",
                    "algorithmic_gb": round(db / 1e9, 5), "roofline": dict(dec_roof, kernel=(
