@@ -867,6 +867,54 @@ def summarize_mfma(mfma_dir, pass_json, command) -> str:
     return "\n".join(lines) + "\n"
 
 
+WAVE_COUNTERS = (("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                  "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_VMEM"),
+                 ("SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_DATA_FIFO_FULL", "SQ_LDS_CMD_FIFO_FULL",
+                  "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_MISC", "SQ_ACTIVE_INST_SCA", "SQ_INSTS_LDS"))
+
+
+def summarize_waves(dir1, dir2, pass_json, command) -> str:
+    """JSON lines: per workload and kernel, where the waves' cycles go, from two rocprofv3 --pmc runs of
+    WAVE_COUNTERS: the shares of all wave-cycles spent issuing (any instruction, and VALU including MFMA, LDS,
+    VMEM, scalar), waiting for an instruction to issue (the pipe is taken by the SIMD's other wave, or an
+    operand is not ready) and waiting at s_waitcnt or a barrier; LDS bank-conflict cycles per LDS-active
+    cycle."""
+    with open(pass_json) as f:
+        meta = json.loads([l for l in f if l.startswith("{")][-1])
+    names = meta["phases"]
+    per = {}
+    for d, counters in zip((dir1, dir2), WAVE_COUNTERS):
+        for counter in counters:
+            groups = _split_phases(_load_counters(d, counter), len(names))
+            if len(groups) != len(names) or any(COPY_KERNEL_TAG not in r["name"] for r in groups[0]):
+                raise SystemExit(f"{counter}: dispatches do not split into the pass's phases {names}")
+            for name, g in zip(names[1:], groups[1:]):
+                for r in g:
+                    per.setdefault((name, _short(r["name"])), {}).setdefault(counter, []).append(r["value"])
+    lines = ["# Where the waves' cycles go, per workload and kernel, from two rocprofv3 --pmc runs (per-dispatch",
+             "# means of counters summed over waves), as % of SQ_WAVE_CYCLES.",
+             f"# Command (repository root): {command}",
+             "# issuing: SQ_ACTIVE_INST_ANY (of it VALU incl. MFMA, LDS, VMEM, scalar); waiting_to_issue:",
+             "# SQ_WAIT_INST_ANY; waiting_waitcnt_or_barrier: SQ_WAIT_ANY; lds_bank_conflict: SQ_LDS_BANK_CONFLICT /",
+             "# SQ_LDS_IDX_ACTIVE."]
+    for (name, kernel), c in per.items():
+        mean = {k: statistics.fmean(v) for k, v in c.items()}
+        wc = mean.get("SQ_WAVE_CYCLES", 0.0)
+        if wc <= 0:
+            continue
+        pct = lambda k: round(100.0 * mean.get(k, 0.0) / wc, 1)  # noqa: E731
+        lds = mean.get("SQ_LDS_IDX_ACTIVE", 0.0)
+        lines.append(json.dumps({
+            "workload": name, "kernel": kernel, "issuing_pct": pct("SQ_ACTIVE_INST_ANY"),
+            "valu_incl_mfma_pct": pct("SQ_ACTIVE_INST_VALU"), "lds_pct": pct("SQ_ACTIVE_INST_LDS"),
+            "vmem_pct": pct("SQ_ACTIVE_INST_VMEM"), "scalar_pct": pct("SQ_ACTIVE_INST_SCA"),
+            "waiting_to_issue_pct": pct("SQ_WAIT_INST_ANY"), "waiting_to_issue_lds_pct": pct("SQ_WAIT_INST_LDS"),
+            "waiting_waitcnt_or_barrier_pct": pct("SQ_WAIT_ANY"),
+            "lds_bank_conflict_pct": round(100.0 * mean.get("SQ_LDS_BANK_CONFLICT", 0.0) / lds, 2) if lds else None,
+            "sources": meta["sources"]}))
+    return "\n".join(lines) + "\n"
+
+
 # ----------------------------------------------------------------- main
 
 def main() -> int:
@@ -883,6 +931,7 @@ def main() -> int:
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"))
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PASS_JSON"))
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("MFMA_DIR", "PASS_JSON"))
+    ap.add_argument("--summarize-waves", nargs=3, metavar=("PASS1_DIR", "PASS2_DIR", "PASS_JSON"))
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     args = ap.parse_args()
 
@@ -894,6 +943,9 @@ def main() -> int:
         return 0
     if args.summarize_mfma:
         sys.stdout.write(summarize_mfma(*args.summarize_mfma, args.command))
+        return 0
+    if args.summarize_waves:
+        sys.stdout.write(summarize_waves(*args.summarize_waves, args.command))
         return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
