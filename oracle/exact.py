@@ -16,7 +16,7 @@ Sources (the pages this follows; cited by page title and section):
   kernel must translate each logical token position through that table.  The
   block size in the pages' serving example is 16 tokens.
 
-Readings taken where the pages are silent (each repeated in the design doc):
+Readings taken where the pages are silent:
 
 * LSE is the natural log of the sum of exp over the scaled, masked scores of
   a row: LSE_i = m_i + ln(l_i), with m_i the row max and l_i the shifted sum.
